@@ -1,0 +1,161 @@
+"""Seeded synthetic inputs for the Agent Attention forward.
+
+This module only draws random numbers and converts number formats.  It holds
+none of the attention arithmetic, so the CPU oracle and the GPU path can both
+consume exactly the same operands without sharing any method code.
+
+Workloads (shapes named after the models the Agent Attention pages evaluate:
+DeiT-S at 224^2, PVT stage 1, the Stable-Diffusion v1.5 UNet latent, and a
+high-resolution latent; see "Agent Attention: On the Integration of Softmax and
+Linear Attention", §4 Agent Transformer and §5 Experiments).  Trained weights
+and datasets are not used: Q, K, V (and caller-supplied agents) are i.i.d.
+normal draws of the stated standard deviation, generated in float32 with
+numpy's PCG64 in the order Q, K, V, A and then rounded to bfloat16 with
+round-to-nearest-even for the bf16 workloads.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    h: int          # token-grid rows
+    w: int          # token-grid columns
+    d: int          # head dimension
+    s: int          # agent grid side: k = s*s agents
+    dtype: str      # "f32" or "bf16"
+    sigma: float    # std of the i.i.d. normal Q, K, V draws
+    supplied_agents: bool = False   # caller passes A instead of pooling Q
+    agent_sigma: float = 1.0
+
+    @property
+    def N(self) -> int:
+        return self.h * self.w
+
+    @property
+    def k(self) -> int:
+        return self.s * self.s
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    @property
+    def es(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+
+WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("tiny_fp32", 1, 1, 14, 14, 64, 7, "f32", 1.0),
+        Workload("deit_s", 64, 6, 14, 14, 64, 7, "bf16", 1.0),
+        Workload("pvt_stage1", 16, 1, 56, 56, 64, 7, "bf16", 0.5),
+        Workload("sd_unet", 2, 8, 64, 64, 40, 8, "bf16", 1.0),
+        Workload("sd_unet_agents", 2, 8, 64, 64, 40, 8, "bf16", 1.0,
+                 supplied_agents=True, agent_sigma=1.0),
+        Workload("latent_hr", 1, 8, 128, 128, 64, 16, "bf16", 1.0),
+    ]
+}
+
+
+def custom(name="custom", *, B, H, h, w, d, s, dtype="bf16", sigma=1.0,
+           supplied_agents=False, agent_sigma=1.0) -> Workload:
+    return Workload(name, B, H, h, w, d, s, dtype, sigma, supplied_agents,
+                    agent_sigma)
+
+
+# ---------------------------------------------------------------------------
+# number formats
+
+def bf16_bits_from_f32(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns (uint16), round to nearest even.
+
+    Finite inputs only (the generators never produce inf/nan)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    r = (u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def f32_from_bf16_bits(b: np.ndarray) -> np.ndarray:
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32)
+            << np.uint32(16)).view(np.float32)
+
+
+@dataclasses.dataclass
+class Operand:
+    """One tensor in its storage format plus its exact value in float64."""
+    storage: np.ndarray   # float32 array, or uint16 bfloat16 bit patterns
+    exact: np.ndarray     # the same values, widened exactly to float64
+    dtype: str
+
+
+def _pack(x32: np.ndarray, dtype: str) -> Operand:
+    if dtype == "f32":
+        x32 = np.ascontiguousarray(x32, dtype=np.float32)
+        return Operand(x32, x32.astype(np.float64), dtype)
+    bits = bf16_bits_from_f32(x32)
+    return Operand(bits, f32_from_bf16_bits(bits).astype(np.float64), dtype)
+
+
+@dataclasses.dataclass
+class Inputs:
+    wl: Workload
+    Q: Operand
+    K: Operand
+    V: Operand
+    A: Operand | None     # caller-supplied agents, or None (pool Q)
+
+
+def make_inputs(wl: Workload, seed: int, kind: str = "iid") -> Inputs:
+    """Draw Q, K, V (and A when the workload supplies agents).
+
+    kind="iid":  i.i.d. N(0, sigma^2) as the workload states.
+    kind="discriminating":  inputs for which |O| is of order one and both
+    softmaxes are far from uniform, so that a wrong output cannot hide inside
+    the absolute tolerance:
+      * Q is a smooth random field over the h x w grid (three low-frequency
+        cosines per channel plus a little noise), so that window means of Q
+        stay far from zero;
+      * K ~ N(0, 1.8^2);
+      * V has per-channel means spread over [-2, 2] plus N(0, 1) noise;
+      * supplied agents ~ N(0, 1).
+    Amplitudes are chosen so that the logits of both softmaxes have a
+    standard deviation of roughly 1.5-2.5.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    shp = (wl.B, wl.H, wl.N, wl.d)
+    ashp = (wl.B, wl.H, wl.k, wl.d)
+    if kind == "iid":
+        q = rng.standard_normal(shp, dtype=np.float32) * np.float32(wl.sigma)
+        k = rng.standard_normal(shp, dtype=np.float32) * np.float32(wl.sigma)
+        v = rng.standard_normal(shp, dtype=np.float32) * np.float32(wl.sigma)
+        a = (rng.standard_normal(ashp, dtype=np.float32)
+             * np.float32(wl.agent_sigma)) if wl.supplied_agents else None
+    elif kind == "discriminating":
+        rr = np.arange(wl.h, dtype=np.float64)[:, None] / wl.h
+        cc = np.arange(wl.w, dtype=np.float64)[None, :] / wl.w
+        field = np.zeros((wl.B, wl.H, wl.h, wl.w, wl.d))
+        for _ in range(3):
+            fr = rng.uniform(0.0, 2.0, size=(wl.B, wl.H, 1, 1, wl.d))
+            fc = rng.uniform(0.0, 2.0, size=(wl.B, wl.H, 1, 1, wl.d))
+            ph = rng.uniform(0.0, 2 * np.pi, size=(wl.B, wl.H, 1, 1, wl.d))
+            field += np.cos(2 * np.pi * (fr * rr[..., None] + fc * cc[..., None]) + ph)
+        q = (0.7 * field.reshape(shp)
+             + 0.3 * rng.standard_normal(shp)).astype(np.float32)
+        k = (1.8 * rng.standard_normal(shp)).astype(np.float32)
+        mu = np.linspace(-2.0, 2.0, wl.d)
+        v = (mu + rng.standard_normal(shp)).astype(np.float32)
+        a = rng.standard_normal(ashp).astype(np.float32) if wl.supplied_agents else None
+    else:
+        raise ValueError(f"unknown input kind {kind!r}")
+    return Inputs(wl, _pack(q, wl.dtype), _pack(k, wl.dtype), _pack(v, wl.dtype),
+                  _pack(a, wl.dtype) if a is not None else None)

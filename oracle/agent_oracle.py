@@ -1,0 +1,115 @@
+"""CPU oracle for the Agent Attention forward pass -- TEST INFRASTRUCTURE ONLY.
+
+Plain, slow and deliberately obvious float64 numpy code.  Only the tests, the
+smoke check and the benchmark's CPU-baseline leg may import it; the product
+path (the HIP library and its Python binding) never does, and this module
+imports nothing from the product path.
+
+Sources (web pages about Agent Attention, Han et al., arXiv 2312.08874):
+  [Paper]  "Agent Attention: On the Integration of Softmax and Linear
+           Attention" (paperlayer.ai summary of arXiv 2312.08874v3).
+  [JSQMD]  "Agent Attention：Transformer计算量太大？试试这个'代理令牌'的轻量化方案"
+           (jsqmd.com news article).
+
+What is computed, for every batch b and head h independently:
+  1. agents:      A = 2-D average pool of Q over the h x w token grid down to
+                  an s x s grid ([Paper] §4 Agent Transformer: agents come
+                  from pooling by default; §6 Conclusion: A = f(Q); [JSQMD] §2
+                  binds agents to the image grid, e.g. 7 x 7 = 49), unless the
+                  caller supplies A ([Paper] §4: learnable agents).
+  2. aggregation: V_A = softmax(scale * A K^T) V      ([JSQMD] §1 pseudocode,
+                  stage one; [Paper] §4: first of two Softmax attentions).
+  3. broadcast:   O   = softmax(scale * Q A^T) V_A    ([JSQMD] §1 pseudocode,
+                  stage two; [Paper] §4: second Softmax attention).
+The composition equals the generalised linear attention
+phi_q(Q) phi_k(K)^T V with phi_q(Q) = softmax(scale Q A^T) and
+phi_k(K)^T = softmax(scale A K^T) ([Paper] Abstract and §4).
+
+Readings where the pages leave a step open:
+  * pooling windows for agent (i, j) cover rows [floor(i h/s), ceil((i+1) h/s))
+    and columns [floor(j w/s), ceil((j+1) w/s)) of the row-major grid (token
+    n = r*w + c); agents are numbered i*s + j.  For h, w divisible by s these
+    are the plain non-overlapping block means.
+  * one scale factor (1/sqrt(d) in every workload) is applied in both
+    softmaxes, as in the [JSQMD] §1 pseudocode.
+  * the broadcast keys are the agents A (not V_A); agent bias, the
+    depth-wise convolution and projections are not part of this operator.
+  * softmax runs over the last axis: over the N keys in aggregation, over
+    the k agents in broadcast.
+Every function is pinned by tests (library cross-checks, closed forms,
+invariants and brute force); see tests/test_oracle_pins.py.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def window_bounds(i: int, n: int, s: int) -> tuple[int, int]:
+    """Half-open range of grid rows (or columns) averaged into agent row i."""
+    start = (i * n) // s
+    stop = -((-(i + 1) * n) // s)          # ceil((i+1) n / s)
+    return start, stop
+
+
+def pool_agents(Q: np.ndarray, h: int, w: int, s: int) -> np.ndarray:
+    """A[b, h, i*s+j, :] = mean of Q over agent (i, j)'s window.
+
+    Q: [B, H, h*w, d] float64 -> A: [B, H, s*s, d] float64.
+    ([Paper] §4 and §6: agents are pooled from the queries by default.)
+    """
+    B, H, N, d = Q.shape
+    assert N == h * w and 1 <= s <= h and s <= w
+    grid = Q.reshape(B, H, h, w, d)
+    A = np.empty((B, H, s * s, d), dtype=np.float64)
+    for i in range(s):
+        r0, r1 = window_bounds(i, h, s)
+        for j in range(s):
+            c0, c1 = window_bounds(j, w, s)
+            A[:, :, i * s + j, :] = grid[:, :, r0:r1, c0:c1, :].mean(axis=(2, 3))
+    return A
+
+
+def softmax_last(S: np.ndarray) -> np.ndarray:
+    """Row-wise softmax over the last axis; rows are checked to sum to one."""
+    E = np.exp(S - S.max(axis=-1, keepdims=True))
+    P = E / E.sum(axis=-1, keepdims=True)
+    assert np.allclose(P.sum(axis=-1), 1.0, rtol=0, atol=1e-12)
+    return P
+
+
+def aggregate(A: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndarray:
+    """Agent aggregation: V_A = softmax(scale * A K^T) V, per (b, h).
+
+    A: [B, H, k, d], K, V: [B, H, N, d] -> V_A: [B, H, k, d].
+    ([JSQMD] §1, stage one; [Paper] §4, first Softmax attention.)
+    """
+    S1 = scale * (A @ np.swapaxes(K, -1, -2))          # [B, H, k, N]
+    return softmax_last(S1) @ V
+
+
+def broadcast(Q: np.ndarray, A: np.ndarray, V_A: np.ndarray, scale: float) -> np.ndarray:
+    """Agent broadcast: O = softmax(scale * Q A^T) V_A, per (b, h).
+
+    Q: [B, H, N, d], A, V_A: [B, H, k, d] -> O: [B, H, N, d].
+    ([JSQMD] §1, stage two; [Paper] §4, second Softmax attention.)
+    """
+    S2 = scale * (Q @ np.swapaxes(A, -1, -2))          # [B, H, N, k]
+    return softmax_last(S2) @ V_A
+
+
+def forward(Q, K, V, h: int, w: int, s: int, scale: float, A=None):
+    """Full forward.  Returns (O, A, V_A), all float64.
+
+    Q, K, V: [B, H, h*w, d]; A: None (pool Q to s x s) or [B, H, s*s, d].
+    """
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    if A is None:
+        A = pool_agents(Q, h, w, s)
+    else:
+        A = np.asarray(A, dtype=np.float64)
+        assert A.shape == Q.shape[:2] + (s * s, Q.shape[3])
+    V_A = aggregate(A, K, V, scale)
+    O = broadcast(Q, A, V_A, scale)
+    return O, A, V_A

@@ -1,0 +1,296 @@
+"""Pins for the CPU oracle: checks against things other than the oracle itself.
+
+Each pin takes the oracle module and raises AssertionError if the oracle
+disagrees with what the pages and the mathematics fix:
+  * independent library routines for the special cases that reduce to them
+    (torch's adaptive_avg_pool2d for the pooling, torch's float64
+    scaled_dot_product_attention for each of the two Softmax attention
+    operations that "Agent Attention: On the Integration of Softmax and Linear
+    Attention" (§1, §4) says the method consists of);
+  * closed forms (one agent; all keys equal; constant values; hand-derived
+    examples with exact rational softmax weights);
+  * invariants (key translation, joint key/value permutation, agent
+    permutation, outputs as convex combinations of value rows);
+  * brute force with explicit loops on tiny inputs, including the explicit
+    N x N generalised-linear-attention matrix
+    softmax(Q A^T) softmax(A K^T) (Abstract and §4 of the same page).
+The mutation tests plant plausible mistakes in the oracle and require that at
+least one pin fails for each.
+"""
+from __future__ import annotations
+
+import math
+from fractions import Fraction
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+
+def _rng(seed):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def _t(x):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float64))
+
+
+def _sdpa(q, k, v, scale):
+    return F.scaled_dot_product_attention(_t(q), _t(k), _t(v), scale=scale).numpy()
+
+
+def _torch_pool(Q, h, w, s):
+    B, H, N, d = Q.shape
+    x = _t(Q).reshape(B * H, h, w, d).permute(0, 3, 1, 2)
+    y = F.adaptive_avg_pool2d(x, (s, s))                  # [B*H, d, s, s]
+    return y.permute(0, 2, 3, 1).reshape(B, H, s * s, d).numpy()
+
+
+# --------------------------------------------------------------------- pooling
+
+def pin_pool_vs_adaptive_avg_pool2d(orc):
+    for seed, (B, H, h, w, d, s) in enumerate([
+            (2, 3, 14, 14, 8, 7), (1, 2, 7, 9, 5, 4), (1, 1, 5, 3, 4, 3),
+            (1, 1, 56, 56, 4, 7), (2, 1, 10, 6, 3, 1), (1, 1, 9, 16, 2, 5)]):
+        Q = _rng(seed).standard_normal((B, H, h * w, d))
+        A = orc.pool_agents(Q, h, w, s)
+        ref = _torch_pool(Q, h, w, s)
+        assert A.shape == ref.shape
+        assert np.allclose(A, ref, rtol=0, atol=1e-12), (h, w, s)
+
+
+def pin_pool_explicit_loops(orc):
+    """Window sums by explicit token indexing n = r*w + c on a tiny grid."""
+    h, w, s, d = 5, 4, 2, 3
+    Q = _rng(11).standard_normal((1, 1, h * w, d))
+    A = orc.pool_agents(Q, h, w, s)
+    # agent row i covers grid rows [floor(i*h/s), ceil((i+1)*h/s))
+    rows = {0: [0, 1, 2], 1: [2, 3, 4]}
+    cols = {0: [0, 1], 1: [2, 3]}
+    for i in range(s):
+        for j in range(s):
+            acc = [0.0] * d
+            cnt = 0
+            for r in rows[i]:
+                for c in cols[j]:
+                    for ch in range(d):
+                        acc[ch] += Q[0, 0, r * w + c, ch]
+                    cnt += 1
+            for ch in range(d):
+                assert abs(A[0, 0, i * s + j, ch] - acc[ch] / cnt) < 1e-13
+
+
+def pin_pool_window_one_is_identity(orc):
+    h, w, d = 6, 6, 5
+    Q = _rng(12).standard_normal((2, 2, h * w, d))
+    assert np.array_equal(orc.pool_agents(Q, h, w, h), Q)
+
+
+# --------------------------------------------------- the two softmax attentions
+
+def pin_aggregate_is_softmax_attention(orc):
+    rng = _rng(21)
+    B, H, N, k, d, scale = 2, 3, 37, 9, 16, 0.37
+    A = 2.0 * rng.standard_normal((B, H, k, d))
+    K = rng.standard_normal((B, H, N, d))
+    V = rng.standard_normal((B, H, N, d))
+    assert np.allclose(orc.aggregate(A, K, V, scale), _sdpa(A, K, V, scale),
+                       rtol=0, atol=1e-12)
+
+
+def pin_broadcast_is_softmax_attention(orc):
+    rng = _rng(22)
+    B, H, N, k, d, scale = 2, 3, 41, 9, 16, 0.41
+    Q = 2.0 * rng.standard_normal((B, H, N, d))
+    A = rng.standard_normal((B, H, k, d))
+    VA = rng.standard_normal((B, H, k, d))
+    assert np.allclose(orc.broadcast(Q, A, VA, scale), _sdpa(Q, A, VA, scale),
+                       rtol=0, atol=1e-12)
+
+
+def pin_forward_is_pool_then_two_attentions(orc):
+    rng = _rng(23)
+    B, H, h, w, d, s, scale = 2, 2, 6, 10, 8, 3, 0.5
+    Q = 1.5 * rng.standard_normal((B, H, h * w, d))
+    K = 1.5 * rng.standard_normal((B, H, h * w, d))
+    V = rng.standard_normal((B, H, h * w, d))
+    O, A, VA = orc.forward(Q, K, V, h, w, s, scale)
+    A_ref = _torch_pool(Q, h, w, s)
+    VA_ref = _sdpa(A_ref, K, V, scale)
+    O_ref = _sdpa(Q, A_ref, VA_ref, scale)
+    for got, ref in ((A, A_ref), (VA, VA_ref), (O, O_ref)):
+        assert np.allclose(got, ref, rtol=0, atol=1e-12)
+    # caller-supplied agents bypass pooling
+    A2 = rng.standard_normal((B, H, s * s, d))
+    O2, A2_out, VA2 = orc.forward(Q, K, V, h, w, s, scale, A=A2)
+    assert np.array_equal(A2_out, A2)
+    assert np.allclose(O2, _sdpa(Q, A2, _sdpa(A2, K, V, scale), scale),
+                       rtol=0, atol=1e-12)
+
+
+def pin_one_agent_per_token_is_textbook_attention(orc):
+    """s = h = w: every agent is its own query, so V_A is textbook attention."""
+    rng = _rng(24)
+    h = w = 5
+    Q, K, V = (rng.standard_normal((1, 2, h * w, 8)) for _ in range(3))
+    _, A, VA = orc.forward(Q, K, V, h, w, h, 0.6)
+    assert np.array_equal(A, Q)
+    assert np.allclose(VA, _sdpa(Q, K, V, 0.6), rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------------------- closed forms
+
+def pin_single_agent_closed_form(orc):
+    """s = 1: the broadcast softmax has one entry, so every O row is V_A[0],
+    and V_A[0] is the softmax attention of the single query mean(Q)."""
+    rng = _rng(31)
+    h, w, d, scale = 4, 5, 3, 0.7
+    Q, K, V = (rng.standard_normal((1, 1, h * w, d)) for _ in range(3))
+    O, _, VA = orc.forward(Q, K, V, h, w, 1, scale)
+    N = h * w
+    a = [sum(Q[0, 0, n, c] for n in range(N)) / N for c in range(d)]
+    logits = [scale * sum(a[c] * K[0, 0, n, c] for c in range(d)) for n in range(N)]
+    mx = max(logits)
+    e = [math.exp(x - mx) for x in logits]
+    z = sum(e)
+    va = [sum(e[n] / z * V[0, 0, n, c] for n in range(N)) for c in range(d)]
+    assert np.allclose(VA[0, 0, 0], va, rtol=0, atol=1e-13)
+    assert np.allclose(O[0, 0], np.broadcast_to(va, (N, d)), rtol=0, atol=1e-13)
+
+
+def pin_equal_keys_average_values(orc):
+    """All keys equal: the aggregation weights are uniform, so every output
+    row is the mean of V whatever Q and A are."""
+    rng = _rng(32)
+    h, w, d, s = 6, 6, 4, 3
+    Q = 3 * rng.standard_normal((1, 2, h * w, d))
+    K = np.broadcast_to(rng.standard_normal((1, 2, 1, d)), (1, 2, h * w, d)).copy()
+    V = rng.standard_normal((1, 2, h * w, d))
+    O, _, _ = orc.forward(Q, K, V, h, w, s, 0.9)
+    assert np.allclose(O, np.broadcast_to(V.mean(axis=2, keepdims=True), O.shape),
+                       rtol=0, atol=1e-13)
+
+
+def pin_constant_values(orc):
+    rng = _rng(33)
+    h, w, d, s = 4, 6, 5, 2
+    Q, K = (2 * rng.standard_normal((2, 1, h * w, d)) for _ in range(2))
+    v = rng.standard_normal((2, 1, 1, d))
+    V = np.broadcast_to(v, (2, 1, h * w, d)).copy()
+    O, _, _ = orc.forward(Q, K, V, h, w, s, 0.8)
+    assert np.allclose(O, np.broadcast_to(v, O.shape), rtol=0, atol=1e-13)
+
+
+def pin_hand_examples(orc):
+    """Two examples worked by hand with exact softmax weights.
+
+    (1) 2x2 grid, one agent (s=1), scale 1.  Q rows (1,1),(1,-1),(1,3),(1,-3)
+        pool to A = (1, 0).  Key first components ln1, ln2, ln3, ln1 give
+        aggregation weights (1,2,3,1)/7; values (7,0),(0,7),(14,-7),(0,0)
+        give V_A = (49, -7)/7 = (7, -1), and every output row is (7, -1).
+    (2) 2x2 grid, s=2 (each agent is one token, A = Q), Q = identity rows in
+        d=4, scale 1.  K[n, i] = ln m[i][n] makes the aggregation weights
+        m[i][n] / sum_n m[i][n]; the broadcast logits are the identity, so
+        O[n] = ((e-1) V_A[n] + sum_j V_A[j]) / (e + 3).
+    """
+    Q = np.array([[1, 1], [1, -1], [1, 3], [1, -3]], float)[None, None]
+    K = np.array([[0, 5], [math.log(2), -7], [math.log(3), 2], [0, 0]], float)[None, None]
+    V = np.array([[7, 0], [0, 7], [14, -7], [0, 0]], float)[None, None]
+    O, A, VA = orc.forward(Q, K, V, 2, 2, 1, 1.0)
+    assert np.allclose(A[0, 0], [[1, 0]], rtol=0, atol=1e-15)
+    assert np.allclose(VA[0, 0], [[7, -1]], rtol=0, atol=1e-13)
+    assert np.allclose(O[0, 0], [[7, -1]] * 4, rtol=0, atol=1e-13)
+
+    m = [[1, 1, 1, 1], [1, 2, 3, 4], [4, 3, 2, 1], [1, 1, 2, 4]]
+    Vi = [[3, -1, 0, 2], [5, 4, -2, 0], [-6, 1, 1, 1], [0, 0, 8, -4]]
+    Q = np.eye(4)[None, None]
+    K = np.array([[math.log(m[i][n]) for i in range(4)] for n in range(4)])[None, None]
+    V = np.array(Vi, float)[None, None]
+    VA_exact = [[sum(Fraction(m[i][n]) * Vi[n][c] for n in range(4)) / sum(m[i])
+                 for c in range(4)] for i in range(4)]
+    tot = [sum(VA_exact[j][c] for j in range(4)) for c in range(4)]
+    O_exact = [[((math.e - 1) * float(VA_exact[n][c]) + float(tot[c])) / (math.e + 3)
+                for c in range(4)] for n in range(4)]
+    O, A, VA = orc.forward(Q, K, V, 2, 2, 2, 1.0)
+    assert np.array_equal(A[0, 0], np.eye(4))
+    assert np.allclose(VA[0, 0], [[float(x) for x in r] for r in VA_exact], rtol=0, atol=1e-13)
+    assert np.allclose(O[0, 0], O_exact, rtol=0, atol=1e-13)
+
+
+# --------------------------------------------------------------- invariants
+
+def pin_key_translation_invariance(orc):
+    rng = _rng(41)
+    h, w, d, s = 6, 8, 6, 2
+    Q, K, V = (rng.standard_normal((2, 2, h * w, d)) for _ in range(3))
+    u = rng.standard_normal((2, 2, 1, d))
+    O1, _, _ = orc.forward(Q, K, V, h, w, s, 0.5)
+    O2, _, _ = orc.forward(Q, K + u, V, h, w, s, 0.5)
+    assert np.allclose(O1, O2, rtol=0, atol=1e-12)
+
+
+def pin_joint_key_value_permutation(orc):
+    rng = _rng(42)
+    h, w, d, s = 6, 8, 6, 2
+    Q, K, V = (rng.standard_normal((2, 2, h * w, d)) for _ in range(3))
+    p = rng.permutation(h * w)
+    O1, _, _ = orc.forward(Q, K, V, h, w, s, 0.5)
+    O2, _, _ = orc.forward(Q, K[:, :, p], V[:, :, p], h, w, s, 0.5)
+    assert np.allclose(O1, O2, rtol=0, atol=1e-12)
+
+
+def pin_agent_permutation(orc):
+    rng = _rng(43)
+    h, w, d, s = 6, 6, 6, 3
+    Q, K, V = (rng.standard_normal((1, 2, h * w, d)) for _ in range(3))
+    A = rng.standard_normal((1, 2, s * s, d))
+    p = rng.permutation(s * s)
+    O1, _, _ = orc.forward(Q, K, V, h, w, s, 0.7, A=A)
+    O2, _, _ = orc.forward(Q, K, V, h, w, s, 0.7, A=A[:, :, p])
+    assert np.allclose(O1, O2, rtol=0, atol=1e-12)
+
+
+def pin_outputs_are_convex_combinations(orc):
+    rng = _rng(44)
+    h, w, d, s = 8, 8, 7, 4
+    Q, K = (3 * rng.standard_normal((2, 2, h * w, d)) for _ in range(2))
+    V = rng.standard_normal((2, 2, h * w, d))
+    O, _, VA = orc.forward(Q, K, V, h, w, s, 0.8)
+    lo = V.min(axis=2, keepdims=True) - 1e-12
+    hi = V.max(axis=2, keepdims=True) + 1e-12
+    assert np.all((VA >= lo) & (VA <= hi))
+    assert np.all((O >= lo) & (O <= hi))
+
+
+# ---------------------------------------------------------------- brute force
+
+def _softmax_loops(row):
+    mx = max(row)
+    e = [math.exp(x - mx) for x in row]
+    z = sum(e)
+    return [x / z for x in e]
+
+
+def pin_brute_force_generalised_linear_attention(orc):
+    """O = softmax(s Q A^T) softmax(s A K^T) V with the N x N product formed
+    explicitly, by loops, on tiny inputs; for pooled and supplied agents."""
+    rng = _rng(51)
+    h, w, d, s, scale = 4, 6, 3, 2, 0.9
+    N, k = h * w, s * s
+    Q, K, V = (1.5 * rng.standard_normal((1, 1, N, d)) for _ in range(3))
+    for A in (None, rng.standard_normal((1, 1, k, d))):
+        O, A_used, _ = orc.forward(Q, K, V, h, w, s, scale, A=A)
+        a = A_used[0, 0]
+        q, kk, v = Q[0, 0], K[0, 0], V[0, 0]
+        phi_q = [_softmax_loops([scale * sum(q[n, c] * a[i, c] for c in range(d))
+                                 for i in range(k)]) for n in range(N)]
+        phi_k = [_softmax_loops([scale * sum(a[i, c] * kk[m, c] for c in range(d))
+                                 for m in range(N)]) for i in range(k)]
+        M = [[sum(phi_q[n][i] * phi_k[i][m] for i in range(k)) for m in range(N)]
+             for n in range(N)]
+        ref = [[sum(M[n][m] * v[m, c] for m in range(N)) for c in range(d)]
+               for n in range(N)]
+        assert np.allclose(O[0, 0], ref, rtol=0, atol=1e-12)
+
+
+ALL_PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_")]

@@ -1,0 +1,218 @@
+"""Planted mistakes in the oracle must be caught (CPU only).
+
+Each mutant replaces one function of the oracle module with a plausible wrong
+version (a dropped term, a wrong sign, axis or index, a transposed operand);
+at least one pin must then fail.  A second group shows that the parity
+criterion used against the GPU rejects wrong outputs at the workloads' shapes
+on the discriminating inputs, while it accepts the rounding that a correct
+bf16 kernel performs.
+"""
+import numpy as np
+import pytest
+
+from oracle import agent_oracle as orc
+from tests import oracle_pins, parity
+from efficient_attention_vision_amd import inputs
+
+
+def _pool_column_major(Q, h, w, s):
+    B, H, N, d = Q.shape
+    grid = Q.reshape(B, H, w, h, d).swapaxes(2, 3)      # token n read as c*h + r
+    A = np.empty((B, H, s * s, d))
+    for i in range(s):
+        r0, r1 = orc.window_bounds(i, h, s)
+        for j in range(s):
+            c0, c1 = orc.window_bounds(j, w, s)
+            A[:, :, i * s + j] = grid[:, :, r0:r1, c0:c1].mean(axis=(2, 3))
+    return A
+
+
+def _window_floor(i, n, s):
+    """window stop rounded down instead of up."""
+    return (i * n) // s, max(((i + 1) * n) // s, (i * n) // s + 1)
+
+
+def _pool_sum(Q, h, w, s):
+    B, H, N, d = Q.shape
+    grid = Q.reshape(B, H, h, w, d)
+    A = np.empty((B, H, s * s, d))
+    for i in range(s):
+        r0, r1 = orc.window_bounds(i, h, s)
+        for j in range(s):
+            c0, c1 = orc.window_bounds(j, w, s)
+            A[:, :, i * s + j] = grid[:, :, r0:r1, c0:c1].sum(axis=(2, 3))
+    return A
+
+
+def _agg_no_scale(A, K, V, scale):
+    return orc.softmax_last(A @ np.swapaxes(K, -1, -2)) @ V
+
+
+def _agg_wrong_axis(A, K, V, scale):
+    S = scale * (A @ np.swapaxes(K, -1, -2))
+    E = np.exp(S - S.max(axis=-2, keepdims=True))
+    return (E / E.sum(axis=-2, keepdims=True)) @ V
+
+
+def _agg_scale_twice(A, K, V, scale):
+    return orc.softmax_last(scale * scale * (A @ np.swapaxes(K, -1, -2))) @ V
+
+
+def _bc_values_as_keys(Q, A, VA, scale):
+    """the garbled broadcast of one blog post: keys V_A, no scale."""
+    return orc.softmax_last(Q @ np.swapaxes(VA, -1, -2)) @ VA
+
+
+def _bc_wrong_axis(Q, A, VA, scale):
+    S = scale * (Q @ np.swapaxes(A, -1, -2))
+    E = np.exp(S - S.max(axis=-2, keepdims=True))
+    return (E / E.sum(axis=-2, keepdims=True)) @ VA
+
+
+def _bc_no_scale(Q, A, VA, scale):
+    return orc.softmax_last(Q @ np.swapaxes(A, -1, -2)) @ VA
+
+
+def _softmax_neg(S):
+    E = np.exp(-S - (-S).max(axis=-1, keepdims=True))
+    return E / E.sum(axis=-1, keepdims=True)
+
+
+def _softmax_norm_by_max(S):
+    E = np.exp(S - S.max(axis=-1, keepdims=True))
+    return E / E.max(axis=-1, keepdims=True)
+
+
+def _softmax_no_norm(S):
+    return np.exp(S - S.max(axis=-1, keepdims=True))
+
+
+def _forward_swap_kv(Q, K, V, h, w, s, scale, A=None):
+    Q, K, V = (np.asarray(x, float) for x in (Q, K, V))
+    A = orc.pool_agents(Q, h, w, s) if A is None else np.asarray(A, float)
+    VA = orc.aggregate(A, V, K, scale)
+    return orc.broadcast(Q, A, VA, scale), A, VA
+
+
+def _forward_agents_as_values(Q, K, V, h, w, s, scale, A=None):
+    Q, K, V = (np.asarray(x, float) for x in (Q, K, V))
+    A = orc.pool_agents(Q, h, w, s) if A is None else np.asarray(A, float)
+    VA = orc.aggregate(A, K, V, scale)
+    return orc.broadcast(Q, A, A, scale), A, VA
+
+
+def _forward_pool_keys(Q, K, V, h, w, s, scale, A=None):
+    Q, K, V = (np.asarray(x, float) for x in (Q, K, V))
+    A = orc.pool_agents(K, h, w, s) if A is None else np.asarray(A, float)
+    VA = orc.aggregate(A, K, V, scale)
+    return orc.broadcast(Q, A, VA, scale), A, VA
+
+
+def _forward_skip_aggregation(Q, K, V, h, w, s, scale, A=None):
+    """a dropped step: broadcast straight from pooled values."""
+    Q, K, V = (np.asarray(x, float) for x in (Q, K, V))
+    A = orc.pool_agents(Q, h, w, s) if A is None else np.asarray(A, float)
+    VA = orc.pool_agents(V, h, w, s)
+    return orc.broadcast(Q, A, VA, scale), A, VA
+
+
+MUTANTS = {
+    "pool_column_major": ("pool_agents", _pool_column_major),
+    "window_floor_stop": ("window_bounds", _window_floor),
+    "pool_sum_not_mean": ("pool_agents", _pool_sum),
+    "aggregate_no_scale": ("aggregate", _agg_no_scale),
+    "aggregate_softmax_over_agents": ("aggregate", _agg_wrong_axis),
+    "aggregate_scale_twice": ("aggregate", _agg_scale_twice),
+    "broadcast_values_as_keys": ("broadcast", _bc_values_as_keys),
+    "broadcast_softmax_over_tokens": ("broadcast", _bc_wrong_axis),
+    "broadcast_no_scale": ("broadcast", _bc_no_scale),
+    "softmax_negated": ("softmax_last", _softmax_neg),
+    "softmax_divided_by_max": ("softmax_last", _softmax_norm_by_max),
+    "softmax_unnormalised": ("softmax_last", _softmax_no_norm),
+    "forward_swaps_keys_values": ("forward", _forward_swap_kv),
+    "forward_agents_as_values": ("forward", _forward_agents_as_values),
+    "forward_pools_keys": ("forward", _forward_pool_keys),
+    "forward_skips_aggregation": ("forward", _forward_skip_aggregation),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(orc, attr, fn)
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(orc)
+        except (AssertionError, ValueError, IndexError, ZeroDivisionError):
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches mutant {name}"
+
+
+# ----------------------------------------------- power of the parity criterion
+
+def _bf16(x):
+    return inputs.f32_from_bf16_bits(inputs.bf16_bits_from_f32(
+        np.asarray(x, np.float32))).astype(np.float64)
+
+
+def _emulated_bf16_kernel(Q, K, V, h, w, s, scale, A=None):
+    """What a correct kernel is allowed to round: agents, both probability
+    matrices and V_A as bf16 matrix-core operands, and O itself."""
+    A = orc.pool_agents(Q, h, w, s) if A is None else A
+    Ab = _bf16(A)
+    P1 = orc.softmax_last(scale * (Ab @ np.swapaxes(K, -1, -2)))
+    VA = _bf16(P1) @ V
+    P2 = orc.softmax_last(scale * (Q @ np.swapaxes(Ab, -1, -2)))
+    return _bf16(_bf16(P2) @ _bf16(VA))
+
+
+@pytest.fixture(scope="module", params=["deit_s", "pvt_stage1", "sd_unet", "sd_unet_agents"])
+def workload_case(request):
+    wl = inputs.WORKLOADS[request.param]
+    inp = inputs.make_inputs(wl, 0, "discriminating")
+    args = (inp.Q.exact, inp.K.exact, inp.V.exact, wl.h, wl.w, wl.s, wl.scale)
+    A = None if inp.A is None else inp.A.exact
+    O, _, _ = orc.forward(*args, A=A)
+    return wl, args, A, O
+
+
+def test_discriminating_inputs_have_order_one_outputs(workload_case):
+    wl, args, A, O = workload_case
+    assert np.abs(O).max() > 0.5
+
+
+def test_correct_bf16_rounding_passes(workload_case):
+    wl, args, A, O = workload_case
+    parity.assert_close(_emulated_bf16_kernel(*args, A=A), O, "bf16", wl.name,
+                        kind="discriminating")
+
+
+WRONG_OUTPUTS = {
+    "zeros": lambda args, A: np.zeros_like(args[0]),
+    "no_scale": lambda args, A: orc.forward(*args[:-1], 1.0, A=A)[0],
+    "values_as_broadcast_keys": lambda args, A: _bc_values_as_keys(
+        args[0], None, orc.forward(*args, A=A)[2], args[-1]),
+    "broadcast_softmax_over_tokens": lambda args, A: _bc_wrong_axis(
+        args[0], *orc.forward(*args, A=A)[1:], args[-1]),
+    # (column-major pooling is not listed: on the square grids of these
+    # workloads it only renumbers the agents, which O cannot see; the pins
+    # catch it on non-square grids)
+    "agents_pooled_from_keys": lambda args, A: orc.broadcast(
+        args[0], orc.pool_agents(args[1], *args[3:6]),
+        orc.aggregate(orc.pool_agents(args[1], *args[3:6]), args[1], args[2], args[-1]),
+        args[-1]) if A is None else None,
+    "unnormalised_broadcast": lambda args, A: _softmax_no_norm(
+        args[-1] * (args[0] @ np.swapaxes(orc.forward(*args, A=A)[1], -1, -2)))
+        @ orc.forward(*args, A=A)[2],
+}
+
+
+@pytest.mark.parametrize("wrong", sorted(WRONG_OUTPUTS))
+def test_criterion_rejects_wrong_outputs(workload_case, wrong):
+    wl, args, A, O = workload_case
+    out = WRONG_OUTPUTS[wrong](args, A)
+    if out is None:
+        pytest.skip("pooling is bypassed when agents are supplied")
+    assert not parity.close(out, O, "bf16", kind="discriminating"), \
+        f"{wrong} passes on {wl.name}"
