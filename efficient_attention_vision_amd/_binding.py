@@ -1,0 +1,256 @@
+"""ctypes binding of libagent_attn.so (argument marshalling only).
+
+Every step of the forward runs in the library's HIP kernels; this module
+only turns torch tensors into pointers and sizes, picks torch's current
+stream, allocates the workspace through torch's caching allocator and maps
+status codes to exceptions.  There is no fallback: without the built library
+every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libagent_attn.so")
+
+F32, BF16 = 0, 1
+OK = 0
+_VALIDATION = {-1, -2, -3, -4, -5, -6, -7, -8}
+
+_c_int, _c_size, _c_float, _vp = ctypes.c_int, ctypes.c_size_t, ctypes.c_float, ctypes.c_void_p
+
+_SIGNATURES = {
+    "agent_attn_workspace_bytes": (_c_size, [_c_int] * 7),
+    "agent_attn_forward": (_c_int, [_vp] * 5 + [_c_int] * 6 + [_c_float, _c_int, _vp]),
+    "agent_attn_forward_ws": (_c_int, [_vp] * 5 + [_c_int] * 6 + [_c_float, _c_int, _vp, _c_size,
+                                                                  _vp]),
+    "agent_attn_pool": (_c_int, [_vp, _vp] + [_c_int] * 7 + [_vp]),
+    "agent_attn_aggregate_workspace_bytes": (_c_size, [_c_int] * 6),
+    "agent_attn_aggregate": (_c_int, [_vp] * 4 + [_c_int] * 5 + [_c_float, _c_int, _vp, _c_size,
+                                                                 _vp]),
+    "agent_attn_broadcast": (_c_int, [_vp] * 4 + [_c_int] * 5 + [_c_float, _c_int, _vp]),
+    "agent_attn_release": (None, []),
+    "agent_attn_status_string": (ctypes.c_char_p, [_c_int]),
+    "agent_attn_last_error": (ctypes.c_char_p, []),
+}
+
+EXPORTED = tuple(_SIGNATURES)
+
+_lib = None
+
+
+class AgentAttnError(RuntimeError):
+    """A HIP failure reported by the library."""
+
+
+def lib() -> ctypes.CDLL:
+    """Load the shared library once (after torch, so that both use the same
+    HIP runtime).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m efficient_attention_vision_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(rc: int) -> None:
+    if rc == OK:
+        return
+    L = lib()
+    msg = f"{L.agent_attn_status_string(rc).decode()}: {L.agent_attn_last_error().decode()}"
+    if rc in _VALIDATION:
+        raise ValueError(msg)
+    raise AgentAttnError(msg)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise ValueError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _dev_tensor(t, name, ndim=4):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+    return t
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _same(ref, t, name, shape=None, dtype=None):
+    if t.device != ref.device:
+        raise ValueError(f"{name} is on {t.device}, expected {ref.device}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def agent_attn_workspace_bytes(B, H, h, w, d, s, dtype_code) -> int:
+    return int(lib().agent_attn_workspace_bytes(B, H, h, w, d, s, dtype_code))
+
+
+def agent_attn_forward(q, k, v, grid_hw, s, scale=None, agents=None, out=None, workspace=None):
+    """O = softmax(scale Q A^T) softmax(scale A K^T) V with A = 2-D average
+    pool of Q to s x s agents (or `agents` [B, H, s*s, d]).
+
+    q, k, v: [B, H, h*w, d] float32 or bfloat16 GPU tensors; grid_hw = (h, w).
+    Runs on torch's current stream; returns `out` ([B, H, h*w, d], q's dtype).
+    """
+    L = lib()
+    _dev_tensor(q, "q")
+    B, H, N, d = q.shape
+    h, w = (int(x) for x in grid_hw)
+    if h * w != N:
+        raise ValueError(f"grid {h}x{w} does not match N={N}")
+    for name, t in (("k", k), ("v", v)):
+        _dev_tensor(t, name)
+        _same(q, t, name, q.shape, q.dtype)
+    if agents is not None:
+        _dev_tensor(agents, "agents")
+        _same(q, agents, "agents", (B, H, int(s) * int(s), d), q.dtype)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _dev_tensor(out, "out")
+        _same(q, out, "out", q.shape, q.dtype)
+    code = _dtype_code(q)
+    with torch.cuda.device(q.device):
+        need = L.agent_attn_workspace_bytes(B, H, h, w, d, int(s), code)
+        ws_ptr, ws_size = None, 0
+        if need > 0:      # 0: invalid sizes (reported by the call) or an empty batch
+            if workspace is None:
+                workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            ws_ptr, ws_size = _ptr(workspace), workspace.numel() * workspace.element_size()
+        rc = L.agent_attn_forward_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(agents), B, H, h,
+                                     w, d, int(s), float(scale), code, ws_ptr, ws_size,
+                                     _stream(q.device))
+    _check(rc)
+    return out
+
+
+def agent_attn_forward_cached(q, k, v, grid_hw, s, scale=None, agents=None, out=None):
+    """agent_attn_forward through the library's own cached workspace."""
+    L = lib()
+    _dev_tensor(q, "q")
+    B, H, N, d = q.shape
+    h, w = (int(x) for x in grid_hw)
+    if h * w != N:
+        raise ValueError(f"grid {h}x{w} does not match N={N}")
+    for name, t in (("k", k), ("v", v)):
+        _dev_tensor(t, name)
+        _same(q, t, name, q.shape, q.dtype)
+    if agents is not None:
+        _dev_tensor(agents, "agents")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = torch.empty_like(q) if out is None else out
+    with torch.cuda.device(q.device):
+        rc = L.agent_attn_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(agents), B, H, h, w,
+                                  d, int(s), float(scale), _dtype_code(q), _stream(q.device))
+    _check(rc)
+    return out
+
+
+def agent_attn_pool(q, grid_hw, s, out=None):
+    """float32 agents [B, H, s*s, d] = 2-D average pool of q over its h x w grid."""
+    L = lib()
+    _dev_tensor(q, "q")
+    B, H, N, d = q.shape
+    h, w = (int(x) for x in grid_hw)
+    if h * w != N:
+        raise ValueError(f"grid {h}x{w} does not match N={N}")
+    if out is None:
+        out = torch.empty((B, H, int(s) * int(s), d), dtype=torch.float32, device=q.device)
+    else:
+        _dev_tensor(out, "out")
+        _same(q, out, "out", (B, H, int(s) * int(s), d), torch.float32)
+    with torch.cuda.device(q.device):
+        rc = L.agent_attn_pool(_ptr(q), _ptr(out), B, H, h, w, d, int(s), _dtype_code(q),
+                               _stream(q.device))
+    _check(rc)
+    return out
+
+
+def agent_attn_aggregate(agents_f32, k, v, scale, out=None):
+    """float32 V_A [B, H, n_agents, d] = softmax(scale agents k^T) v."""
+    L = lib()
+    _dev_tensor(k, "k")
+    B, H, N, d = k.shape
+    _dev_tensor(v, "v")
+    _same(k, v, "v", k.shape, k.dtype)
+    _dev_tensor(agents_f32, "agents_f32")
+    if agents_f32.shape[:2] != (B, H) or agents_f32.shape[3] != d:
+        raise ValueError(f"agents_f32 shape {tuple(agents_f32.shape)} does not match k")
+    _same(k, agents_f32, "agents_f32", dtype=torch.float32)
+    nag = agents_f32.shape[2]
+    if out is None:
+        out = torch.empty_like(agents_f32)
+    else:
+        _dev_tensor(out, "out")
+        _same(k, out, "out", agents_f32.shape, torch.float32)
+    code = _dtype_code(k)
+    with torch.cuda.device(k.device):
+        need = L.agent_attn_aggregate_workspace_bytes(B, H, N, d, nag, code)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=k.device)
+        rc = L.agent_attn_aggregate(_ptr(agents_f32), _ptr(k), _ptr(v), _ptr(out), B, H, N, d,
+                                    nag, float(scale), code, _ptr(ws), ws.numel(),
+                                    _stream(k.device))
+    _check(rc)
+    return out
+
+
+def agent_attn_broadcast(q, agents_f32, agent_values_f32, scale, out=None):
+    """out [B, H, N, d] (q's dtype) = softmax(scale q agents^T) agent_values."""
+    L = lib()
+    _dev_tensor(q, "q")
+    B, H, N, d = q.shape
+    for name, t in (("agents_f32", agents_f32), ("agent_values_f32", agent_values_f32)):
+        _dev_tensor(t, name)
+        _same(q, t, name, dtype=torch.float32)
+    nag = agents_f32.shape[2]
+    if tuple(agents_f32.shape) != (B, H, nag, d) or agent_values_f32.shape != agents_f32.shape:
+        raise ValueError("agents_f32 and agent_values_f32 must both be [B, H, n_agents, d]")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _dev_tensor(out, "out")
+        _same(q, out, "out", q.shape, q.dtype)
+    with torch.cuda.device(q.device):
+        rc = L.agent_attn_broadcast(_ptr(q), _ptr(agents_f32), _ptr(agent_values_f32), _ptr(out),
+                                    B, H, N, d, nag, float(scale), _dtype_code(q),
+                                    _stream(q.device))
+    _check(rc)
+    return out
+
+
+def agent_attn_release() -> None:
+    lib().agent_attn_release()

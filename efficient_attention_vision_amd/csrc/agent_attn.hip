@@ -1,0 +1,450 @@
+// Host side of the Agent Attention C ABI (include/agent_attn.h): argument
+// validation, workspace layout, kernel selection and launches on the
+// caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "agent_attn.h"
+#include "common.hpp"
+#include "kernels_scalar.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(AGENT_ATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int elem_size(int dtype) { return dtype == AGENT_ATTN_F32 ? 4 : 2; }
+
+bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+bool misaligned(const void* p) { return p && ((uintptr_t)p & 15u) != 0; }
+
+// Sizes shared by every entry point.
+struct Dims {
+  long B = 0, H = 0, BH = 0;
+  long N = 0;
+  int h = 0, w = 0, d = 0, s = 0, nag = 0, dtype = 0;
+};
+
+int check_dtype(int dtype) {
+  if (dtype != AGENT_ATTN_F32 && dtype != AGENT_ATTN_BF16)
+    return fail(AGENT_ATTN_ERR_DTYPE, "dtype %d is neither AGENT_ATTN_F32 nor AGENT_ATTN_BF16",
+                dtype);
+  return AGENT_ATTN_OK;
+}
+
+// Validates B, H, N, d, n_agents, dtype (not the grid).
+int check_core(Dims& D, int B, int H, long N, int d, int nag, int dtype) {
+  int st = check_dtype(dtype);
+  if (st) return st;
+  if (B < 0 || H < 0) return fail(AGENT_ATTN_ERR_SHAPE, "B=%d and H=%d must be >= 0", B, H);
+  if (N < 1) return fail(AGENT_ATTN_ERR_SHAPE, "token count N=%ld must be >= 1", N);
+  if (d < 1) return fail(AGENT_ATTN_ERR_SHAPE, "head dim d=%d must be >= 1", d);
+  if (nag < 1) return fail(AGENT_ATTN_ERR_SHAPE, "agent count %d must be >= 1", nag);
+  if (d % 8 != 0 || d > AGENT_ATTN_MAX_HEAD_DIM)
+    return fail(AGENT_ATTN_ERR_UNSUPPORTED, "head dim d=%d: need d %% 8 == 0 and d <= %d", d,
+                AGENT_ATTN_MAX_HEAD_DIM);
+  if (nag > AGENT_ATTN_MAX_AGENTS)
+    return fail(AGENT_ATTN_ERR_UNSUPPORTED, "%d agents exceed the limit of %d", nag,
+                AGENT_ATTN_MAX_AGENTS);
+  const long BH = (long)B * H;
+  if (BH >= (1L << 23))
+    return fail(AGENT_ATTN_ERR_SHAPE, "B*H=%ld must be below 2^23", BH);
+  if (BH * N * d >= (1L << 40))
+    return fail(AGENT_ATTN_ERR_SHAPE, "B*H*N*d=%ld elements exceed 2^40", BH * N * d);
+  D.B = B;
+  D.H = H;
+  D.BH = BH;
+  D.N = N;
+  D.d = d;
+  D.nag = nag;
+  D.dtype = dtype;
+  return AGENT_ATTN_OK;
+}
+
+int check_grid(Dims& D, int B, int H, int h, int w, int d, int s, int dtype) {
+  if (h < 1 || w < 1) return fail(AGENT_ATTN_ERR_SHAPE, "grid %dx%d must be at least 1x1", h, w);
+  if (h > 32768 || w > 32768)
+    return fail(AGENT_ATTN_ERR_SHAPE, "grid %dx%d: each side must be <= 32768", h, w);
+  if (s < 1 || s > h || s > w)
+    return fail(AGENT_ATTN_ERR_SHAPE, "agent grid side s=%d must satisfy 1 <= s <= min(h=%d, w=%d)",
+                s, h, w);
+  if (s * s > AGENT_ATTN_MAX_AGENTS)
+    return fail(AGENT_ATTN_ERR_UNSUPPORTED, "s*s=%d agents exceed the limit of %d", s * s,
+                AGENT_ATTN_MAX_AGENTS);
+  int st = check_core(D, B, H, (long)h * w, d, s * s, dtype);
+  if (st) return st;
+  D.h = h;
+  D.w = w;
+  D.s = s;
+  return AGENT_ATTN_OK;
+}
+
+int check_scale(float scale) {
+  if (!std::isfinite(scale) || !(scale > 0.f))
+    return fail(AGENT_ATTN_ERR_SCALE, "scale %g must be finite and > 0", (double)scale);
+  return AGENT_ATTN_OK;
+}
+
+// ---------------------------------------------------------------- plans
+// Workspace layout of the forward:
+//   [A  fp32 BH*k*d][V_A fp32 BH*k*d][split-N partials BH*nchunks*k*(d+2)]
+struct Plan {
+  int chunk = 0, nchunks = 0;
+  size_t off_A = 0, off_VA = 0, off_part = 0, bytes = 0;
+};
+
+void aggregate_split(const Dims& D, int& chunk, int& nchunks) {
+  // Enough blocks to give every one of the 256 CUs two of them, but at
+  // least 64 tokens per block.
+  long want = (512 + D.BH - 1) / D.BH;
+  long maxc = (D.N + 63) / 64;
+  long nc = want < maxc ? want : maxc;
+  if (nc < 1) nc = 1;
+  long ch = (D.N + nc - 1) / nc;
+  ch = (ch + 31) / 32 * 32;
+  chunk = (int)ch;
+  nchunks = (int)((D.N + ch - 1) / ch);
+}
+
+size_t partial_bytes(const Dims& D, int nchunks) {
+  return (size_t)D.BH * nchunks * D.nag * (D.d + 2) * sizeof(float);
+}
+
+Plan make_plan(const Dims& D) {
+  Plan P;
+  aggregate_split(D, P.chunk, P.nchunks);
+  const size_t ad = (size_t)D.BH * D.nag * D.d * sizeof(float);
+  P.off_A = 0;
+  P.off_VA = align_up(P.off_A + ad, 256);
+  P.off_part = align_up(P.off_VA + ad, 256);
+  P.bytes = align_up(P.off_part + partial_bytes(D, P.nchunks), 256);
+  return P;
+}
+
+// ------------------------------------------------------------- launches
+#define AA_LAUNCH_CHECK(what)                      \
+  do {                                             \
+    hipError_t e_ = hipGetLastError();             \
+    if (e_ != hipSuccess) return hip_fail(e_, what); \
+  } while (0)
+
+template <typename T>
+int launch_pool(const Dims& D, const void* q, float* A, hipStream_t st) {
+  const long blocks = D.BH * D.nag;
+  hipLaunchKernelGGL(aa::pool_kernel<T>, dim3((unsigned)blocks), dim3(256), 0, st,
+                     (const T*)q, A, D.h, D.w, D.d, D.s);
+  AA_LAUNCH_CHECK("agent_pool launch");
+  return AGENT_ATTN_OK;
+}
+
+template <typename T>
+int launch_widen(const Dims& D, const void* src, float* dst, hipStream_t st) {
+  const long n = D.BH * D.nag * D.d;
+  long blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(aa::widen_kernel<T>, dim3((unsigned)blocks), dim3(256), 0, st,
+                     (const T*)src, dst, n);
+  AA_LAUNCH_CHECK("agent widen launch");
+  return AGENT_ATTN_OK;
+}
+
+template <typename T>
+int launch_aggregate(const Dims& D, const float* A, const void* k, const void* v, float* VA,
+                     float* part, int chunk, int nchunks, float sl2, hipStream_t st) {
+  const long blocks = D.BH * nchunks;
+  if (D.d <= 64)
+    hipLaunchKernelGGL((aa::aggregate_partial_scalar<T, 64>), dim3((unsigned)blocks), dim3(256), 0,
+                       st, A, (const T*)k, (const T*)v, part, (int)D.N, D.d, D.nag, sl2, chunk,
+                       nchunks);
+  else
+    hipLaunchKernelGGL((aa::aggregate_partial_scalar<T, 128>), dim3((unsigned)blocks), dim3(256),
+                       0, st, A, (const T*)k, (const T*)v, part, (int)D.N, D.d, D.nag, sl2, chunk,
+                       nchunks);
+  AA_LAUNCH_CHECK("agent_aggregate launch");
+  hipLaunchKernelGGL(aa::merge_partials_kernel, dim3((unsigned)(D.BH * D.nag)), dim3(128), 0, st,
+                     part, VA, D.d, D.nag, nchunks);
+  AA_LAUNCH_CHECK("agent_aggregate merge launch");
+  return AGENT_ATTN_OK;
+}
+
+template <typename T>
+int launch_broadcast(const Dims& D, const void* q, const float* A, const float* VA, void* out,
+                     float sl2, hipStream_t st) {
+  const int nqblk = (int)((D.N + 255) / 256);
+  const long blocks = D.BH * nqblk;
+  if (D.d <= 64)
+    hipLaunchKernelGGL((aa::broadcast_scalar<T, 64>), dim3((unsigned)blocks), dim3(256), 0, st,
+                       (const T*)q, A, VA, (T*)out, (int)D.N, D.d, D.nag, sl2, nqblk);
+  else
+    hipLaunchKernelGGL((aa::broadcast_scalar<T, 128>), dim3((unsigned)blocks), dim3(256), 0, st,
+                       (const T*)q, A, VA, (T*)out, (int)D.N, D.d, D.nag, sl2, nqblk);
+  AA_LAUNCH_CHECK("agent_broadcast launch");
+  return AGENT_ATTN_OK;
+}
+
+template <typename T>
+int run_forward(const Dims& D, const Plan& P, const void* q, const void* k, const void* v,
+                void* out, const void* agents, float scale, char* ws, hipStream_t st) {
+  float* A = (float*)(ws + P.off_A);
+  float* VA = (float*)(ws + P.off_VA);
+  float* part = (float*)(ws + P.off_part);
+  const float sl2 = scale * aa::kLog2e;
+  int rc = agents ? launch_widen<T>(D, agents, A, st) : launch_pool<T>(D, q, A, st);
+  if (rc) return rc;
+  rc = launch_aggregate<T>(D, A, k, v, VA, part, P.chunk, P.nchunks, sl2, st);
+  if (rc) return rc;
+  return launch_broadcast<T>(D, q, A, VA, out, sl2, st);
+}
+
+int validate_forward(Dims& D, const void* q, const void* k, const void* v, void* out,
+                     const void* agents, int B, int H, int h, int w, int d, int s, float scale,
+                     int dtype) {
+  int rc = check_grid(D, B, H, h, w, d, s, dtype);
+  if (rc) return rc;
+  rc = check_scale(scale);
+  if (rc) return rc;
+  if (!q || !k || !v || !out)
+    return fail(AGENT_ATTN_ERR_NULL, "q, k, v and out must be non-NULL");
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(out) || misaligned(agents))
+    return fail(AGENT_ATTN_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  const size_t tb = (size_t)D.BH * D.N * D.d * elem_size(dtype);
+  const size_t ab = (size_t)D.BH * D.nag * D.d * elem_size(dtype);
+  if (ranges_overlap(out, tb, q, tb) || ranges_overlap(out, tb, k, tb) ||
+      ranges_overlap(out, tb, v, tb) || ranges_overlap(out, tb, agents, ab))
+    return fail(AGENT_ATTN_ERR_ALIAS, "out overlaps an input tensor");
+  return AGENT_ATTN_OK;
+}
+
+int dispatch_forward(const Dims& D, const Plan& P, const void* q, const void* k, const void* v,
+                     void* out, const void* agents, float scale, void* ws, hipStream_t st) {
+  if (D.dtype == AGENT_ATTN_F32)
+    return run_forward<float>(D, P, q, k, v, out, agents, scale, (char*)ws, st);
+  return run_forward<aa::bf16_t>(D, P, q, k, v, out, agents, scale, (char*)ws, st);
+}
+
+// Per-device grow-only scratch for agent_attn_forward.
+std::mutex g_ws_mutex;
+std::vector<std::pair<void*, size_t>> g_ws;
+
+int cached_workspace(size_t bytes, void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  if ((int)g_ws.size() <= dev) g_ws.resize(dev + 1, {nullptr, 0});
+  auto& slot = g_ws[dev];
+  if (slot.second < bytes) {
+    if (slot.first) {
+      e = hipDeviceSynchronize();
+      if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize before workspace growth");
+      e = hipFree(slot.first);
+      slot = {nullptr, 0};
+      if (e != hipSuccess) return hip_fail(e, "hipFree of the old workspace");
+    }
+    void* p = nullptr;
+    e = hipMalloc(&p, bytes);
+    if (e != hipSuccess) return hip_fail(e, "hipMalloc of the workspace");
+    slot = {p, bytes};
+  }
+  *ptr = slot.first;
+  return AGENT_ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t agent_attn_workspace_bytes(int B, int H, int h, int w, int d, int s, int dtype) {
+  Dims D;
+  if (check_grid(D, B, H, h, w, d, s, dtype)) return 0;
+  if (D.BH == 0) return 0;
+  return make_plan(D).bytes;
+}
+
+int agent_attn_forward_ws(const void* q, const void* k, const void* v, void* out,
+                          const void* agents, int B, int H, int h, int w, int d, int s,
+                          float scale, int dtype, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  Dims D;
+  int rc = validate_forward(D, q, k, v, out, agents, B, H, h, w, d, s, scale, dtype);
+  if (rc) return rc;
+  if (D.BH == 0) return AGENT_ATTN_OK;
+  const Plan P = make_plan(D);
+  if (!workspace || workspace_bytes < P.bytes)
+    return fail(AGENT_ATTN_ERR_WORKSPACE, "workspace of %zu bytes at %p; %zu bytes needed",
+                workspace_bytes, workspace, P.bytes);
+  if (((uintptr_t)workspace & 255u) != 0)
+    return fail(AGENT_ATTN_ERR_ALIGN, "workspace must be 256-byte aligned");
+  const size_t tb = (size_t)D.BH * D.N * D.d * elem_size(dtype);
+  const size_t ab = (size_t)D.BH * D.nag * D.d * elem_size(dtype);
+  if (ranges_overlap(workspace, P.bytes, q, tb) || ranges_overlap(workspace, P.bytes, k, tb) ||
+      ranges_overlap(workspace, P.bytes, v, tb) || ranges_overlap(workspace, P.bytes, out, tb) ||
+      ranges_overlap(workspace, P.bytes, agents, ab))
+    return fail(AGENT_ATTN_ERR_ALIAS, "workspace overlaps a tensor argument");
+  return dispatch_forward(D, P, q, k, v, out, agents, scale, workspace, (hipStream_t)stream);
+}
+
+int agent_attn_forward(const void* q, const void* k, const void* v, void* out,
+                       const void* agents, int B, int H, int h, int w, int d, int s, float scale,
+                       int dtype, void* stream) {
+  Dims D;
+  int rc = validate_forward(D, q, k, v, out, agents, B, H, h, w, d, s, scale, dtype);
+  if (rc) return rc;
+  if (D.BH == 0) return AGENT_ATTN_OK;
+  const Plan P = make_plan(D);
+  void* ws = nullptr;
+  rc = cached_workspace(P.bytes, &ws);
+  if (rc) return rc;
+  return dispatch_forward(D, P, q, k, v, out, agents, scale, ws, (hipStream_t)stream);
+}
+
+int agent_attn_pool(const void* q, float* agents_f32, int B, int H, int h, int w, int d, int s,
+                    int dtype, void* stream) {
+  Dims D;
+  int rc = check_grid(D, B, H, h, w, d, s, dtype);
+  if (rc) return rc;
+  if (D.BH == 0) return AGENT_ATTN_OK;
+  if (!q || !agents_f32) return fail(AGENT_ATTN_ERR_NULL, "q and agents_f32 must be non-NULL");
+  if (misaligned(q) || misaligned(agents_f32))
+    return fail(AGENT_ATTN_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  if (ranges_overlap(agents_f32, (size_t)D.BH * D.nag * D.d * 4, q,
+                     (size_t)D.BH * D.N * D.d * elem_size(dtype)))
+    return fail(AGENT_ATTN_ERR_ALIAS, "agents_f32 overlaps q");
+  hipStream_t st = (hipStream_t)stream;
+  return dtype == AGENT_ATTN_F32 ? launch_pool<float>(D, q, agents_f32, st)
+                                 : launch_pool<aa::bf16_t>(D, q, agents_f32, st);
+}
+
+size_t agent_attn_aggregate_workspace_bytes(int B, int H, int N, int d, int n_agents, int dtype) {
+  Dims D;
+  if (check_core(D, B, H, N, d, n_agents, dtype)) return 0;
+  if (D.BH == 0) return 0;
+  int chunk, nchunks;
+  aggregate_split(D, chunk, nchunks);
+  return align_up(partial_bytes(D, nchunks), 256);
+}
+
+int agent_attn_aggregate(const float* agents_f32, const void* k, const void* v,
+                         float* agent_values_f32, int B, int H, int N, int d, int n_agents,
+                         float scale, int dtype, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  Dims D;
+  int rc = check_core(D, B, H, N, d, n_agents, dtype);
+  if (rc) return rc;
+  rc = check_scale(scale);
+  if (rc) return rc;
+  if (D.BH == 0) return AGENT_ATTN_OK;
+  if (!agents_f32 || !k || !v || !agent_values_f32)
+    return fail(AGENT_ATTN_ERR_NULL, "agents_f32, k, v and agent_values_f32 must be non-NULL");
+  if (misaligned(agents_f32) || misaligned(k) || misaligned(v) || misaligned(agent_values_f32))
+    return fail(AGENT_ATTN_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  int chunk, nchunks;
+  aggregate_split(D, chunk, nchunks);
+  const size_t need = align_up(partial_bytes(D, nchunks), 256);
+  if (!workspace || workspace_bytes < need)
+    return fail(AGENT_ATTN_ERR_WORKSPACE, "workspace of %zu bytes at %p; %zu bytes needed",
+                workspace_bytes, workspace, need);
+  const size_t tb = (size_t)D.BH * D.N * D.d * elem_size(dtype);
+  const size_t ab = (size_t)D.BH * D.nag * D.d * 4;
+  if (ranges_overlap(agent_values_f32, ab, agents_f32, ab) ||
+      ranges_overlap(agent_values_f32, ab, k, tb) || ranges_overlap(agent_values_f32, ab, v, tb) ||
+      ranges_overlap(workspace, need, agents_f32, ab) || ranges_overlap(workspace, need, k, tb) ||
+      ranges_overlap(workspace, need, v, tb) ||
+      ranges_overlap(workspace, need, agent_values_f32, ab))
+    return fail(AGENT_ATTN_ERR_ALIAS, "an output or the workspace overlaps an input");
+  const float sl2 = scale * aa::kLog2e;
+  hipStream_t st = (hipStream_t)stream;
+  float* part = (float*)workspace;
+  return dtype == AGENT_ATTN_F32
+             ? launch_aggregate<float>(D, agents_f32, k, v, agent_values_f32, part, chunk,
+                                       nchunks, sl2, st)
+             : launch_aggregate<aa::bf16_t>(D, agents_f32, k, v, agent_values_f32, part, chunk,
+                                            nchunks, sl2, st);
+}
+
+int agent_attn_broadcast(const void* q, const float* agents_f32, const float* agent_values_f32,
+                         void* out, int B, int H, int N, int d, int n_agents, float scale,
+                         int dtype, void* stream) {
+  Dims D;
+  int rc = check_core(D, B, H, N, d, n_agents, dtype);
+  if (rc) return rc;
+  rc = check_scale(scale);
+  if (rc) return rc;
+  if (D.BH == 0) return AGENT_ATTN_OK;
+  if (!q || !agents_f32 || !agent_values_f32 || !out)
+    return fail(AGENT_ATTN_ERR_NULL, "q, agents_f32, agent_values_f32 and out must be non-NULL");
+  if (misaligned(q) || misaligned(agents_f32) || misaligned(agent_values_f32) || misaligned(out))
+    return fail(AGENT_ATTN_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  const size_t tb = (size_t)D.BH * D.N * D.d * elem_size(dtype);
+  const size_t ab = (size_t)D.BH * D.nag * D.d * 4;
+  if (ranges_overlap(out, tb, q, tb) || ranges_overlap(out, tb, agents_f32, ab) ||
+      ranges_overlap(out, tb, agent_values_f32, ab))
+    return fail(AGENT_ATTN_ERR_ALIAS, "out overlaps an input tensor");
+  const float sl2 = scale * aa::kLog2e;
+  hipStream_t st = (hipStream_t)stream;
+  return dtype == AGENT_ATTN_F32
+             ? launch_broadcast<float>(D, q, agents_f32, agent_values_f32, out, sl2, st)
+             : launch_broadcast<aa::bf16_t>(D, q, agents_f32, agent_values_f32, out, sl2, st);
+}
+
+void agent_attn_release(void) {
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) cur = -1;
+  for (size_t dev = 0; dev < g_ws.size(); ++dev) {
+    if (!g_ws[dev].first) continue;
+    if (hipSetDevice((int)dev) == hipSuccess) {
+      (void)hipDeviceSynchronize();
+      (void)hipFree(g_ws[dev].first);
+    }
+    g_ws[dev] = {nullptr, 0};
+  }
+  if (cur >= 0) (void)hipSetDevice(cur);
+}
+
+const char* agent_attn_status_string(int status) {
+  switch (status) {
+    case AGENT_ATTN_OK: return "ok";
+    case AGENT_ATTN_ERR_NULL: return "a required pointer is NULL";
+    case AGENT_ATTN_ERR_SHAPE: return "a size is out of range";
+    case AGENT_ATTN_ERR_DTYPE: return "unknown dtype";
+    case AGENT_ATTN_ERR_UNSUPPORTED: return "head dim or agent count outside the supported limits";
+    case AGENT_ATTN_ERR_SCALE: return "scale must be finite and > 0";
+    case AGENT_ATTN_ERR_ALIAS: return "an output overlaps an input";
+    case AGENT_ATTN_ERR_ALIGN: return "a pointer is not sufficiently aligned";
+    case AGENT_ATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case AGENT_ATTN_ERR_HIP: return "a HIP runtime call failed";
+    default: return "unknown status";
+  }
+}
+
+const char* agent_attn_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,34 @@
+// Shared device helpers of the Agent Attention kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "agent_attn.h"
+
+namespace aa {
+
+typedef uint16_t bf16_t;  // bfloat16 storage
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kMaxD = AGENT_ATTN_MAX_HEAD_DIM;
+constexpr int kMaxAgents = AGENT_ATTN_MAX_AGENTS;
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16_t x) {
+  return __uint_as_float(static_cast<uint32_t>(x) << 16);
+}
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float x);
+template <>
+__device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <>
+__device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) {
+  // v_cvt_pk_bf16_f32: round to nearest even
+  return __builtin_bit_cast(bf16_t, static_cast<__bf16>(x));
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace aa

@@ -1,0 +1,140 @@
+/*
+ * agent_attn.h -- C ABI of the MI355X (gfx950) Agent Attention forward.
+ *
+ * The operation (sources: the web pages
+ *   "Agent Attention: On the Integration of Softmax and Linear Attention"
+ *   (paperlayer.ai summary of arXiv 2312.08874v3), Abstract, §4 Agent
+ *   Transformer and §6 Conclusion; and
+ *   "Agent Attention：Transformer计算量太大？试试这个'代理令牌'的轻量化方案"
+ *   (jsqmd.com), §1 pseudocode and §2):
+ *
+ *   For every batch b and head h independently, with Q, K, V of shape
+ *   [N, d] over a row-major h x w token grid (token n = r*w + c):
+ *     1. agents   A   = 2-D average pool of Q down to an s x s grid, k = s*s
+ *                       (agent i*s+j averages grid rows
+ *                       [floor(i*h/s), ceil((i+1)*h/s)) and columns
+ *                       [floor(j*w/s), ceil((j+1)*w/s))), or caller-supplied;
+ *     2. aggregation  V_A = softmax(scale * A K^T) V      (softmax over N)
+ *     3. broadcast    O   = softmax(scale * Q A^T) V_A    (softmax over k)
+ *   Both steps are ordinary Softmax attentions; together they form the
+ *   generalised linear attention phi_q(Q) phi_k(K)^T V of §4.
+ *
+ * Layout: every tensor is dense, row-major, contiguous:
+ *   q, k, v, out : [B, H, N, d]      (N = h*w)
+ *   agents       : [B, H, k, d]      (k = s*s, or n_agents in the step calls)
+ *   agents_f32 / agent_values_f32 in the step calls: float32 [B, H, k, d].
+ * Element type of q, k, v, out and caller agents: `dtype` (float32 or
+ * bfloat16).  Arithmetic is float32 (bf16 inputs feed the matrix cores,
+ * accumulation is float32, O is rounded to bf16 with round-to-nearest-even).
+ *
+ * Pointers: device pointers (hipMalloc/torch CUDA tensors) of the current
+ * device, 16-byte aligned.  The library never frees or retains them.
+ * `stream` is a hipStream_t (NULL = the default stream); all work is
+ * enqueued on it asynchronously and the call returns once it is enqueued.
+ *
+ * Errors: every argument is validated on the host before any HIP call; a
+ * failed check returns a negative status and enqueues nothing.  Kernel
+ * launch failures return AGENT_ATTN_ERR_HIP.  Faults inside kernels surface
+ * at the caller's next synchronisation.  agent_attn_last_error() gives a
+ * message for the calling thread's last failure.  Non-finite inputs are not
+ * checked and propagate.  B == 0 or H == 0 is an empty batch: nothing is
+ * enqueued and AGENT_ATTN_OK is returned.
+ *
+ * Limits: 1 <= s <= min(h, w); s*s <= 256 agents; d % 8 == 0, 8 <= d <= 128;
+ * B*H*N*d < 2^40 elements; scale finite and > 0.
+ *
+ * Thread safety: all entry points may be called from several threads.
+ * Calls that share a workspace buffer must be ordered on one stream.
+ */
+#ifndef AGENT_ATTN_H_
+#define AGENT_ATTN_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  AGENT_ATTN_F32 = 0,
+  AGENT_ATTN_BF16 = 1
+} agent_attn_dtype_t;
+
+typedef enum {
+  AGENT_ATTN_OK = 0,
+  AGENT_ATTN_ERR_NULL = -1,        /* a required pointer is NULL */
+  AGENT_ATTN_ERR_SHAPE = -2,       /* a size is out of range */
+  AGENT_ATTN_ERR_DTYPE = -3,       /* unknown dtype */
+  AGENT_ATTN_ERR_UNSUPPORTED = -4, /* d or agent count outside the limits */
+  AGENT_ATTN_ERR_SCALE = -5,       /* scale not finite or not > 0 */
+  AGENT_ATTN_ERR_ALIAS = -6,       /* an output overlaps an input */
+  AGENT_ATTN_ERR_ALIGN = -7,       /* a pointer is not 16-byte aligned */
+  AGENT_ATTN_ERR_WORKSPACE = -8,   /* workspace NULL or too small */
+  AGENT_ATTN_ERR_HIP = -9          /* a HIP call failed */
+} agent_attn_status_t;
+
+#define AGENT_ATTN_MAX_AGENTS 256
+#define AGENT_ATTN_MAX_HEAD_DIM 128
+
+/* Bytes of device scratch the forward needs for these sizes (0 when
+ * B*H == 0).  Returns 0 and sets the last error for invalid sizes. */
+size_t agent_attn_workspace_bytes(int B, int H, int h, int w, int d, int s,
+                                  int dtype);
+
+/* Full forward: pool (when agents == NULL) -> aggregate -> broadcast.
+ * agents: NULL, or caller-supplied agents [B, H, s*s, d] of `dtype`.
+ * Uses a per-device scratch buffer that the library allocates on first use
+ * and grows as needed (hipMalloc; freed by agent_attn_release).  Calls on
+ * different streams of one device that overlap in time share that buffer
+ * and therefore race: use agent_attn_forward_ws for concurrent streams. */
+int agent_attn_forward(const void* q, const void* k, const void* v, void* out,
+                       const void* agents, int B, int H, int h, int w, int d,
+                       int s, float scale, int dtype, void* stream);
+
+/* Same as agent_attn_forward with caller-owned scratch of at least
+ * agent_attn_workspace_bytes(...) bytes, 256-byte aligned.  The
+ * workspace is overwritten; it must not overlap any tensor argument.  The
+ * call allocates nothing. */
+int agent_attn_forward_ws(const void* q, const void* k, const void* v,
+                          void* out, const void* agents, int B, int H, int h,
+                          int w, int d, int s, float scale, int dtype,
+                          void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* Step 1 alone: agents_f32 [B, H, s*s, d] (float32) = 2-D average pool of q. */
+int agent_attn_pool(const void* q, float* agents_f32, int B, int H, int h,
+                    int w, int d, int s, int dtype, void* stream);
+
+/* Scratch bytes that agent_attn_aggregate needs for these sizes. */
+size_t agent_attn_aggregate_workspace_bytes(int B, int H, int N, int d,
+                                            int n_agents, int dtype);
+
+/* Step 2 alone: agent_values_f32 [B, H, n_agents, d] (float32) =
+ * softmax(scale * agents_f32 k^T) v, with k, v [B, H, N, d] of `dtype`.
+ * Any 1 <= n_agents <= 256. */
+int agent_attn_aggregate(const float* agents_f32, const void* k, const void* v,
+                         float* agent_values_f32, int B, int H, int N, int d,
+                         int n_agents, float scale, int dtype, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* Step 3 alone: out [B, H, N, d] (`dtype`) =
+ * softmax(scale * q agents_f32^T) agent_values_f32. */
+int agent_attn_broadcast(const void* q, const float* agents_f32,
+                         const float* agent_values_f32, void* out, int B,
+                         int H, int N, int d, int n_agents, float scale,
+                         int dtype, void* stream);
+
+/* Frees the library's cached per-device scratch buffers. */
+void agent_attn_release(void);
+
+/* Static description of a status code. */
+const char* agent_attn_status_string(int status);
+
+/* Message describing the calling thread's last failed call ("" if none). */
+const char* agent_attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AGENT_ATTN_H_ */

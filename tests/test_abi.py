@@ -1,0 +1,119 @@
+"""The C ABI without a GPU: the library loads, exports every declared entry
+point, and rejects bad arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from efficient_attention_vision_amd import _binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "agent_attn.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_UNSUP, ERR_SCALE, ERR_ALIAS, ERR_ALIGN, ERR_WS = (
+    0, -1, -2, -3, -4, -5, -6, -7, -8)
+
+# fake, never dereferenced device addresses: validation fails before any use
+P = [ctypes.c_void_p(0x7f0000000000 + i * (1 << 32)) for i in range(8)]
+WS = ctypes.c_void_p(0x7f1000000000)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(agent_attn_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return _binding.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(_binding.EXPORTED)
+
+
+def fwd(L, *, q=P[0], k=P[1], v=P[2], out=P[3], agents=None, B=2, H=3, h=8, w=8, d=64, s=4,
+        scale=0.125, dtype=1, ws=WS, ws_bytes=1 << 40):
+    return L.agent_attn_forward_ws(q, k, v, out, agents, B, H, h, w, d, s, scale, dtype, ws,
+                                   ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), ERR_NULL),
+    (dict(out=None), ERR_NULL),
+    (dict(B=-1), ERR_SHAPE),
+    (dict(h=0), ERR_SHAPE),
+    (dict(s=0), ERR_SHAPE),
+    (dict(s=9), ERR_SHAPE),                  # s > h
+    (dict(h=40, w=40, s=17), ERR_UNSUP),     # 289 agents
+    (dict(d=12), ERR_UNSUP),
+    (dict(d=136), ERR_UNSUP),
+    (dict(d=0), ERR_SHAPE),
+    (dict(dtype=7), ERR_DTYPE),
+    (dict(scale=0.0), ERR_SCALE),
+    (dict(scale=float("nan")), ERR_SCALE),
+    (dict(scale=float("inf")), ERR_SCALE),
+    (dict(scale=-1.0), ERR_SCALE),
+    (dict(out=P[0]), ERR_ALIAS),
+    (dict(out=ctypes.c_void_p(P[1].value + 64)), ERR_ALIAS),
+    (dict(q=ctypes.c_void_p(P[0].value + 8)), ERR_ALIGN),
+    (dict(ws=None), ERR_WS),
+    (dict(ws_bytes=100), ERR_WS),
+    (dict(ws=ctypes.c_void_p(WS.value + 16)), ERR_ALIGN),
+    (dict(ws=P[1]), ERR_ALIAS),
+    (dict(B=1 << 20, H=16), ERR_SHAPE),       # B*H >= 2^23
+])
+def test_forward_validation(L, kw, code):
+    assert fwd(L, **kw) == code
+    assert L.agent_attn_last_error().decode() != ""
+
+
+def test_empty_batch_is_a_no_op(L):
+    assert fwd(L, B=0) == OK
+    assert fwd(L, H=0, ws=None, ws_bytes=0) == OK
+    assert L.agent_attn_workspace_bytes(0, 4, 8, 8, 64, 4, 1) == 0
+
+
+def test_workspace_bytes(L):
+    assert L.agent_attn_workspace_bytes(16, 1, 56, 56, 64, 7, 1) > 0
+    assert L.agent_attn_workspace_bytes(16, 1, 56, 56, 12, 7, 1) == 0     # invalid d
+    assert L.agent_attn_workspace_bytes(16, 1, 56, 56, 64, 7, 9) == 0     # invalid dtype
+
+
+def test_step_entry_points_validate(L):
+    assert L.agent_attn_pool(P[0], None, 1, 1, 8, 8, 64, 2, 1, None) == ERR_NULL
+    assert L.agent_attn_pool(P[0], P[1], 1, 1, 8, 8, 64, 9, 1, None) == ERR_SHAPE
+    assert L.agent_attn_pool(P[0], P[0], 1, 1, 8, 8, 64, 2, 1, None) == ERR_ALIAS
+    assert L.agent_attn_aggregate(P[0], P[1], P[2], P[3], 1, 1, 64, 64, 300, 0.1, 1, WS, 1 << 30,
+                                  None) == ERR_UNSUP
+    assert L.agent_attn_aggregate(P[0], P[1], P[2], P[3], 1, 1, 64, 64, 16, 0.1, 1, WS, 10,
+                                  None) == ERR_WS
+    assert L.agent_attn_aggregate(P[0], P[1], P[2], P[1], 1, 1, 64, 64, 16, 0.1, 1, WS, 1 << 30,
+                                  None) == ERR_ALIAS
+    assert L.agent_attn_broadcast(P[0], P[1], P[2], P[0], 1, 1, 64, 64, 16, 0.1, 1,
+                                  None) == ERR_ALIAS
+    assert L.agent_attn_broadcast(P[0], P[1], P[2], P[3], 1, 1, 0, 64, 16, 0.1, 1,
+                                  None) == ERR_SHAPE
+    assert L.agent_attn_broadcast(P[0], P[1], P[2], P[3], 1, 1, 64, 64, 16, 0.0, 1,
+                                  None) == ERR_SCALE
+    assert L.agent_attn_aggregate_workspace_bytes(2, 2, 1000, 64, 49, 1) > 0
+
+
+def test_status_strings(L):
+    for code in range(-9, 1):
+        assert L.agent_attn_status_string(code).decode() not in ("", "unknown status")
+    assert L.agent_attn_status_string(-100).decode() == "unknown status"
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    import efficient_attention_vision_amd as eav
+    q = torch.zeros(1, 1, 4, 8)
+    with pytest.raises(ValueError):
+        eav.agent_attn_forward(q, q, q, (2, 2), 1)
