@@ -112,6 +112,22 @@ def _same(ref, t, name, shape=None, dtype=None):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
+_ws_cache: dict = {}
+
+
+def cached_workspace(device, nbytes: int) -> torch.Tensor:
+    """A zero-initialised workspace of at least `nbytes` for torch's current
+    stream on `device`, reused across calls on that stream (the library
+    leaves its synchronisation counters at zero after every call)."""
+    device = torch.device(device)
+    key = (device.index, torch.cuda.current_stream(device).cuda_stream)
+    t = _ws_cache.get(key)
+    if t is None or t.numel() < nbytes:
+        t = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        _ws_cache[key] = t
+    return t
+
+
 def agent_attn_workspace_bytes(B, H, h, w, d, s, dtype_code) -> int:
     return int(lib().agent_attn_workspace_bytes(B, H, h, w, d, s, dtype_code))
 
@@ -148,7 +164,7 @@ def agent_attn_forward(q, k, v, grid_hw, s, scale=None, agents=None, out=None, w
         ws_ptr, ws_size = None, 0
         if need > 0:      # 0: invalid sizes (reported by the call) or an empty batch
             if workspace is None:
-                workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+                workspace = cached_workspace(q.device, need)
             ws_ptr, ws_size = _ptr(workspace), workspace.numel() * workspace.element_size()
         rc = L.agent_attn_forward_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(agents), B, H, h,
                                      w, d, int(s), float(scale), code, ws_ptr, ws_size,

@@ -13,6 +13,7 @@
 
 #include "agent_attn.h"
 #include "common.hpp"
+#include "kernels_mfma.hpp"
 #include "kernels_scalar.hpp"
 
 namespace {
@@ -113,12 +114,20 @@ int check_scale(float scale) {
 }
 
 // ---------------------------------------------------------------- plans
-// Workspace layout of the forward:
-//   [A  fp32 BH*k*d][V_A fp32 BH*k*d][split-N partials BH*nchunks*k*(d+2)]
+// Workspace layout of the forward (every region 256-byte aligned):
+//   [sync counters BH * 512 B, zero between calls][status 256 B]
+//   [A fp32 BH*k*d][V_A fp32 BH*k*d][partials]
+// float32 I/O: partials are BH*nchunks*k*(d+2) floats of the scalar split-N
+// aggregation; bfloat16 I/O: BH*k*P*(d+2) floats of the matrix-core kernel.
 struct Plan {
+  // scalar path
   int chunk = 0, nchunks = 0;
-  size_t off_A = 0, off_VA = 0, off_part = 0, bytes = 0;
+  // matrix-core path
+  int DC = 0, P = 1, T = 0, fused = 1, xcd_heads = 0, lds = 0;
+  size_t off_sync = 0, off_status = 0, off_A = 0, off_VA = 0, off_part = 0, bytes = 0;
 };
+
+constexpr size_t kSyncBytesPerHead = (aa::kBarriers + 1) * aa::kSyncStride * sizeof(unsigned);
 
 void aggregate_split(const Dims& D, int& chunk, int& nchunks) {
   // Enough blocks to give every one of the 256 CUs two of them, but at
@@ -133,18 +142,68 @@ void aggregate_split(const Dims& D, int& chunk, int& nchunks) {
   nchunks = (int)((D.N + ch - 1) / ch);
 }
 
-size_t partial_bytes(const Dims& D, int nchunks) {
-  return (size_t)D.BH * nchunks * D.nag * (D.d + 2) * sizeof(float);
+int mfma_lds_bytes(int DC, int nag) {
+  switch (DC) {
+    case 1: return aa::LdsPlan<1>(nag).total;
+    case 2: return aa::LdsPlan<2>(nag).total;
+    case 3: return aa::LdsPlan<3>(nag).total;
+    default: return aa::LdsPlan<4>(nag).total;
+  }
 }
 
-Plan make_plan(const Dims& D) {
+// Number of compute units of the current device (cached per device).
+int device_cus() {
+  static std::mutex mu;
+  static std::vector<int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)cache.size() <= dev) cache.resize(dev + 1, 0);
+  if (cache[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    cache[dev] = cus;
+  }
+  return cache[dev];
+}
+
+// Split of each head over P workgroups of T tokens (T a multiple of 16):
+// P = floor(CUs / BH), so that the P workgroups of every head fit on the
+// chip at once (one per compute unit) and can meet at group barriers.
+void mfma_split(const Dims& D, int cus, int& P, int& T) {
+  long p = D.BH >= cus ? 1 : cus / D.BH;
+  const long maxp = (D.N + 15) / 16;
+  if (p > maxp) p = maxp;
+  if (p < 1) p = 1;
+  long t = (D.N + p - 1) / p;
+  t = (t + 15) / 16 * 16;
+  P = (int)((D.N + t - 1) / t);
+  T = (int)t;
+}
+
+Plan make_plan(const Dims& D, int cus) {
   Plan P;
-  aggregate_split(D, P.chunk, P.nchunks);
+  size_t part_bytes;
+  if (D.dtype == AGENT_ATTN_F32) {
+    aggregate_split(D, P.chunk, P.nchunks);
+    part_bytes = (size_t)D.BH * P.nchunks * D.nag * (D.d + 2) * sizeof(float);
+  } else {
+    P.DC = (D.d + 31) / 32;
+    mfma_split(D, cus, P.P, P.T);
+    P.lds = mfma_lds_bytes(P.DC, D.nag);
+    P.fused = 1;  // BH*P <= CUs: the whole grid is co-resident
+    P.xcd_heads = (P.P > 1 && D.BH % 8 == 0 && cus % 8 == 0) ? (int)(D.BH / 8) : 0;
+    part_bytes = (size_t)D.BH * D.nag * P.P * (D.d + 2) * sizeof(float);
+  }
   const size_t ad = (size_t)D.BH * D.nag * D.d * sizeof(float);
-  P.off_A = 0;
+  P.off_sync = 0;
+  P.off_status = align_up((size_t)D.BH * kSyncBytesPerHead, 256);
+  P.off_A = P.off_status + 256;
   P.off_VA = align_up(P.off_A + ad, 256);
   P.off_part = align_up(P.off_VA + ad, 256);
-  P.bytes = align_up(P.off_part + partial_bytes(D, P.nchunks), 256);
+  P.bytes = align_up(P.off_part + part_bytes, 256);
   return P;
 }
 
@@ -209,6 +268,87 @@ int launch_broadcast(const Dims& D, const void* q, const float* A, const float* 
   return AGENT_ATTN_OK;
 }
 
+// ------------------------------------------------------ matrix-core path
+template <int DC>
+int launch_mfma_dc(const aa::MfmaParams& mp, long grid, int lds, hipStream_t st) {
+  static std::once_flag once;
+  static hipError_t attr_err = hipSuccess;
+  std::call_once(once, [] {
+    attr_err = hipFuncSetAttribute((const void*)aa::agent_mfma_kernel<DC>,
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  });
+  if (attr_err != hipSuccess) return hip_fail(attr_err, "hipFuncSetAttribute (dynamic LDS)");
+  hipLaunchKernelGGL(aa::agent_mfma_kernel<DC>, dim3((unsigned)grid), dim3(aa::kThreads),
+                     (unsigned)lds, st, mp);
+  AA_LAUNCH_CHECK("agent attention matrix-core kernel launch");
+  return AGENT_ATTN_OK;
+}
+
+int launch_mfma(int DC, const aa::MfmaParams& mp, long grid, int lds, hipStream_t st) {
+  switch (DC) {
+    case 1: return launch_mfma_dc<1>(mp, grid, lds, st);
+    case 2: return launch_mfma_dc<2>(mp, grid, lds, st);
+    case 3: return launch_mfma_dc<3>(mp, grid, lds, st);
+    default: return launch_mfma_dc<4>(mp, grid, lds, st);
+  }
+}
+
+aa::MfmaParams mfma_params(const Dims& D, int P, int T, float scale) {
+  aa::MfmaParams mp{};
+  mp.BH = (int)D.BH;
+  mp.N = (int)D.N;
+  mp.h = D.h;
+  mp.w = D.w;
+  mp.d = D.d;
+  mp.s = D.s;
+  mp.nag = D.nag;
+  mp.P = P;
+  mp.T = T;
+  mp.sl2 = scale * aa::kLog2e;
+  return mp;
+}
+
+// Runs `phases` either in one fused launch or as one launch per phase.
+int run_mfma_phases(const Dims& D, aa::MfmaParams mp, int DC, int phases, bool fused,
+                    hipStream_t st) {
+  const int lds = mfma_lds_bytes(DC, D.nag);
+  const long grid = D.BH * mp.P;
+  if (fused) {
+    mp.phases = phases;
+    mp.fused = 1;
+    return launch_mfma(DC, mp, grid, lds, st);
+  }
+  mp.fused = 0;
+  mp.xcd_heads = 0;
+  for (int ph : {aa::PH_POOL, aa::PH_AGG, aa::PH_MERGE, aa::PH_BCAST}) {
+    if (!(phases & ph)) continue;
+    if (ph == aa::PH_MERGE && mp.P == 1) continue;
+    mp.phases = ph;
+    const int rc = launch_mfma(DC, mp, grid, lds, st);
+    if (rc) return rc;
+  }
+  return AGENT_ATTN_OK;
+}
+
+int run_forward_mfma(const Dims& D, const Plan& P, const void* q, const void* k, const void* v,
+                     void* out, const void* agents, float scale, char* ws, hipStream_t st) {
+  aa::MfmaParams mp = mfma_params(D, P.P, P.T, scale);
+  mp.q = (const aa::bf16_t*)q;
+  mp.k = (const aa::bf16_t*)k;
+  mp.v = (const aa::bf16_t*)v;
+  mp.out = (aa::bf16_t*)out;
+  mp.agents_in = (const aa::bf16_t*)agents;
+  mp.agents_f32 = (float*)(ws + P.off_A);
+  mp.values_f32 = (float*)(ws + P.off_VA);
+  mp.part = (float*)(ws + P.off_part);
+  mp.sync = (unsigned*)(ws + P.off_sync);
+  mp.status = (int*)(ws + P.off_status);
+  mp.xcd_heads = P.xcd_heads;
+  const int phases =
+      (agents ? 0 : aa::PH_POOL) | aa::PH_AGG | aa::PH_MERGE | aa::PH_BCAST;
+  return run_mfma_phases(D, mp, P.DC, phases, P.fused != 0, st);
+}
+
 template <typename T>
 int run_forward(const Dims& D, const Plan& P, const void* q, const void* k, const void* v,
                 void* out, const void* agents, float scale, char* ws, hipStream_t st) {
@@ -230,6 +370,7 @@ int validate_forward(Dims& D, const void* q, const void* k, const void* v, void*
   if (rc) return rc;
   rc = check_scale(scale);
   if (rc) return rc;
+  if (D.BH == 0) return AGENT_ATTN_OK;  // empty batch: tensors may be NULL
   if (!q || !k || !v || !out)
     return fail(AGENT_ATTN_ERR_NULL, "q, k, v and out must be non-NULL");
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(out) || misaligned(agents))
@@ -246,7 +387,7 @@ int dispatch_forward(const Dims& D, const Plan& P, const void* q, const void* k,
                      void* out, const void* agents, float scale, void* ws, hipStream_t st) {
   if (D.dtype == AGENT_ATTN_F32)
     return run_forward<float>(D, P, q, k, v, out, agents, scale, (char*)ws, st);
-  return run_forward<aa::bf16_t>(D, P, q, k, v, out, agents, scale, (char*)ws, st);
+  return run_forward_mfma(D, P, q, k, v, out, agents, scale, (char*)ws, st);
 }
 
 // Per-device grow-only scratch for agent_attn_forward.
@@ -271,10 +412,26 @@ int cached_workspace(size_t bytes, void** ptr) {
     void* p = nullptr;
     e = hipMalloc(&p, bytes);
     if (e != hipSuccess) return hip_fail(e, "hipMalloc of the workspace");
+    e = hipMemset(p, 0, bytes);  // the sync counters must start at zero
+    if (e != hipSuccess) {
+      (void)hipFree(p);
+      return hip_fail(e, "hipMemset of the workspace");
+    }
     slot = {p, bytes};
   }
   *ptr = slot.first;
   return AGENT_ATTN_OK;
+}
+
+size_t aggregate_ws_bytes(const Dims& D) {
+  if (D.dtype == AGENT_ATTN_F32) {
+    int chunk, nchunks;
+    aggregate_split(D, chunk, nchunks);
+    return align_up((size_t)D.BH * nchunks * D.nag * (D.d + 2) * sizeof(float), 256);
+  }
+  int P, T;
+  mfma_split(D, device_cus(), P, T);
+  return align_up((size_t)D.BH * D.nag * P * (D.d + 2) * sizeof(float), 256);
 }
 
 }  // namespace
@@ -285,7 +442,7 @@ size_t agent_attn_workspace_bytes(int B, int H, int h, int w, int d, int s, int 
   Dims D;
   if (check_grid(D, B, H, h, w, d, s, dtype)) return 0;
   if (D.BH == 0) return 0;
-  return make_plan(D).bytes;
+  return make_plan(D, device_cus()).bytes;
 }
 
 int agent_attn_forward_ws(const void* q, const void* k, const void* v, void* out,
@@ -296,7 +453,7 @@ int agent_attn_forward_ws(const void* q, const void* k, const void* v, void* out
   int rc = validate_forward(D, q, k, v, out, agents, B, H, h, w, d, s, scale, dtype);
   if (rc) return rc;
   if (D.BH == 0) return AGENT_ATTN_OK;
-  const Plan P = make_plan(D);
+  const Plan P = make_plan(D, device_cus());
   if (!workspace || workspace_bytes < P.bytes)
     return fail(AGENT_ATTN_ERR_WORKSPACE, "workspace of %zu bytes at %p; %zu bytes needed",
                 workspace_bytes, workspace, P.bytes);
@@ -318,7 +475,7 @@ int agent_attn_forward(const void* q, const void* k, const void* v, void* out,
   int rc = validate_forward(D, q, k, v, out, agents, B, H, h, w, d, s, scale, dtype);
   if (rc) return rc;
   if (D.BH == 0) return AGENT_ATTN_OK;
-  const Plan P = make_plan(D);
+  const Plan P = make_plan(D, device_cus());
   void* ws = nullptr;
   rc = cached_workspace(P.bytes, &ws);
   if (rc) return rc;
@@ -338,17 +495,18 @@ int agent_attn_pool(const void* q, float* agents_f32, int B, int H, int h, int w
                      (size_t)D.BH * D.N * D.d * elem_size(dtype)))
     return fail(AGENT_ATTN_ERR_ALIAS, "agents_f32 overlaps q");
   hipStream_t st = (hipStream_t)stream;
-  return dtype == AGENT_ATTN_F32 ? launch_pool<float>(D, q, agents_f32, st)
-                                 : launch_pool<aa::bf16_t>(D, q, agents_f32, st);
+  if (dtype == AGENT_ATTN_F32) return launch_pool<float>(D, q, agents_f32, st);
+  aa::MfmaParams mp = mfma_params(D, 1, (int)D.N, 1.0f);
+  mp.q = (const aa::bf16_t*)q;
+  mp.agents_f32 = agents_f32;
+  return run_mfma_phases(D, mp, (D.d + 31) / 32, aa::PH_POOL, false, st);
 }
 
 size_t agent_attn_aggregate_workspace_bytes(int B, int H, int N, int d, int n_agents, int dtype) {
   Dims D;
   if (check_core(D, B, H, N, d, n_agents, dtype)) return 0;
   if (D.BH == 0) return 0;
-  int chunk, nchunks;
-  aggregate_split(D, chunk, nchunks);
-  return align_up(partial_bytes(D, nchunks), 256);
+  return aggregate_ws_bytes(D);
 }
 
 int agent_attn_aggregate(const float* agents_f32, const void* k, const void* v,
@@ -365,9 +523,7 @@ int agent_attn_aggregate(const float* agents_f32, const void* k, const void* v,
     return fail(AGENT_ATTN_ERR_NULL, "agents_f32, k, v and agent_values_f32 must be non-NULL");
   if (misaligned(agents_f32) || misaligned(k) || misaligned(v) || misaligned(agent_values_f32))
     return fail(AGENT_ATTN_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
-  int chunk, nchunks;
-  aggregate_split(D, chunk, nchunks);
-  const size_t need = align_up(partial_bytes(D, nchunks), 256);
+  const size_t need = aggregate_ws_bytes(D);
   if (!workspace || workspace_bytes < need)
     return fail(AGENT_ATTN_ERR_WORKSPACE, "workspace of %zu bytes at %p; %zu bytes needed",
                 workspace_bytes, workspace, need);
@@ -382,11 +538,21 @@ int agent_attn_aggregate(const float* agents_f32, const void* k, const void* v,
   const float sl2 = scale * aa::kLog2e;
   hipStream_t st = (hipStream_t)stream;
   float* part = (float*)workspace;
-  return dtype == AGENT_ATTN_F32
-             ? launch_aggregate<float>(D, agents_f32, k, v, agent_values_f32, part, chunk,
-                                       nchunks, sl2, st)
-             : launch_aggregate<aa::bf16_t>(D, agents_f32, k, v, agent_values_f32, part, chunk,
-                                            nchunks, sl2, st);
+  if (dtype == AGENT_ATTN_F32) {
+    int chunk, nchunks;
+    aggregate_split(D, chunk, nchunks);
+    return launch_aggregate<float>(D, agents_f32, k, v, agent_values_f32, part, chunk, nchunks,
+                                   sl2, st);
+  }
+  int P, T;
+  mfma_split(D, device_cus(), P, T);
+  aa::MfmaParams mp = mfma_params(D, P, T, scale);
+  mp.k = (const aa::bf16_t*)k;
+  mp.v = (const aa::bf16_t*)v;
+  mp.agents_f32_in = agents_f32;
+  mp.values_f32 = agent_values_f32;
+  mp.part = part;
+  return run_mfma_phases(D, mp, (D.d + 31) / 32, aa::PH_AGG | aa::PH_MERGE, false, st);
 }
 
 int agent_attn_broadcast(const void* q, const float* agents_f32, const float* agent_values_f32,
@@ -409,9 +575,16 @@ int agent_attn_broadcast(const void* q, const float* agents_f32, const float* ag
     return fail(AGENT_ATTN_ERR_ALIAS, "out overlaps an input tensor");
   const float sl2 = scale * aa::kLog2e;
   hipStream_t st = (hipStream_t)stream;
-  return dtype == AGENT_ATTN_F32
-             ? launch_broadcast<float>(D, q, agents_f32, agent_values_f32, out, sl2, st)
-             : launch_broadcast<aa::bf16_t>(D, q, agents_f32, agent_values_f32, out, sl2, st);
+  if (dtype == AGENT_ATTN_F32)
+    return launch_broadcast<float>(D, q, agents_f32, agent_values_f32, out, sl2, st);
+  int P, T;
+  mfma_split(D, device_cus(), P, T);
+  aa::MfmaParams mp = mfma_params(D, P, T, scale);
+  mp.q = (const aa::bf16_t*)q;
+  mp.out = (aa::bf16_t*)out;
+  mp.agents_f32_in = agents_f32;
+  mp.values_f32_in = agent_values_f32;
+  return run_mfma_phases(D, mp, (D.d + 31) / 32, aa::PH_BCAST, false, st);
 }
 
 void agent_attn_release(void) {

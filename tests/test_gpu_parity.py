@@ -157,3 +157,29 @@ def test_broadcast_step(wl):
                            wl.scale)
     parity.assert_close(to_host_f64(out), ref, wl.dtype, "broadcast " + wl.name,
                         kind="discriminating")
+
+
+def test_fused_counters_return_to_zero():
+    """Many fused launches on one caller workspace, alternating shapes: every
+    result matches the oracle and the group counters end at zero."""
+    from efficient_attention_vision_amd import _binding
+    wls = [inputs.WORKLOADS["pvt_stage1"], inputs.WORKLOADS["sd_unet"],
+           inputs.custom("p3", B=3, H=5, h=20, w=18, d=64, s=4)]
+    need = max(_binding.agent_attn_workspace_bytes(w.B, w.H, w.h, w.w, w.d, w.s, 1)
+               for w in wls)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    cases = []
+    for i, wl in enumerate(wls):
+        inp = inputs.make_inputs(wl, 10 + i, "discriminating")
+        O, _, _ = oracle.forward(inp.Q.exact, inp.K.exact, inp.V.exact, wl.h, wl.w, wl.s,
+                                 wl.scale)
+        cases.append((wl, [to_device(x) for x in (inp.Q, inp.K, inp.V)], O))
+    for rep in range(12):
+        wl, (q, k, v), O = cases[rep % len(cases)]
+        say(f"[fused repeat] {rep} {wl.name}")
+        out = eav.agent_attn_forward(q, k, v, (wl.h, wl.w), wl.s, wl.scale, workspace=ws)
+        torch.cuda.synchronize()
+        parity.assert_close(to_host_f64(out), O, "bf16", wl.name, kind="discriminating")
+    torch.cuda.synchronize()
+    max_bh = max(w.B * w.H for w in wls)
+    assert int(ws[: max_bh * 512].count_nonzero()) == 0     # counters
