@@ -115,7 +115,7 @@ int check_scale(float scale) {
 
 // ---------------------------------------------------------------- plans
 // Workspace layout of the forward (every region 256-byte aligned):
-//   [sync counters BH * 512 B, zero between calls][status 256 B]
+//   [group counters, 512 heads * 512 B, zero between calls][status 256 B]
 //   [A fp32 BH*k*d][V_A fp32 BH*k*d][partials]
 // float32 I/O: partials are BH*nchunks*k*(d+2) floats of the scalar split-N
 // aggregation; bfloat16 I/O: BH*k*P*(d+2) floats of the matrix-core kernel.
@@ -128,6 +128,12 @@ struct Plan {
 };
 
 constexpr size_t kSyncBytesPerHead = (aa::kBarriers + 1) * aa::kSyncStride * sizeof(unsigned);
+// Heads that can own group counters: P > 1 needs B*H*P <= CUs, so at most
+// CUs/2 heads.  The counters live in a fixed-size prefix of every workspace
+// so that calls of different shapes sharing one workspace never place other
+// scratch data on them.
+constexpr long kMaxSyncHeads = 512;
+constexpr size_t kSyncRegionBytes = kMaxSyncHeads * kSyncBytesPerHead;
 
 void aggregate_split(const Dims& D, int& chunk, int& nchunks) {
   // Enough blocks to give every one of the 256 CUs two of them, but at
@@ -173,7 +179,7 @@ int device_cus() {
 // P = floor(CUs / BH), so that the P workgroups of every head fit on the
 // chip at once (one per compute unit) and can meet at group barriers.
 void mfma_split(const Dims& D, int cus, int& P, int& T) {
-  long p = D.BH >= cus ? 1 : cus / D.BH;
+  long p = (D.BH >= cus || D.BH > kMaxSyncHeads) ? 1 : cus / D.BH;
   const long maxp = (D.N + 15) / 16;
   if (p > maxp) p = maxp;
   if (p < 1) p = 1;
@@ -199,7 +205,7 @@ Plan make_plan(const Dims& D, int cus) {
   }
   const size_t ad = (size_t)D.BH * D.nag * D.d * sizeof(float);
   P.off_sync = 0;
-  P.off_status = align_up((size_t)D.BH * kSyncBytesPerHead, 256);
+  P.off_status = kSyncRegionBytes;
   P.off_A = P.off_status + 256;
   P.off_VA = align_up(P.off_A + ad, 256);
   P.off_part = align_up(P.off_VA + ad, 256);
@@ -271,13 +277,6 @@ int launch_broadcast(const Dims& D, const void* q, const float* A, const float* 
 // ------------------------------------------------------ matrix-core path
 template <int DC>
 int launch_mfma_dc(const aa::MfmaParams& mp, long grid, int lds, hipStream_t st) {
-  static std::once_flag once;
-  static hipError_t attr_err = hipSuccess;
-  std::call_once(once, [] {
-    attr_err = hipFuncSetAttribute((const void*)aa::agent_mfma_kernel<DC>,
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-  });
-  if (attr_err != hipSuccess) return hip_fail(attr_err, "hipFuncSetAttribute (dynamic LDS)");
   hipLaunchKernelGGL(aa::agent_mfma_kernel<DC>, dim3((unsigned)grid), dim3(aa::kThreads),
                      (unsigned)lds, st, mp);
   AA_LAUNCH_CHECK("agent attention matrix-core kernel launch");

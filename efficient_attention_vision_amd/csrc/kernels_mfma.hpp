@@ -323,6 +323,16 @@ __device__ __forceinline__ void load_k_block(bf16x8 (&kf)[2][DC], const bf16_t* 
   }
 }
 
+// Eight consecutive bf16 channels of one token -> one column of Vt (rows
+// dst, dst + stride, ...).  Elements are taken out of the 32-bit words with
+// shifts so that each 16-bit store gets its own element.
+__device__ __forceinline__ void store_transposed8(bf16_t* dst, int stride, uint4 x) {
+  const unsigned w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    dst[e * stride] = static_cast<bf16_t>((w[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+}
+
 // Stage V[tok0, tok0+cnt) of the head transposed into LDS: Vt[ch][col].
 __device__ __forceinline__ void stage_v(bf16_t* Vt, int vt_stride, const bf16_t* Vh, int tok0,
                                         int cnt, int d) {
@@ -330,9 +340,8 @@ __device__ __forceinline__ void stage_v(bf16_t* Vt, int vt_stride, const bf16_t*
   const int total = cnt * DCH;
   for (int i = threadIdx.x; i < total; i += kThreads) {
     const int t = i / DCH, ch = i - t * DCH;
-    const bf16x8 x = ld_bf16x8(Vh + (long)(tok0 + t) * d + 8 * ch);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) Vt[(8 * ch + e) * vt_stride + t] = __builtin_bit_cast(bf16_t, x[e]);
+    const uint4 x = *reinterpret_cast<const uint4*>(Vh + (long)(tok0 + t) * d + 8 * ch);
+    store_transposed8(Vt + 8 * ch * vt_stride + t, vt_stride, x);
   }
 }
 
@@ -560,12 +569,7 @@ agent_mfma_kernel(MfmaParams p) {
         for (int u = 0; u < VPF; ++u) {
           const int f = threadIdx.x + kThreads * u;
           const int t = f / DCH, ch = f - t * DCH;
-          if (t < rcnt) {
-            const bf16x8 x = __builtin_bit_cast(bf16x8, vpf[u]);
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              Vt[(8 * ch + e) * L.vt_stride + t] = __builtin_bit_cast(bf16_t, x[e]);
-          }
+          if (t < rcnt) store_transposed8(Vt + 8 * ch * L.vt_stride + t, L.vt_stride, vpf[u]);
         }
       } else {
         stage_v(Vt, L.vt_stride, p.v + hoff, rt0, rcnt, p.d);

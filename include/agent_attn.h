@@ -74,6 +74,8 @@ typedef enum {
 } agent_attn_status_t;
 
 #define AGENT_ATTN_MAX_AGENTS 256
+/* Leading workspace bytes that must be zero before a workspace's first use. */
+#define AGENT_ATTN_SYNC_BYTES (512 * 512)
 #define AGENT_ATTN_MAX_HEAD_DIM 128
 
 /* Bytes of device scratch the forward needs for these sizes (0 when
@@ -92,9 +94,13 @@ int agent_attn_forward(const void* q, const void* k, const void* v, void* out,
                        int s, float scale, int dtype, void* stream);
 
 /* Same as agent_attn_forward with caller-owned scratch of at least
- * agent_attn_workspace_bytes(...) bytes, 256-byte aligned.  The
- * workspace is overwritten; it must not overlap any tensor argument.  The
- * call allocates nothing. */
+ * agent_attn_workspace_bytes(...) bytes, 256-byte aligned, that must not
+ * overlap any tensor argument.  Its first AGENT_ATTN_SYNC_BYTES bytes hold
+ * the counters of the workgroup barriers: they must be zero before the
+ * workspace is first used (zero-fill it once after allocation), and every
+ * call leaves them zero again, so one workspace serves any sequence of
+ * calls of any shapes that are ordered on one stream.  The rest is
+ * overwritten freely.  The call allocates nothing. */
 int agent_attn_forward_ws(const void* q, const void* k, const void* v,
                           void* out, const void* agents, int B, int H, int h,
                           int w, int d, int s, float scale, int dtype,
