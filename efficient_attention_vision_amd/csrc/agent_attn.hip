@@ -116,15 +116,18 @@ int check_scale(float scale) {
 // ---------------------------------------------------------------- plans
 // Workspace layout of the forward (every region 256-byte aligned):
 //   [group counters, 512 heads * 512 B, zero between calls][status 256 B]
-//   [A fp32 BH*k*d][V_A fp32 BH*k*d][partials]
+//   [A fp32 BH*k*d][V_A fp32 BH*k*d][partials ...]
 // float32 I/O: partials are BH*nchunks*k*(d+2) floats of the scalar split-N
-// aggregation; bfloat16 I/O: BH*k*P*(d+2) floats of the matrix-core kernel.
+// aggregation.  bfloat16 I/O: agent and V_A hi/lo fragments exchanged
+// between the workgroups of a head, then the partial max/sum (BH*k*P*2
+// floats) and accumulators (BH*k*P*d floats).
 struct Plan {
   // scalar path
   int chunk = 0, nchunks = 0;
   // matrix-core path
   int DC = 0, P = 1, T = 0, fused = 1, xcd_heads = 0, lds = 0;
   size_t off_sync = 0, off_status = 0, off_A = 0, off_VA = 0, off_part = 0, bytes = 0;
+  size_t off_ml = 0;
 };
 
 constexpr size_t kSyncBytesPerHead = (aa::kBarriers + 1) * aa::kSyncStride * sizeof(unsigned);
@@ -155,6 +158,32 @@ int mfma_lds_bytes(int DC, int nag) {
     case 3: return aa::LdsPlan<3>(nag).total;
     default: return aa::LdsPlan<4>(nag).total;
   }
+}
+
+// Partials of the matrix-core aggregation, in register order: per (head,
+// slot, agent tile) the max/sum of 16 agents and 2*DC rows of 64 x 4 floats.
+size_t mfma_ml_bytes(const Dims& D, int P, int DC) {
+  (void)DC;
+  return (size_t)D.BH * P * ((D.nag + 15) / 16) * 16 * 2 * sizeof(float);
+}
+size_t mfma_acc_bytes(const Dims& D, int P, int DC) {
+  return (size_t)D.BH * P * ((D.nag + 15) / 16) * 2 * DC * 256 * sizeof(float);
+}
+
+// Pooling window geometry: the largest window (tokens) and the number of
+// token groups per (agent, chunk) item (a power of two, at most 256).
+void pool_params(const Dims& D, int& tgp, int& maxcnt) {
+  int mr = 0, mc = 0;
+  for (int i = 0; i < D.s; ++i) {
+    const int r0 = (i * D.h) / D.s, r1 = ((i + 1) * D.h + D.s - 1) / D.s;
+    const int c0 = (i * D.w) / D.s, c1 = ((i + 1) * D.w + D.s - 1) / D.s;
+    if (r1 - r0 > mr) mr = r1 - r0;
+    if (c1 - c0 > mc) mc = c1 - c0;
+  }
+  maxcnt = mr * mc;
+  const int want = (maxcnt + aa::kPoolTok - 1) / aa::kPoolTok;
+  tgp = 1;
+  while (tgp < want && tgp < 256) tgp *= 2;
 }
 
 // Number of compute units of the current device (cached per device).
@@ -201,7 +230,7 @@ Plan make_plan(const Dims& D, int cus) {
     P.lds = mfma_lds_bytes(P.DC, D.nag);
     P.fused = 1;  // BH*P <= CUs: the whole grid is co-resident
     P.xcd_heads = (P.P > 1 && D.BH % 8 == 0 && cus % 8 == 0) ? (int)(D.BH / 8) : 0;
-    part_bytes = (size_t)D.BH * D.nag * P.P * (D.d + 2) * sizeof(float);
+    part_bytes = 0;  // set with the fragment regions below
   }
   const size_t ad = (size_t)D.BH * D.nag * D.d * sizeof(float);
   P.off_sync = 0;
@@ -209,6 +238,11 @@ Plan make_plan(const Dims& D, int cus) {
   P.off_A = P.off_status + 256;
   P.off_VA = align_up(P.off_A + ad, 256);
   P.off_part = align_up(P.off_VA + ad, 256);
+  if (D.dtype != AGENT_ATTN_F32) {
+    P.off_ml = P.off_part;
+    P.off_part = align_up(P.off_ml + mfma_ml_bytes(D, P.P, P.DC), 256);
+    part_bytes = mfma_acc_bytes(D, P.P, P.DC);
+  }
   P.bytes = align_up(P.off_part + part_bytes, 256);
   return P;
 }
@@ -275,10 +309,21 @@ int launch_broadcast(const Dims& D, const void* q, const float* A, const float* 
 }
 
 // ------------------------------------------------------ matrix-core path
+#ifdef AGENT_ATTN_PHASE_TRACE
+long long* g_trace = nullptr;  // profiling builds: per-workgroup phase stamps
+#endif
+
+// Two register budgets: one workgroup per CU (grid-synchronised groups, at
+// most one workgroup per CU by construction) or two per CU (independent
+// workgroups, P = 1, grids larger than the chip).
 template <int DC>
 int launch_mfma_dc(const aa::MfmaParams& mp, long grid, int lds, hipStream_t st) {
-  hipLaunchKernelGGL(aa::agent_mfma_kernel<DC>, dim3((unsigned)grid), dim3(aa::kThreads),
-                     (unsigned)lds, st, mp);
+  if (mp.P > 1)
+    hipLaunchKernelGGL((aa::agent_mfma_kernel<DC, 1>), dim3((unsigned)grid), dim3(aa::kThreads),
+                       (unsigned)lds, st, mp);
+  else
+    hipLaunchKernelGGL((aa::agent_mfma_kernel<DC, 2>), dim3((unsigned)grid), dim3(aa::kThreads),
+                       (unsigned)lds, st, mp);
   AA_LAUNCH_CHECK("agent attention matrix-core kernel launch");
   return AGENT_ATTN_OK;
 }
@@ -304,6 +349,10 @@ aa::MfmaParams mfma_params(const Dims& D, int P, int T, float scale) {
   mp.P = P;
   mp.T = T;
   mp.sl2 = scale * aa::kLog2e;
+  if (D.s > 0) {
+    pool_params(D, mp.pool_tgp, mp.pool_maxcnt);
+    while ((1 << mp.pool_tgp_log2) < mp.pool_tgp) ++mp.pool_tgp_log2;
+  }
   return mp;
 }
 
@@ -311,6 +360,12 @@ aa::MfmaParams mfma_params(const Dims& D, int P, int T, float scale) {
 int run_mfma_phases(const Dims& D, aa::MfmaParams mp, int DC, int phases, bool fused,
                     hipStream_t st) {
   const int lds = mfma_lds_bytes(DC, D.nag);
+  if (lds > 160 * 1024 - 64)
+    return fail(AGENT_ATTN_ERR_UNSUPPORTED, "d=%d with %d agents needs %d bytes of LDS", D.d,
+                D.nag, lds);
+  if (D.N * (long)D.d * 2 > (long)aa::kOOB)
+    return fail(AGENT_ATTN_ERR_SHAPE, "N*d=%ld exceeds the per-head limit of 2^30 elements",
+                D.N * (long)D.d);
   const long grid = D.BH * mp.P;
   if (fused) {
     mp.phases = phases;
@@ -339,10 +394,14 @@ int run_forward_mfma(const Dims& D, const Plan& P, const void* q, const void* k,
   mp.agents_in = (const aa::bf16_t*)agents;
   mp.agents_f32 = (float*)(ws + P.off_A);
   mp.values_f32 = (float*)(ws + P.off_VA);
-  mp.part = (float*)(ws + P.off_part);
+  mp.part_ml = (float*)(ws + P.off_ml);
+  mp.part_acc = (float*)(ws + P.off_part);
   mp.sync = (unsigned*)(ws + P.off_sync);
   mp.status = (int*)(ws + P.off_status);
   mp.xcd_heads = P.xcd_heads;
+#ifdef AGENT_ATTN_PHASE_TRACE
+  mp.trace = g_trace;
+#endif
   const int phases =
       (agents ? 0 : aa::PH_POOL) | aa::PH_AGG | aa::PH_MERGE | aa::PH_BCAST;
   return run_mfma_phases(D, mp, P.DC, phases, P.fused != 0, st);
@@ -430,7 +489,8 @@ size_t aggregate_ws_bytes(const Dims& D) {
   }
   int P, T;
   mfma_split(D, device_cus(), P, T);
-  return align_up((size_t)D.BH * D.nag * P * (D.d + 2) * sizeof(float), 256);
+  const int DC = (D.d + 31) / 32;
+  return align_up(mfma_ml_bytes(D, P, DC), 256) + align_up(mfma_acc_bytes(D, P, DC), 256);
 }
 
 }  // namespace
@@ -550,7 +610,8 @@ int agent_attn_aggregate(const float* agents_f32, const void* k, const void* v,
   mp.v = (const aa::bf16_t*)v;
   mp.agents_f32_in = agents_f32;
   mp.values_f32 = agent_values_f32;
-  mp.part = part;
+  mp.part_ml = part;
+  mp.part_acc = (float*)((char*)workspace + align_up(mfma_ml_bytes(D, P, (D.d + 31) / 32), 256));
   return run_mfma_phases(D, mp, (D.d + 31) / 32, aa::PH_AGG | aa::PH_MERGE, false, st);
 }
 
@@ -618,5 +679,10 @@ const char* agent_attn_status_string(int status) {
 }
 
 const char* agent_attn_last_error(void) { return g_last_error.c_str(); }
+
+#ifdef AGENT_ATTN_PHASE_TRACE
+// Profiling builds only: device buffer of 16 int64 stamps per workgroup.
+void agent_attn_debug_set_trace(void* trace) { g_trace = (long long*)trace; }
+#endif
 
 }  // extern "C"

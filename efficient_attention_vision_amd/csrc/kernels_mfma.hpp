@@ -13,8 +13,18 @@
 // broadcast and agents {j, j+P, ...} for pooling and merging.  In fused mode
 // all phases run in one launch of a co-resident grid and the P workgroups of
 // a head meet at three group barriers (after pooling, after the partials,
-// after merging); otherwise the host launches the phases one after another
-// and kernel boundaries order them.
+// after merging); with P = 1 one workgroup does everything for its head.
+// Otherwise the host launches the phases one after another and kernel
+// boundaries order them.
+//
+// Memory: every stream of Q, K, V goes through buffer loads whose range is
+// the head (or the workgroup's slice), so that loads past the end return
+// zeros without branches, and all loads a phase needs are issued before any
+// of them is waited for.  The pooling loads are issued first (they start
+// the dependency chain), then this workgroup's K blocks, V round and query
+// tiles.  Data exchanged between the workgroups of a head (agents, partials,
+// V_A) is written and read with the device-coherent cache policy in
+// contiguous 16-byte pieces.
 //
 // Matrix-core mapping (v_mfma_f32_16x16x32_bf16, wave64): for lane l, with
 // r = l % 16 and g = l / 16, the A operand holds row r, the B operand column
@@ -24,7 +34,9 @@
 // order never matters.  The two probability matrices are produced in the
 // result layout and consumed directly as B operands: a pair of 16-wide tiles
 // gives each lane the 8 contraction indices {4g..4g+3, 16+4g..16+4g+3}, and
-// the value operands (V^T, V_A^T) are read in that same order.
+// the value operands (V^T, V_A^T) are read in that same order.  V_A enters
+// the matrix cores as a bf16 pair hi + lo (two products) where LDS allows,
+// so that only the agents, the probabilities and O itself are rounded.
 #pragma once
 
 #include "common.hpp"
@@ -33,16 +45,20 @@ namespace aa {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 enum : int { PH_POOL = 1, PH_AGG = 2, PH_MERGE = 4, PH_BCAST = 8 };
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kRoundTokens = 256;        // tokens of V staged in LDS at a time
 constexpr int kVtPad = 8;                // LDS row padding (bf16) of staged V^T
 constexpr int kBarriers = 3;
 constexpr int kSyncStride = 32;          // dwords between counters (own 128 B line)
 constexpr long kSpinLimit = 1L << 20;    // bounded waits: ~1 s, then an error
+constexpr int kPoolTok = 8;              // window tokens per pooling work item
+constexpr unsigned kOOB = 0x7ffffff0u;   // an offset past every buffer range
 
 struct MfmaParams {
   const bf16_t* q;
@@ -52,55 +68,127 @@ struct MfmaParams {
   const bf16_t* agents_in;      // caller agents [BH, nag, d] (bf16) or null
   const float* agents_f32_in;   // agents [BH, nag, d] fp32 (step calls) or null
   const float* values_f32_in;   // V_A [BH, nag, d] fp32 (step calls) or null
-  float* agents_f32;            // pooled agents out [BH, nag, d]
-  float* values_f32;            // V_A out [BH, nag, d]
-  float* part;                  // partials [BH, nag, P, d + 2]
+  float* agents_f32;            // agents [BH, nag, d] (exchange, or step output)
+  float* values_f32;            // V_A [BH, nag, d] (exchange, staging, or step output)
+  float* part_acc;              // partials [BH][P][KT][DT][64][4]
+  float* part_ml;               // partial max and sum [BH][P][KT][16][2]
   unsigned* sync;               // group counters, zero between launches
   int* status;                  // nonzero after a barrier timed out
   int BH, N, h, w, d, s, nag;
   int P, T;                     // workgroups per head, tokens per workgroup
+  int pool_tgp;                 // pooling token groups per (agent, chunk): power of 2
+  int pool_tgp_log2;
+  int pool_maxcnt;              // largest pooling window, in tokens
   float sl2;                    // scale * log2(e)
   int phases;
   int fused;
   int xcd_heads;                // >0: heads per XCD for the XCD-aware mapping
+  long long* trace;             // phase timestamps (trace builds only)
 };
 
-// ------------------------------------------------------------ small helpers
-__device__ __forceinline__ bf16x8 ld_bf16x8(const bf16_t* p) {
-  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
-}
+// Phase timestamps for profiling builds (-DAGENT_ATTN_PHASE_TRACE): 16
+// wall-clock stamps per workgroup.  Compiled out otherwise.
+#ifdef AGENT_ATTN_PHASE_TRACE
+#define AA_STAMP(i)                                                            \
+  do {                                                                         \
+    if (p.trace && threadIdx.x == 0)                                           \
+      p.trace[(long)blockIdx.x * 16 + (i)] = (long long)wall_clock64();        \
+  } while (0)
+#else
+#define AA_STAMP(i) \
+  do {              \
+  } while (0)
+#endif
 
+// ------------------------------------------------------------ small helpers
 __device__ __forceinline__ bf16x8 zero_bf16x8() {
   return __builtin_bit_cast(bf16x8, uint4{0u, 0u, 0u, 0u});
 }
-
-__device__ __forceinline__ float shfl_xor_f(float x, int m) { return __shfl_xor(x, m, 64); }
-
+// Reductions over the four 16-lane groups of a wave (lanes r, r+16, r+32,
+// r+48) with the gfx950 row-swap permutes: after permlane16_swap(x, x) the
+// two results hold x of lanes l and l^16 (in some order), after
+// permlane32_swap those of l and l^32.
 __device__ __forceinline__ float group4_max(float x) {
-  x = fmaxf(x, shfl_xor_f(x, 16));
-  return fmaxf(x, shfl_xor_f(x, 32));
+  const u32x2 a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                   false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const u32x2 b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                   false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float group4_sum(float x) {
-  x += shfl_xor_f(x, 16);
-  return x + shfl_xor_f(x, 32);
+  const u32x2 a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                   false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const u32x2 b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                   false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// Device-coherent exchange of small data between the workgroups of a group:
-// relaxed agent-scope accesses bypass the non-coherent caches; ordering comes
-// from s_waitcnt before the barrier arrival (see group_barrier).
-__device__ __forceinline__ void st_dev(float* p, float x) {
-  __hip_atomic_store(reinterpret_cast<unsigned*>(p), __float_as_uint(x), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
+// a / b for 0 <= a < 2^22, 1 <= b, given rb = 1/b (approximate reciprocal):
+// the float estimate is within one of the quotient and one step fixes it.
+__device__ __forceinline__ int idiv(int a, int b, float rb) {
+  int q = (int)((float)a * rb);
+  const int r = a - q * b;
+  q += (r >= b) ? 1 : 0;
+  q -= (r < 0) ? 1 : 0;
+  return q;
 }
-__device__ __forceinline__ float ld_dev(const float* p) {
-  return __uint_as_float(__hip_atomic_load(reinterpret_cast<const unsigned*>(p), __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT));
+__device__ __forceinline__ float rcp_approx(int b) { return __builtin_amdgcn_rcpf((float)b); }
+__device__ __forceinline__ bf16_t bf16_bits(float x) {
+  return __builtin_bit_cast(bf16_t, static_cast<__bf16>(x));
+}
+__device__ __forceinline__ float bf16_value(bf16_t b) {
+  return __uint_as_float(static_cast<unsigned>(b) << 16);
+}
+__device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {
+  return (unsigned)bf16_bits(lo) | ((unsigned)bf16_bits(hi) << 16);
+}
+
+// Buffer accesses.  CPol: kPlain = default caching; kCoherent = sc1, the
+// device-coherent policy of agent-scope atomics (used for data that other
+// workgroups, possibly on another XCD, read after a group barrier).
+constexpr int kPlain = 0;
+constexpr int kCoherent = 16;
+
+__device__ __forceinline__ rsrc_t rsrc_of(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+template <int POL>
+__device__ __forceinline__ uint4 bld16(rsrc_t r, unsigned off) {
+  const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, POL);
+  return uint4{x[0], x[1], x[2], x[3]};
+}
+template <int POL>
+__device__ __forceinline__ float bld4(rsrc_t r, unsigned off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, POL));
+}
+template <int POL>
+__device__ __forceinline__ void bst16(rsrc_t r, unsigned off, uint4 x) {
+  __builtin_amdgcn_raw_buffer_store_b128(u32x4{x.x, x.y, x.z, x.w}, r, (int)off, 0, POL);
+}
+template <int POL>
+__device__ __forceinline__ void bst8(rsrc_t r, unsigned off, uint2 x) {
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2{x.x, x.y}, r, (int)off, 0, POL);
+}
+template <int POL>
+__device__ __forceinline__ void bst4(rsrc_t r, unsigned off, float x) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, (int)off, 0, POL);
+}
+__device__ __forceinline__ uint4 f4_bits(float4 x) {
+  return uint4{__float_as_uint(x.x), __float_as_uint(x.y), __float_as_uint(x.z),
+               __float_as_uint(x.w)};
+}
+__device__ __forceinline__ float4 bits_f4(uint4 x) {
+  return float4{__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z),
+                __uint_as_float(x.w)};
 }
 
 // Barrier of the P workgroups of one head.  Counters start at zero in every
 // launch: the last workgroup to finish the kernel resets them.  Every wave
-// first waits for its own stores to complete, so data stored before the
-// barrier is visible to device-coherent loads after it.
+// first waits for its own loads and stores to complete, so data stored
+// before the barrier is visible to device-coherent loads after it.
 __device__ __forceinline__ bool group_barrier(unsigned* ctr, unsigned n, int* status) {
   __shared__ int ok;
   __builtin_amdgcn_s_waitcnt(0);
@@ -129,104 +217,111 @@ __device__ __forceinline__ int pair_index(int j, int g, int e) {
   return 32 * j + (e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4));
 }
 
-// ------------------------------------------------------------ LDS operands
-// A fragments: [KT][DC][64 lanes] x 8 bf16; fragment (t, c, lane) holds
-// agents 16t + lane%16, channels 8*(DC*(lane/16) + c) .. +8.
-template <int DC>
-__device__ void load_agent_frags(bf16x8* lds, const MfmaParams& p, int head, bool device_coherent) {
-  const int KT = (p.nag + 15) / 16;
-  const int total = KT * DC * 64;
-  const long hb = (long)head * p.nag * p.d;
-  for (int f = threadIdx.x; f < total; f += kThreads) {
-    const int lane = f & 63, c = (f >> 6) % DC, t = (f >> 6) / DC;
-    const int agent = 16 * t + (lane & 15);
-    const int ch0 = 8 * (DC * (lane >> 4) + c);
-    union { bf16x8 v; __bf16 e[8]; } u;
-    if (agent < p.nag && ch0 < p.d) {
-      if (p.agents_in) {
-        u.v = ld_bf16x8(p.agents_in + hb + (long)agent * p.d + ch0);
-      } else {
-        const float* src = (p.agents_f32_in ? p.agents_f32_in : p.agents_f32) + hb +
-                           (long)agent * p.d + ch0;
+// 8 x 8 transpose of bf16: x[j] holds 8 channels of token j; the result y[e]
+// holds channel e of tokens 0..7.
+__device__ __forceinline__ void transpose8x8(const uint4 (&x)[8], uint4 (&y)[8]) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          u.e[e] = (__bf16)(device_coherent ? ld_dev(src + e) : src[e]);
-      }
-    } else {
-      u.v = zero_bf16x8();
+  for (int e = 0; e < 8; ++e) {
+    const unsigned sel = (e & 1) ? 0x07060302u : 0x05040100u;
+    unsigned w[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const uint4 a = x[2 * jj], b = x[2 * jj + 1];
+      const unsigned wa = (e >> 1) == 0 ? a.x : (e >> 1) == 1 ? a.y : (e >> 1) == 2 ? a.z : a.w;
+      const unsigned wb = (e >> 1) == 0 ? b.x : (e >> 1) == 1 ? b.y : (e >> 1) == 2 ? b.z : b.w;
+      w[jj] = __builtin_amdgcn_perm(wb, wa, sel);   // {a.elem(e), b.elem(e)}
     }
-    lds[f] = u.v;
+    y[e] = uint4{w[0], w[1], w[2], w[3]};
   }
 }
 
-// V_A fragments: [KC][DT][64 lanes] x 8 bf16; fragment (j, dt, lane) holds
-// channel 16dt + lane%16 of agents pair_index(j, lane/16, e).
+// ------------------------------------------------------------ LDS plan
+// Bytes, computed identically on the host by mfma_lds_bytes():
+//   [0, a_bytes)      A fragments [KT][DC][64 lanes] x 8 bf16
+//   [a_bytes, +big)   union of: pooling partial sums; {staged V^T, staged K
+//                     rows} of one round; cross-wave partials; {V_A staging
+//                     rows, V_A fragments}
 template <int DC>
-__device__ void load_value_frags(bf16x8* lds, const float* VA, const MfmaParams& p, int head,
-                                 bool device_coherent) {
-  constexpr int DT = 2 * DC;
-  const int KC = (p.nag + 31) / 32;
-  const int total = KC * DT * 64;
-  const long hb = (long)head * p.nag * p.d;
-  for (int f = threadIdx.x; f < total; f += kThreads) {
-    const int lane = f & 63, dt = (f >> 6) % DT, j = (f >> 6) / DT;
-    const int ch = 16 * dt + (lane & 15), g = lane >> 4;
-    union { bf16x8 v; __bf16 e[8]; } u;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int agent = pair_index(j, g, e);
-      float x = 0.f;
-      if (agent < p.nag && ch < p.d) {
-        const float* src = VA + hb + (long)agent * p.d + ch;
-        x = device_coherent ? ld_dev(src) : *src;
-      }
-      u.e[e] = (__bf16)x;
+struct LdsPlan {
+  static constexpr int RT = DC <= 2 ? 256 : 128;   // tokens per round
+  int KT, KC, AG, TG, vparts, stage_lds;
+  int a_bytes, vt_stride, vt_bytes, ks_stride, ks_bytes, comb_bytes, va_bytes, stage_bytes;
+  int big, total;
+  __host__ __device__ LdsPlan(int nag) {
+    constexpr int DPAD = 32 * DC;
+    constexpr int kMaxLds = 160 * 1024 - 64;   // static LDS of the barrier flag
+    KT = (nag + 15) / 16;
+    KC = (nag + 31) / 32;
+    AG = KT <= 4 ? 1 : (KT <= 8 ? 2 : 4);
+    TG = kWaves / AG;
+    a_bytes = KT * DC * 1024;
+    vt_stride = RT + kVtPad;
+    vt_bytes = DPAD * vt_stride * 2;
+    ks_stride = DPAD + 8;
+    ks_bytes = RT * ks_stride * 2;
+    comb_bytes = (TG - 1) * AG * 4 * (2 * DC + 1) * 64 * 16;
+    stage_bytes = KT * 16 * DPAD * 4;
+    const int pool_bytes = kThreads * 8 * 4;
+    // V_A as hi + lo when it fits, staging rows in LDS when they fit
+    vparts = 2;
+    stage_lds = 1;
+    for (;;) {
+      va_bytes = vparts * KC * 2 * DC * 1024;
+      const int need = va_bytes + (stage_lds ? stage_bytes : 0);
+      big = vt_bytes + ks_bytes;
+      if (comb_bytes > big) big = comb_bytes;
+      if (pool_bytes > big) big = pool_bytes;
+      if (need > big) big = need;
+      total = a_bytes + big;
+      if (total <= kMaxLds) break;
+      if (stage_lds) stage_lds = 0;
+      else if (vparts == 2) { vparts = 1; stage_lds = 1; }
+      else break;   // host rejects
     }
-    lds[f] = u.v;
   }
-}
+};
 
 // ------------------------------------------------------------------ pooling
-// Agents a = j, j+P, ... of the head: mean of Q over the agent's window.
-// Wave w pools the agents with (a - j)/P = w mod 4.  Lane layout: DCH = d/8
-// lanes per token, 64/DCH tokens per pass.
-__device__ void pool_phase(const MfmaParams& p, int head, int j, float* red) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int DCH = p.d >> 3;
-  const int tpp = 64 / DCH;                    // tokens per pass
-  const int ltok = lane / DCH, lch = lane - ltok * DCH;
-  const bool lane_on = ltok < tpp;
-  const bf16_t* Qh = p.q + (long)head * p.N * p.d;
-  float* red_w = red + wave * 64 * 8;
-  for (int a = j + p.P * wave; a < p.nag; a += p.P * kWaves) {
-    const int ai = a / p.s, aj = a - ai * p.s;
-    const int r0 = (ai * p.h) / p.s, r1 = ((ai + 1) * p.h + p.s - 1) / p.s;
-    const int c0 = (aj * p.w) / p.s, c1 = ((aj + 1) * p.w + p.s - 1) / p.s;
-    const int wc = c1 - c0;
-    const int cnt = (r1 - r0) * wc;
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (lane_on) {
-      for (int t = ltok; t < cnt; t += tpp) {
-        const int rr = r0 + t / wc, cc = c0 + t % wc;
-        const bf16x8 x = ld_bf16x8(Qh + ((long)rr * p.w + cc) * p.d + 8 * lch);
+// Agents a = slot + P*m (m < na) of the head.  Work item (m, chunk c, token
+// group tg) sums window tokens tg, tg + TGP, ... (kPoolTok of them) over 8
+// channels; the TGP groups of a (m, c) pair are then added in a fixed order.
+struct PoolGeo {
+  int r0, c0, wc, cnt;
+};
+__device__ __forceinline__ PoolGeo pool_geo(const MfmaParams& p, int a) {
+  const float rs = rcp_approx(p.s);
+  const int ai = idiv(a, p.s, rs), aj = a - ai * p.s;
+  const int r0 = idiv(ai * p.h, p.s, rs), r1 = idiv((ai + 1) * p.h + p.s - 1, p.s, rs);
+  const int c0 = idiv(aj * p.w, p.s, rs), c1 = idiv((aj + 1) * p.w + p.s - 1, p.s, rs);
+  return PoolGeo{r0, c0, c1 - c0, (r1 - r0) * (c1 - c0)};
+}
+
+__device__ __forceinline__ void pool_issue(const MfmaParams& p, rsrc_t rq, int slot, int item,
+                                           int items, int tbase, uint4 (&x)[kPoolTok]) {
+  const int DCH = p.d >> 3, TGP = p.pool_tgp;
+  const int pr = item >> p.pool_tgp_log2, tg = item - pr * TGP;
+  const int m = idiv(pr, DCH, rcp_approx(DCH)), c = pr - m * DCH;
+  const PoolGeo G = pool_geo(p, slot + p.P * m);
+  const float rwc = rcp_approx(G.wc);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] += (float)x[e];
-      }
-    }
+  for (int u = 0; u < kPoolTok; ++u) {
+    const int t = tbase + tg + TGP * u;
+    const int tq = idiv(t, G.wc, rwc);
+    const int rr = G.r0 + tq, cc = G.c0 + (t - tq * G.wc);
+    const unsigned off = (item < items && t < G.cnt)
+                             ? (unsigned)(((rr * p.w + cc) * p.d + 8 * c) * 2)
+                             : kOOB;
+    x[u] = bld16<kPlain>(rq, off);
+  }
+}
+
+__device__ __forceinline__ void pool_accum(const uint4 (&x)[kPoolTok], float (&acc)[8]) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) red_w[lane * 8 + e] = acc[e];
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    // lanes < d: channel = lane (two passes for d > 64)
-    const float inv = 1.0f / (float)cnt;
-    for (int ch = lane; ch < p.d; ch += 64) {
-      const int cchunk = ch >> 3, ce = ch & 7;
-      float sum = 0.f;
-      for (int t = 0; t < tpp; ++t) sum += red_w[(t * DCH + cchunk) * 8 + ce];
-      float* dst = p.agents_f32 + ((long)head * p.nag + a) * p.d + ch;
-      if (p.fused && p.P > 1) st_dev(dst, sum * inv); else *dst = sum * inv;
-    }
-    __builtin_amdgcn_wave_barrier();
+  for (int u = 0; u < kPoolTok; ++u) {
+    const unsigned w[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      acc[e] += __uint_as_float((e & 1) ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16));
   }
 }
 
@@ -240,11 +335,24 @@ struct AggState {
 };
 
 template <int DC>
-__device__ __forceinline__ void agg_block(AggState<DC>& st, const bf16x8 (&kf)[2][DC],
+__device__ __forceinline__ void agg_block(AggState<DC>& st, const bf16_t* Ks, int ks_stride,
                                           const bf16x8* Af, const bf16_t* Vt, int vt_stride,
-                                          int blk_col, int ag, int KT, int valid, float sl2) {
+                                          int blk_col, int ag, int KT, int valid, int d,
+                                          float sl2) {
   constexpr int DT = 2 * DC;
   const int lane = threadIdx.x & 63, g = lane >> 4;
+  // K fragments: token row blk_col + 16tt + lane%16, channel chunk DC*g + c
+  // (chunks at or past d are never staged: zero them here)
+  bf16x8 kf[2][DC];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int c = 0; c < DC; ++c) {
+      const int ch0 = 8 * (DC * g + c);
+      const bf16x8 x = *reinterpret_cast<const bf16x8*>(
+          Ks + (blk_col + 16 * tt + (lane & 15)) * ks_stride + ch0);
+      kf[tt][c] = ch0 < d ? x : zero_bf16x8();
+    }
   f32x4 S[2][4];
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
@@ -261,7 +369,6 @@ __device__ __forceinline__ void agg_block(AggState<DC>& st, const bf16x8 (&kf)[2
       }
     }
   }
-  // mask tokens past the slice end (rows 16tt + 4g + i of the block)
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
@@ -269,8 +376,6 @@ __device__ __forceinline__ void agg_block(AggState<DC>& st, const bf16x8 (&kf)[2
       if (16 * tt + 4 * g + i >= valid)
 #pragma unroll
         for (int a = 0; a < 4; ++a) S[tt][a][i] = -INFINITY;
-  // V^T fragments for this block: channel row 16dt + lane%16, tokens
-  // {4g..4g+3} and {16+4g..16+4g+3} of the block.
   bf16x8 vf[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
@@ -308,72 +413,60 @@ __device__ __forceinline__ void agg_block(AggState<DC>& st, const bf16x8 (&kf)[2
   }
 }
 
-template <int DC>
-__device__ __forceinline__ void load_k_block(bf16x8 (&kf)[2][DC], const bf16_t* Kh, int tok0,
-                                             int tok_end, int d) {
-  const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+// 8-token x 8-channel tiles of K or V: tile `it` covers tokens
+// tok0 + 8*(it / DCH) .. +8 and channels 8*(it % DCH) .. +8.  Tokens at or
+// past tok_end load as zeros.
+__device__ __forceinline__ void load_tile8(uint4 (&x)[8], rsrc_t r, int it, int tok0, int tok_end,
+                                           int d) {
+  const int DCH = d >> 3;
+  const int t8 = idiv(it, DCH, rcp_approx(DCH)), ch = it - t8 * DCH;
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
-    const int tok = tok0 + 16 * tt + r;
-#pragma unroll
-    for (int c = 0; c < DC; ++c) {
-      const int ch0 = 8 * (DC * g + c);
-      kf[tt][c] = (tok < tok_end && ch0 < d) ? ld_bf16x8(Kh + (long)tok * d + ch0) : zero_bf16x8();
-    }
+  for (int j = 0; j < 8; ++j) {
+    const int tok = tok0 + 8 * t8 + j;
+    x[j] = bld16<kPlain>(r, tok < tok_end ? (unsigned)((tok * d + 8 * ch) * 2) : kOOB);
   }
 }
-
-// Eight consecutive bf16 channels of one token -> one column of Vt (rows
-// dst, dst + stride, ...).  Elements are taken out of the 32-bit words with
-// shifts so that each 16-bit store gets its own element.
-__device__ __forceinline__ void store_transposed8(bf16_t* dst, int stride, uint4 x) {
-  const unsigned w[4] = {x.x, x.y, x.z, x.w};
+// V tile -> transposed rows Vt[channel][token] of the round
+__device__ __forceinline__ void store_tile_t(bf16_t* Vt, int vt_stride, const uint4 (&x)[8], int it,
+                                             int d) {
+  const int DCH = d >> 3;
+  const int t8 = idiv(it, DCH, rcp_approx(DCH)), ch = it - t8 * DCH;
+  uint4 y[8];
+  transpose8x8(x, y);
 #pragma unroll
   for (int e = 0; e < 8; ++e)
-    dst[e * stride] = static_cast<bf16_t>((w[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+    *reinterpret_cast<uint4*>(Vt + (8 * ch + e) * vt_stride + 8 * t8) = y[e];
 }
-
-// Stage V[tok0, tok0+cnt) of the head transposed into LDS: Vt[ch][col].
-__device__ __forceinline__ void stage_v(bf16_t* Vt, int vt_stride, const bf16_t* Vh, int tok0,
-                                        int cnt, int d) {
+// K tile -> rows Ks[token][channel] of the round
+__device__ __forceinline__ void store_tile_rows(bf16_t* Ks, int ks_stride, const uint4 (&x)[8],
+                                                int it, int d) {
   const int DCH = d >> 3;
-  const int total = cnt * DCH;
-  for (int i = threadIdx.x; i < total; i += kThreads) {
-    const int t = i / DCH, ch = i - t * DCH;
-    const uint4 x = *reinterpret_cast<const uint4*>(Vh + (long)(tok0 + t) * d + 8 * ch);
-    store_transposed8(Vt + 8 * ch * vt_stride + t, vt_stride, x);
-  }
-}
-
-// Zero the staged columns [cnt, cnt_pad) so that masked tokens contribute
-// 0 * finite instead of 0 * garbage (garbage could be NaN).
-__device__ __forceinline__ void zero_v_tail(bf16_t* Vt, int vt_stride, int cnt, int cnt_pad,
-                                            int dpad) {
-  const int w = cnt_pad - cnt;
-  if (w <= 0) return;
-  for (int i = threadIdx.x; i < w * dpad; i += kThreads) {
-    const int ch = i / w, t = cnt + (i - ch * w);
-    Vt[ch * vt_stride + t] = 0;
-  }
+  const int t8 = idiv(it, DCH, rcp_approx(DCH)), ch = it - t8 * DCH;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    *reinterpret_cast<uint4*>(Ks + (8 * t8 + j) * ks_stride + 8 * ch) = x[j];
 }
 
 // ------------------------------------------------------------ broadcast
 template <int DC>
-__device__ __forceinline__ void load_q_tile(bf16x8 (&qf)[DC], const bf16_t* Qh, int tok0,
-                                            int tok_end, int d) {
+__device__ __forceinline__ void load_q_tile(bf16x8 (&qf)[DC], rsrc_t rq, int tok0, int tok_end,
+                                            int d) {
   const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
   const int tok = tok0 + r;
 #pragma unroll
   for (int c = 0; c < DC; ++c) {
     const int ch0 = 8 * (DC * g + c);
-    qf[c] = (tok < tok_end && ch0 < d) ? ld_bf16x8(Qh + (long)tok * d + ch0) : zero_bf16x8();
+    const unsigned off = (tok < tok_end && ch0 < d) ? (unsigned)((tok * d + ch0) * 2) : kOOB;
+    qf[c] = __builtin_bit_cast(bf16x8, bld16<kPlain>(rq, off));
   }
 }
 
+// VAf: [vparts][KC][DT][64] fragments (hi part, then lo part va_stride apart).
 template <int DC>
 __device__ __forceinline__ void bcast_tile(const bf16x8 (&qf)[DC], const bf16x8* Af,
-                                           const bf16x8* VAf, bf16_t* Oh, int tok0, int tok_end,
-                                           int d, int nag, float sl2) {
+                                           const bf16x8* VAf, int va_stride, int vparts,
+                                           rsrc_t ro, int tok0, int tok_end, int d, int nag,
+                                           float sl2) {
   constexpr int DT = 2 * DC;
   const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
   const int KT = (nag + 15) / 16;
@@ -424,66 +517,42 @@ __device__ __forceinline__ void bcast_tile(const bf16x8 (&qf)[DC], const bf16x8*
           pf.e[4 * h2 + i] = (__bf16)pv;
         }
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(VAf[(jj * DT + dt) * 64 + lane], pf.v,
-                                                        O[dt], 0, 0, 0);
+      for (int dt = 0; dt < DT; ++dt) {
+        const int f = (jj * DT + dt) * 64 + lane;
+        O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(VAf[f], pf.v, O[dt], 0, 0, 0);
+        if (vparts > 1)
+          O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(VAf[va_stride + f], pf.v, O[dt], 0, 0, 0);
+      }
     }
   }
   L = group4_sum(L);
   const float inv = 1.0f / L;
   const int tok = tok0 + r;
-  if (tok < tok_end) {
-    bf16_t* orow = Oh + (long)tok * d;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const int ch = 16 * dt + 4 * g;
-      if (ch < d) {
-        union { uint2 u; __bf16 e[4]; } o;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o.e[i] = (__bf16)(O[dt][i] * inv);
-        *reinterpret_cast<uint2*>(orow + ch) = o.u;
-      }
-    }
+  for (int dt = 0; dt < DT; ++dt) {
+    const int ch = 16 * dt + 4 * g;
+    const unsigned off = (tok < tok_end && ch < d) ? (unsigned)((tok * d + ch) * 2) : kOOB;
+    bst8<kPlain>(ro, off, uint2{pack_bf16(O[dt][0] * inv, O[dt][1] * inv),
+                                pack_bf16(O[dt][2] * inv, O[dt][3] * inv)});
   }
 }
 
 // ------------------------------------------------------------- the kernel
-// LDS plan (bytes), computed identically on the host by mfma_lds_bytes():
-//   [0, a_bytes)                  A fragments, KT*DC KiB
-//   [a_bytes, a_bytes + big)      union of: staged V^T + pool scratch,
-//                                 cross-wave partials, V_A fragments
-template <int DC>
-struct LdsPlan {
-  int KT, KC, AG, TG;
-  int a_bytes, vt_stride, vt_bytes, comb_bytes, va_bytes, pool_bytes, big, total;
-  __host__ __device__ LdsPlan(int nag) {
-    constexpr int DPAD = 32 * DC;
-    KT = (nag + 15) / 16;
-    KC = (nag + 31) / 32;
-    AG = KT <= 4 ? 1 : (KT <= 8 ? 2 : 4);
-    TG = kWaves / AG;
-    a_bytes = KT * DC * 1024;
-    vt_stride = kRoundTokens + kVtPad;
-    vt_bytes = DPAD * vt_stride * 2;
-    comb_bytes = (TG - 1) * AG * 64 * 4 * (2 * DC * 4 + 2) * 4;
-    va_bytes = KC * 2 * DC * 1024;
-    pool_bytes = kWaves * 64 * 8 * 4;
-    big = vt_bytes;
-    if (comb_bytes > big) big = comb_bytes;
-    if (va_bytes > big) big = va_bytes;
-    if (pool_bytes > big) big = pool_bytes;
-    total = a_bytes + big;
-  }
-};
-
-template <int DC>
-__global__ void __launch_bounds__(kThreads)
+template <int DC, int MINB>
+__global__ void __launch_bounds__(kThreads, MINB)
 agent_mfma_kernel(MfmaParams p) {
   constexpr int DT = 2 * DC;
+  constexpr int DPAD = 32 * DC;
+  constexpr int RT = LdsPlan<DC>::RT;
+  constexpr int QPF = DC <= 2 ? 4 : 2;        // query tiles loaded ahead per wave
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const LdsPlan<DC> L(p.nag);
   bf16x8* Af = reinterpret_cast<bf16x8*>(smem);
   unsigned char* big = smem + L.a_bytes;
+  bf16_t* Vt = reinterpret_cast<bf16_t*>(big);
+  bf16_t* Ks = reinterpret_cast<bf16_t*>(big + L.vt_bytes);
+  const int a_frags = L.KT * DC * 64;         // bf16x8 fragments
+  const int va_frags = L.KC * DT * 64;        // per hi / lo part
 
   // workgroup -> (head, slot)
   int head, slot;
@@ -496,58 +565,155 @@ agent_mfma_kernel(MfmaParams p) {
     slot = blockIdx.x % p.P;
   }
   if (head >= p.BH) return;
+  AA_STAMP(0);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int d = p.d, DCH = d >> 3;
   const int n0 = slot * p.T;
   const int n1 = min(p.N, n0 + p.T);
-  const long hoff = (long)head * p.N * p.d;
+  const long hoff = (long)head * p.N * d;
+  const unsigned head_bytes = (unsigned)(p.N * d * 2);
   unsigned* ctr = p.sync + (long)head * (kBarriers + 1) * kSyncStride;
   const bool sync_group = p.fused && p.P > 1;
+  const bool single = p.fused && p.P == 1;   // whole head in this workgroup
   bool ok = true;
+  const rsrc_t rq = rsrc_of(p.q + hoff, head_bytes);
+  const rsrc_t rk = rsrc_of(p.k + hoff, head_bytes);
+  const rsrc_t rv = rsrc_of(p.v + hoff, head_bytes);
+  const long ahb = (long)head * p.nag * d;    // offset of this head's agent rows
+  const unsigned arow_bytes = (unsigned)(p.nag * d * 4);
 
-  // ---- prefetch: first K block pair of this wave and first query tiles
+  // ---- pooling loads first: they start the dependency chain
+  const int pool_na = p.nag > slot ? (p.nag - slot + p.P - 1) / p.P : 0;
+  const int pool_items = pool_na * DCH * p.pool_tgp;
+  const int pool_chunk = p.pool_tgp * kPoolTok;       // window tokens per item pass
+  const int pool_npass = (p.pool_maxcnt + pool_chunk - 1) / pool_chunk;
+  uint4 px[kPoolTok];
+  if (p.phases & PH_POOL) pool_issue(p, rq, slot, threadIdx.x, pool_items, 0, px);
+
+  // ---- then K and V of the first round (8x8 tiles, one per thread)
   const int ag = wave % L.AG, tg = wave / L.AG;
-  bf16x8 kf[2][DC];
-  const int nblk = n1 > n0 ? (n1 - n0 + 31) / 32 : 0;
-  if ((p.phases & PH_AGG) && tg < nblk) load_k_block<DC>(kf, p.k + hoff, n0 + 32 * tg, n1, p.d);
-  // V of the first round (up to kRoundTokens tokens), held in registers until
-  // the pooling loads have been issued, then written transposed to LDS
-  constexpr int VPF = 4 * DC;  // 16-byte pieces per thread for a full round
-  uint4 vpf[VPF];
-  const int DCH = p.d >> 3;
-  const int r0cnt = n1 > n0 ? min(kRoundTokens, n1 - n0) : 0;
+  const int r0cnt = n1 > n0 ? min(RT, n1 - n0) : 0;
+  const int r0pad = (r0cnt + 31) / 32 * 32;
+  const int r0tiles = (r0pad / 8) * DCH;
+  uint4 kx[8], vx[8];
   if (p.phases & PH_AGG) {
-#pragma unroll
-    for (int u = 0; u < VPF; ++u) {
-      const int f = threadIdx.x + kThreads * u;
-      const int t = f / DCH, ch = f - t * DCH;
-      if (t < r0cnt)
-        vpf[u] = *reinterpret_cast<const uint4*>(p.v + hoff + (long)(n0 + t) * p.d + 8 * ch);
-    }
+    const int it = threadIdx.x;
+    const int tend = it < r0tiles ? min(n1, n0 + r0cnt) : -1;
+    load_tile8(kx, rk, it, n0, tend, d);
+    load_tile8(vx, rv, it, n0, tend, d);
   }
-  constexpr int QPF = 2;  // query tiles prefetched per wave
-  bf16x8 qf[QPF][DC];
+  // query tiles of this wave, loaded ahead of the broadcast (registers)
   const int nqt = n1 > n0 ? (n1 - n0 + 15) / 16 : 0;
-  if (p.phases & PH_BCAST) {
+  bf16x8 qf[QPF][DC];
+  auto issue_q = [&]() {
 #pragma unroll
-    for (int u = 0; u < QPF; ++u)
-      if (wave + kWaves * u < nqt) load_q_tile<DC>(qf[u], p.q + hoff, n0 + 16 * (wave + kWaves * u), n1, p.d);
-  }
+    for (int u = 0; u < QPF; ++u) load_q_tile<DC>(qf[u], rq, n0 + 16 * (wave + kWaves * u), n1, d);
+  };
+  if ((p.phases & PH_BCAST) && !(p.phases & PH_AGG)) issue_q();
+  AA_STAMP(1);
 
   // ---- POOL
   if (p.phases & PH_POOL) {
-    pool_phase(p, head, slot, reinterpret_cast<float*>(big));
+    float* red = reinterpret_cast<float*>(big);
+    if (single) {
+      for (int f = threadIdx.x; f < a_frags; f += kThreads) Af[f] = zero_bf16x8();
+    }
+    const int TGP = p.pool_tgp;
+    const float rdch = rcp_approx(DCH);
+    for (int b0 = 0; b0 < pool_items; b0 += kThreads) {
+      float acc8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      for (int ps = 0; ps < pool_npass; ++ps) {
+        if (b0 > 0 || ps > 0) pool_issue(p, rq, slot, b0 + threadIdx.x, pool_items, ps * pool_chunk, px);
+        pool_accum(px, acc8);
+      }
+      __syncthreads();   // red free
+      *reinterpret_cast<float4*>(red + threadIdx.x * 8) = float4{acc8[0], acc8[1], acc8[2], acc8[3]};
+      *reinterpret_cast<float4*>(red + threadIdx.x * 8 + 4) = float4{acc8[4], acc8[5], acc8[6], acc8[7]};
+      __syncthreads();
+      // pairs (m, c) of this batch (TGP divides kThreads)
+      const int pr0 = b0 >> p.pool_tgp_log2, npr = min(kThreads, pool_items - b0) >> p.pool_tgp_log2;
+      for (int o = threadIdx.x; o < npr; o += kThreads) {
+        const int pr = pr0 + o;
+        const int m = idiv(pr, DCH, rdch), c = pr - m * DCH;
+        const int a = slot + p.P * m;
+        float s8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < TGP; ++t) {
+          const float4 lo = *reinterpret_cast<const float4*>(red + (o * TGP + t) * 8);
+          const float4 hi = *reinterpret_cast<const float4*>(red + (o * TGP + t) * 8 + 4);
+          s8[0] += lo.x; s8[1] += lo.y; s8[2] += lo.z; s8[3] += lo.w;
+          s8[4] += hi.x; s8[5] += hi.y; s8[6] += hi.z; s8[7] += hi.w;
+        }
+        const float inv = 1.0f / (float)pool_geo(p, a).cnt;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s8[e] *= inv;
+        if (single) {
+          // one whole A fragment: agent a, channels 8c..8c+7
+          const int t16 = a >> 4, r = a & 15, g = c / DC, cc = c - g * DC;
+          union { bf16x8 v; unsigned u[4]; } fr;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) fr.u[e] = pack_bf16(s8[2 * e], s8[2 * e + 1]);
+          Af[(t16 * DC + cc) * 64 + 16 * g + r] = fr.v;
+        } else {
+          const rsrc_t ra = rsrc_of(p.agents_f32 + ahb, arow_bytes);
+          const unsigned off = (unsigned)((a * d + 8 * c) * 4);
+          const uint4 lo = f4_bits(float4{s8[0], s8[1], s8[2], s8[3]});
+          const uint4 hi = f4_bits(float4{s8[4], s8[5], s8[6], s8[7]});
+          if (sync_group) { bst16<kCoherent>(ra, off, lo); bst16<kCoherent>(ra, off + 16, hi); }
+          else { bst16<kPlain>(ra, off, lo); bst16<kPlain>(ra, off + 16, hi); }
+        }
+      }
+    }
+    AA_STAMP(2);
     if (sync_group) ok = group_barrier(ctr + 0 * kSyncStride, p.P, p.status);
-    __syncthreads();
+    AA_STAMP(3);
   }
-  const bool coherent = sync_group;  // data crosses workgroups only when P > 1
 
-  // ---- agents -> LDS fragments
-  if (p.phases & (PH_AGG | PH_BCAST)) {
-    load_agent_frags<DC>(Af, p, head, coherent);
-    __syncthreads();
+  // ---- agents -> LDS fragments (zero for padding agents and channels)
+  if ((p.phases & (PH_AGG | PH_BCAST)) && !(single && (p.phases & PH_POOL))) {
+    const bool from_rows = !p.agents_in;
+    const float* rows = p.agents_f32_in ? p.agents_f32_in : p.agents_f32;
+    const rsrc_t ra = from_rows ? rsrc_of(rows + ahb, arow_bytes)
+                                : rsrc_of(p.agents_in + ahb, (unsigned)(p.nag * d * 2));
+    for (int f0 = 0; f0 < a_frags; f0 += 2 * kThreads) {
+      uint4 x[2][2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int f = f0 + threadIdx.x + kThreads * u;
+        const int fl = f & 63, c = (f >> 6) % DC, t = (f >> 6) / DC;
+        const int agent = 16 * t + (fl & 15), ch0 = 8 * (DC * (fl >> 4) + c);
+        const bool in = f < a_frags && agent < p.nag && ch0 < d;
+        if (from_rows) {
+          const unsigned off = in ? (unsigned)((agent * d + ch0) * 4) : kOOB;
+          if (sync_group) { x[u][0] = bld16<kCoherent>(ra, off); x[u][1] = bld16<kCoherent>(ra, off + 16); }
+          else { x[u][0] = bld16<kPlain>(ra, off); x[u][1] = bld16<kPlain>(ra, off + 16); }
+        } else {
+          x[u][0] = bld16<kPlain>(ra, in ? (unsigned)((agent * d + ch0) * 2) : kOOB);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int f = f0 + threadIdx.x + kThreads * u;
+        if (f >= a_frags) continue;
+        if (from_rows) {
+          const float4 a0 = bits_f4(x[u][0]), a1 = bits_f4(x[u][1]);
+          union { bf16x8 v; unsigned w[4]; } fr;
+          fr.w[0] = pack_bf16(a0.x, a0.y);
+          fr.w[1] = pack_bf16(a0.z, a0.w);
+          fr.w[2] = pack_bf16(a1.x, a1.y);
+          fr.w[3] = pack_bf16(a1.z, a1.w);
+          Af[f] = fr.v;
+        } else {
+          Af[f] = __builtin_bit_cast(bf16x8, x[u][0]);
+        }
+      }
+    }
   }
+  __syncthreads();
+  AA_STAMP(4);
 
   // ---- AGGREGATE
+  bf16x8* VAf = reinterpret_cast<bf16x8*>(big + (L.stage_lds ? L.stage_bytes : 0));
+  float* stage = reinterpret_cast<float*>(big);   // V_A rows [KT*16][DPAD] (single mode)
   if (p.phases & PH_AGG) {
     AggState<DC> st;
 #pragma unroll
@@ -557,168 +723,253 @@ agent_mfma_kernel(MfmaParams p) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) st.acc[a][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    bf16_t* Vt = reinterpret_cast<bf16_t*>(big);
-    const bf16_t* Kh = p.k + hoff;
-    bool have_k = true;  // kf holds this wave's first block of the slice
-    for (int rt0 = n0; rt0 < n1; rt0 += kRoundTokens) {
-      const int rcnt = min(kRoundTokens, n1 - rt0);
-      const int rcnt_pad = (rcnt + 31) / 32 * 32;
-      __syncthreads();
+    for (int rt0 = n0; rt0 < n1; rt0 += RT) {
+      const int rcnt = min(RT, n1 - rt0);
+      const int rpad = (rcnt + 31) / 32 * 32;
+      const int ntile = (rpad / 8) * DCH;
+      __syncthreads();   // previous round (or the pooling sums) fully read
       if (rt0 == n0) {
-#pragma unroll
-        for (int u = 0; u < VPF; ++u) {
-          const int f = threadIdx.x + kThreads * u;
-          const int t = f / DCH, ch = f - t * DCH;
-          if (t < rcnt) store_transposed8(Vt + 8 * ch * L.vt_stride + t, L.vt_stride, vpf[u]);
+        if (threadIdx.x < ntile) {
+          store_tile_rows(Ks, L.ks_stride, kx, threadIdx.x, d);
+          store_tile_t(Vt, L.vt_stride, vx, threadIdx.x, d);
         }
       } else {
-        stage_v(Vt, L.vt_stride, p.v + hoff, rt0, rcnt, p.d);
+        for (int it0 = 0; it0 < ntile; it0 += kThreads) {
+          const int it = it0 + threadIdx.x;
+          const int tend = it < ntile ? n1 : -1;
+          load_tile8(kx, rk, it, rt0, tend, d);
+          load_tile8(vx, rv, it, rt0, tend, d);
+          if (it < ntile) {
+            store_tile_rows(Ks, L.ks_stride, kx, it, d);
+            store_tile_t(Vt, L.vt_stride, vx, it, d);
+          }
+        }
       }
-      zero_v_tail(Vt, L.vt_stride, rcnt, rcnt_pad, 32 * DC);
       __syncthreads();
-      const int rblk = rcnt_pad / 32;
-      for (int b = tg; b < rblk; b += L.TG) {
-        const int tok0 = rt0 + 32 * b;
-        if (!have_k) load_k_block<DC>(kf, Kh, tok0, n1, p.d);
-        have_k = false;
-        agg_block<DC>(st, kf, Af, Vt, L.vt_stride, 32 * b, ag, L.KT, min(32, n1 - tok0), p.sl2);
-      }
-      // a wave with no block in this round keeps its prefetched block for the next one
-      if (tg >= rblk) have_k = false;
+      const int rblk = rpad / 32;
+      for (int b = tg; b < rblk; b += L.TG)
+        agg_block<DC>(st, Ks, L.ks_stride, Af, Vt, L.vt_stride, 32 * b, ag, L.KT,
+                      min(32, n1 - (rt0 + 32 * b)), d, p.sl2);
     }
+    AA_STAMP(5);
+    if (single && (p.phases & PH_BCAST)) issue_q();   // in flight during the combine
 #pragma unroll
     for (int a = 0; a < 4; ++a) st.l[a] = group4_sum(st.l[a]);
 
-    // combine the TG token groups of each agent group through LDS
-    float* comb = reinterpret_cast<float*>(big);
-    constexpr int REC = 2 * DC * 4 + 2;  // floats per lane per agent tile
+    // combine the TG token groups of each agent group through LDS:
+    // records [rec][a][DT acc | 1 (m, l)][64 lanes] x 16 B
+    float4* comb = reinterpret_cast<float4*>(big);
+    constexpr int RQ = DT + 1;
     __syncthreads();
     if (tg > 0) {
-      float* dst = comb + (((tg - 1) * L.AG + ag) * 64 * 4) * REC;
+      float4* dst = comb + ((tg - 1) * L.AG + ag) * 4 * RQ * 64;
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        float* r = dst + (a * 64 + lane) * REC;
-        r[0] = st.m[a];
-        r[1] = st.l[a];
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) r[2 + dt * 4 + i] = st.acc[a][dt][i];
+          dst[(a * RQ + dt) * 64 + lane] =
+              float4{st.acc[a][dt][0], st.acc[a][dt][1], st.acc[a][dt][2], st.acc[a][dt][3]};
+        dst[(a * RQ + DT) * 64 + lane] = float4{st.m[a], st.l[a], 0.f, 0.f};
       }
     }
     __syncthreads();
     if (tg == 0) {
       for (int o = 1; o < L.TG; ++o) {
-        // the partner of wave (ag, 0) in token group o is wave o*AG + ag
-        const float* src = comb + (((o - 1) * L.AG + ag) * 64 * 4) * REC;
+        const float4* src = comb + ((o - 1) * L.AG + ag) * 4 * RQ * 64;
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
-          const float* r = src + (a * 64 + lane) * REC;
-          const float m2 = r[0], l2 = r[1];
-          const float mn = fmaxf(st.m[a], m2);
+          const float4 ml = src[(a * RQ + DT) * 64 + lane];
+          const float mn = fmaxf(st.m[a], ml.x);
           const float c1 = (mn == -INFINITY) ? 0.f : fast_exp2((st.m[a] - mn) * p.sl2);
-          const float c2 = (mn == -INFINITY) ? 0.f : fast_exp2((m2 - mn) * p.sl2);
-          st.l[a] = st.l[a] * c1 + l2 * c2;
+          const float c2 = (mn == -INFINITY) ? 0.f : fast_exp2((ml.x - mn) * p.sl2);
+          st.l[a] = st.l[a] * c1 + ml.y * c2;
           st.m[a] = mn;
 #pragma unroll
-          for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              st.acc[a][dt][i] = st.acc[a][dt][i] * c1 + r[2 + dt * 4 + i] * c2;
+          for (int dt = 0; dt < DT; ++dt) {
+            const float4 r = src[(a * RQ + dt) * 64 + lane];
+            st.acc[a][dt][0] = st.acc[a][dt][0] * c1 + r.x * c2;
+            st.acc[a][dt][1] = st.acc[a][dt][1] * c1 + r.y * c2;
+            st.acc[a][dt][2] = st.acc[a][dt][2] * c1 + r.z * c2;
+            st.acc[a][dt][3] = st.acc[a][dt][3] * c1 + r.w * c2;
+          }
         }
       }
-      // this wave now holds the workgroup's partial for agent tiles 4ag..4ag+3
-      const int g = lane >> 4;
+    }
+    // wave (ag, 0) now holds the workgroup's partial for agent tiles 4ag..4ag+3
+    const int g = lane >> 4;
+    if (p.P == 1) {
+      // V_A rows: staging (LDS or the fp32 scratch) in single mode, the fp32
+      // output otherwise
+      __syncthreads();   // comb fully read (it aliases the staging rows)
+      if (tg == 0) {
+        const bool lds_rows = single && L.stage_lds;
+        const rsrc_t rvo = rsrc_of(p.values_f32 + ahb, arow_bytes);
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const int agent = 16 * (4 * ag + a) + (lane & 15);
+          const float inv = 1.0f / st.l[a];
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) {
+            const int ch = 16 * dt + 4 * g;
+            const float4 x = float4{st.acc[a][dt][0] * inv, st.acc[a][dt][1] * inv,
+                                    st.acc[a][dt][2] * inv, st.acc[a][dt][3] * inv};
+            if (lds_rows) {
+              if (4 * ag + a < L.KT) *reinterpret_cast<float4*>(stage + agent * DPAD + ch) = x;
+            } else {
+              const unsigned off = (agent < p.nag && ch < d) ? (unsigned)((agent * d + ch) * 4) : kOOB;
+              bst16<kPlain>(rvo, off, f4_bits(x));
+            }
+          }
+        }
+      }
+    } else if (tg == 0) {
+      // partials in register order: one contiguous 1 KiB row per (tile, dt)
+      const long pbase = ((long)head * p.P + slot) * L.KT;
+      const rsrc_t racc = rsrc_of(p.part_acc + pbase * DT * 256, (unsigned)(L.KT * DT * 1024));
+      const rsrc_t rml = rsrc_of(p.part_ml + pbase * 32, (unsigned)(L.KT * 128));
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        const int agent = 16 * (4 * ag + a) + (lane & 15);
-        if (agent >= p.nag) continue;
-        if (p.P == 1) {
-          // single slice: V_A directly
-          const float inv = 1.0f / st.l[a];
-          float* dst = p.values_f32 + ((long)head * p.nag + agent) * p.d;
+        const int t = 4 * ag + a;
+        if (t >= L.KT) continue;
 #pragma unroll
-          for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int ch = 16 * dt + 4 * g + i;
-              if (ch < p.d) dst[ch] = st.acc[a][dt][i] * inv;
-            }
-        } else {
-          float* dst = p.part + (((long)head * p.nag + agent) * p.P + slot) * (p.d + 2);
-          if (g == 0) {
-            if (coherent) { st_dev(dst, st.m[a]); st_dev(dst + 1, st.l[a]); }
-            else { dst[0] = st.m[a]; dst[1] = st.l[a]; }
-          }
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int ch = 16 * dt + 4 * g + i;
-              if (ch < p.d) {
-                if (coherent) st_dev(dst + 2 + ch, st.acc[a][dt][i]);
-                else dst[2 + ch] = st.acc[a][dt][i];
-              }
-            }
+        for (int dt = 0; dt < DT; ++dt) {
+          const unsigned off = (unsigned)(((t * DT + dt) * 64 + lane) * 16);
+          const uint4 x = f4_bits(float4{st.acc[a][dt][0], st.acc[a][dt][1], st.acc[a][dt][2],
+                                         st.acc[a][dt][3]});
+          if (sync_group) bst16<kCoherent>(racc, off, x);
+          else bst16<kPlain>(racc, off, x);
         }
+        const unsigned moff = g == 0 ? (unsigned)((t * 16 + (lane & 15)) * 8) : kOOB;
+        const uint2 ml = uint2{__float_as_uint(st.m[a]), __float_as_uint(st.l[a])};
+        if (sync_group) bst8<kCoherent>(rml, moff, ml);
+        else bst8<kPlain>(rml, moff, ml);
       }
     }
+    AA_STAMP(6);
+    if (sync_group && (p.phases & PH_BCAST)) issue_q();   // in flight during the merge
     if (sync_group && ok) ok = group_barrier(ctr + 1 * kSyncStride, p.P, p.status);
+    AA_STAMP(7);
   }
 
-  // ---- MERGE: agents a = slot, slot+P, ... ; one wave per agent, lanes over channels
+  // ---- MERGE: items (agent a = slot + P*m, channel quad q) over the threads
   if ((p.phases & PH_MERGE) && p.P > 1 && ok) {
-    for (int a = slot + p.P * wave; a < p.nag; a += p.P * kWaves) {
-      const float* src = p.part + ((long)head * p.nag + a) * p.P * (p.d + 2);
-      float M = -INFINITY;
-      for (int sl = 0; sl < p.P; ++sl) M = fmaxf(M, coherent ? ld_dev(src + sl * (p.d + 2)) : src[sl * (p.d + 2)]);
-      float Lsum = 0.f;
-      float acc0 = 0.f, acc1 = 0.f;
-      for (int sl = 0; sl < p.P; ++sl) {
-        const float* r = src + sl * (p.d + 2);
-        const float m = coherent ? ld_dev(r) : r[0];
-        const float wgt = (m == -INFINITY) ? 0.f : fast_exp2((m - M) * p.sl2);
-        Lsum = fmaf(coherent ? ld_dev(r + 1) : r[1], wgt, Lsum);
-        if (lane < p.d) acc0 = fmaf(coherent ? ld_dev(r + 2 + lane) : r[2 + lane], wgt, acc0);
-        if (lane + 64 < p.d)
-          acc1 = fmaf(coherent ? ld_dev(r + 2 + lane + 64) : r[2 + lane + 64], wgt, acc1);
+    constexpr int nq = DPAD / 4;
+    const int items = pool_na * nq;   // agents slot, slot+P, ... (pool_na of them)
+    const long hbase = (long)head * p.P * L.KT;
+    const rsrc_t racc = rsrc_of(p.part_acc + hbase * DT * 256, (unsigned)(p.P * L.KT * DT * 1024));
+    const rsrc_t rml = rsrc_of(p.part_ml + hbase * 32, (unsigned)(p.P * L.KT * 128));
+    const rsrc_t rvo = rsrc_of(p.values_f32 + ahb, arow_bytes);
+    for (int it = threadIdx.x; it < items; it += kThreads) {
+      const int m = it / nq, q = it - m * nq;
+      const int a = slot + p.P * m;
+      const int t = a >> 4, r = a & 15, dt = q >> 2, g = q & 3;
+      const unsigned aoff = (unsigned)(((t * DT + dt) * 64 + 16 * g + r) * 16);
+      const unsigned moff = (unsigned)((t * 16 + r) * 8);
+      const unsigned sstride_acc = (unsigned)(L.KT * DT * 1024), sstride_ml = (unsigned)(L.KT * 128);
+      float M = -INFINITY, Ls = 0.f;
+      float4 acc = float4{0.f, 0.f, 0.f, 0.f};
+      for (int s0 = 0; s0 < p.P; s0 += 8) {
+        uint4 xa[8];
+        u32x2 xm[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const bool in = s0 + u < p.P;
+          const unsigned so = (unsigned)(s0 + u);
+          if (sync_group) {
+            xa[u] = bld16<kCoherent>(racc, in ? aoff + so * sstride_acc : kOOB);
+            xm[u] = __builtin_amdgcn_raw_buffer_load_b64(rml, (int)(in ? moff + so * sstride_ml : kOOB), 0, kCoherent);
+          } else {
+            xa[u] = bld16<kPlain>(racc, in ? aoff + so * sstride_acc : kOOB);
+            xm[u] = __builtin_amdgcn_raw_buffer_load_b64(rml, (int)(in ? moff + so * sstride_ml : kOOB), 0, kPlain);
+          }
+        }
+        float cm = M;
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (s0 + u < p.P) cm = fmaxf(cm, __uint_as_float(xm[u][0]));
+        const float corr = (cm == -INFINITY) ? 0.f : fast_exp2((M - cm) * p.sl2);
+        Ls *= corr;
+        acc.x *= corr; acc.y *= corr; acc.z *= corr; acc.w *= corr;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (s0 + u >= p.P) continue;
+          const float mu = __uint_as_float(xm[u][0]);
+          const float wgt = (mu == -INFINITY) ? 0.f : fast_exp2((mu - cm) * p.sl2);
+          const float4 av = bits_f4(xa[u]);
+          Ls = fmaf(__uint_as_float(xm[u][1]), wgt, Ls);
+          acc.x = fmaf(av.x, wgt, acc.x);
+          acc.y = fmaf(av.y, wgt, acc.y);
+          acc.z = fmaf(av.z, wgt, acc.z);
+          acc.w = fmaf(av.w, wgt, acc.w);
+        }
+        M = cm;
       }
-      const float inv = 1.0f / Lsum;
-      float* dst = p.values_f32 + ((long)head * p.nag + a) * p.d;
-      if (lane < p.d) { if (coherent) st_dev(dst + lane, acc0 * inv); else dst[lane] = acc0 * inv; }
-      if (lane + 64 < p.d) {
-        if (coherent) st_dev(dst + lane + 64, acc1 * inv); else dst[lane + 64] = acc1 * inv;
-      }
+      const float inv = 1.0f / Ls;
+      const int ch = 16 * dt + 4 * g;
+      const unsigned off = (a < p.nag && ch < d) ? (unsigned)((a * d + ch) * 4) : kOOB;
+      const uint4 x = f4_bits(float4{acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv});
+      if (sync_group) bst16<kCoherent>(rvo, off, x);
+      else bst16<kPlain>(rvo, off, x);
     }
+    AA_STAMP(8);
     if (sync_group && ok) ok = group_barrier(ctr + 2 * kSyncStride, p.P, p.status);
+    AA_STAMP(9);
   }
 
   // ---- BROADCAST
   if ((p.phases & PH_BCAST) && ok) {
+    // V_A fragments from rows: LDS staging (single mode), the exchanged rows
+    // (groups) or the fp32 input (step call); padding positions are zero
+    const bool lds_rows = single && L.stage_lds && (p.phases & PH_AGG);
+    const float* rows = p.values_f32_in ? p.values_f32_in : p.values_f32;
+    const rsrc_t rvr = rsrc_of(rows + ahb, arow_bytes);
     __syncthreads();
-    bf16x8* VAf = reinterpret_cast<bf16x8*>(big);
-    const float* VA = p.values_f32_in ? p.values_f32_in : p.values_f32;
-    // single-slice fused runs read V_A written by this workgroup: a
-    // workgroup barrier orders it (plain loads suffice)
-    load_value_frags<DC>(VAf, VA, p, head, coherent && p.P > 1);
+    for (int f0 = 0; f0 < va_frags; f0 += kThreads) {
+      const int f = f0 + threadIdx.x;
+      const int fl = f & 63, dt = (f >> 6) % DT, j = (f >> 6) / DT;
+      const int ch = 16 * dt + (fl & 15), g = fl >> 4;
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int agent = pair_index(j, g, e);
+        const bool in = f < va_frags && agent < p.nag && ch < d;
+        if (lds_rows) {
+          x[e] = in ? stage[agent * DPAD + ch] : 0.f;
+        } else {
+          const unsigned off = in ? (unsigned)((agent * d + ch) * 4) : kOOB;
+          x[e] = sync_group ? bld4<kCoherent>(rvr, off) : bld4<kPlain>(rvr, off);
+        }
+      }
+      if (f < va_frags) {
+        union { bf16x8 v; bf16_t e[8]; } hi, lo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          hi.e[e] = bf16_bits(x[e]);
+          lo.e[e] = bf16_bits(x[e] - bf16_value(hi.e[e]));
+        }
+        VAf[f] = hi.v;
+        if (L.vparts > 1) VAf[va_frags + f] = lo.v;
+      }
+    }
     __syncthreads();
-    bf16_t* Oh = p.out + hoff;
-    const bf16_t* Qh = p.q + hoff;
+    AA_STAMP(10);
+    const rsrc_t ro = rsrc_of(p.out + hoff, head_bytes);
     int u = 0;
     for (int qt = wave; qt < nqt; qt += kWaves, ++u) {
       bf16x8 qcur[DC];
-      if (u < QPF) {
+      bool pre = false;
 #pragma unroll
-        for (int uu = 0; uu < QPF; ++uu)
-          if (uu == u)
+      for (int uu = 0; uu < QPF; ++uu)
+        if (uu == u) {
+          pre = true;
 #pragma unroll
-            for (int c = 0; c < DC; ++c) qcur[c] = qf[uu][c];
-      } else {
-        load_q_tile<DC>(qcur, Qh, n0 + 16 * qt, n1, p.d);
-      }
-      bcast_tile<DC>(qcur, Af, VAf, Oh, n0 + 16 * qt, n1, p.d, p.nag, p.sl2);
+          for (int c = 0; c < DC; ++c) qcur[c] = qf[uu][c];
+        }
+      if (!pre) load_q_tile<DC>(qcur, rq, n0 + 16 * qt, n1, d);
+      bcast_tile<DC>(qcur, Af, VAf, va_frags, L.vparts, ro, n0 + 16 * qt, n1, d, p.nag, p.sl2);
     }
   }
+  AA_STAMP(11);
 
   // ---- reset the group's counters once every workgroup of the group is done
   if (sync_group) {
