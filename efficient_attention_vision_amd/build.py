@@ -12,11 +12,11 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libagent_attn.so")
-SOURCES = ["agent_attn.hip"]
+SOURCES = ["agent_attn.hip", "mfma_dc1.hip", "mfma_dc2.hip", "mfma_dc4.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-FLAGS = [
-    "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared",
+COMPILE_FLAGS = [
+    "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC",
     # the packed-fp32 VALU forms are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
@@ -24,22 +24,40 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, *srcs, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+def _filter(out: str) -> str:
     # hipcc's host pass does not know the packed-fp32 feature and says so
-    out = "\n".join(l for l in r.stdout.splitlines()
-                    if "packed-fp32-ops' is not a recognized feature" not in l)
+    return "\n".join(l for l in out.splitlines()
+                     if "packed-fp32-ops' is not a recognized feature" not in l)
+
+
+def build(verbose: bool = False, extra_flags=(), output: str = LIB) -> str:
+    """Compile every source to an object in parallel, then link the library."""
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    procs = []
+    for src in SOURCES:
+        obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
+        cmd = [HIPCC, *COMPILE_FLAGS, *extra_flags, "-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((src, obj, subprocess.Popen(cmd, stdout=subprocess.PIPE,
+                                                 stderr=subprocess.STDOUT, text=True)))
+    objs = []
+    for src, obj, pr in procs:
+        out, _ = pr.communicate()
+        out = _filter(out)
+        if pr.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src} ({pr.returncode}):\n{out}")
+        if verbose and out.strip():
+            print(out)
+        objs.append(obj)
+    tmp = output + ".tmp"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{out}")
-    if verbose and out.strip():
-        print(out)
-    os.replace(tmp, LIB)
-    return LIB
+        raise RuntimeError(f"link failed ({r.returncode}):\n{_filter(r.stdout)}")
+    os.replace(tmp, output)
+    return output
 
 
 if __name__ == "__main__":

@@ -130,6 +130,11 @@ struct Plan {
   size_t off_ml = 0;
 };
 
+// Matrix-core kernel instance for these sizes: DC 32-channel chunks
+// (1, 2 or 4) and KTC 16-agent tiles (4, 8 or 16).
+int mfma_dc(int d) { return d <= 32 ? 1 : (d <= 64 ? 2 : 4); }
+int mfma_ktc(int nag) { return nag <= 64 ? 4 : (nag <= 128 ? 8 : 16); }
+
 constexpr size_t kSyncBytesPerHead = (aa::kBarriers + 1) * aa::kSyncStride * sizeof(unsigned);
 // Heads that can own group counters: P > 1 needs B*H*P <= CUs, so at most
 // CUs/2 heads.  The counters live in a fixed-size prefix of every workspace
@@ -151,23 +156,24 @@ void aggregate_split(const Dims& D, int& chunk, int& nchunks) {
   nchunks = (int)((D.N + ch - 1) / ch);
 }
 
+
+template <int DC>
+int lds_for(int ktc) {
+  return ktc == 4 ? aa::Cfg<DC, 4>::TOTAL : ktc == 8 ? aa::Cfg<DC, 8>::TOTAL : aa::Cfg<DC, 16>::TOTAL;
+}
 int mfma_lds_bytes(int DC, int nag) {
-  switch (DC) {
-    case 1: return aa::LdsPlan<1>(nag).total;
-    case 2: return aa::LdsPlan<2>(nag).total;
-    case 3: return aa::LdsPlan<3>(nag).total;
-    default: return aa::LdsPlan<4>(nag).total;
-  }
+  const int ktc = mfma_ktc(nag);
+  return DC == 1 ? lds_for<1>(ktc) : DC == 2 ? lds_for<2>(ktc) : lds_for<4>(ktc);
 }
 
 // Partials of the matrix-core aggregation, in register order: per (head,
 // slot, agent tile) the max/sum of 16 agents and 2*DC rows of 64 x 4 floats.
 size_t mfma_ml_bytes(const Dims& D, int P, int DC) {
   (void)DC;
-  return (size_t)D.BH * P * ((D.nag + 15) / 16) * 16 * 2 * sizeof(float);
+  return (size_t)D.BH * P * mfma_ktc(D.nag) * 16 * 2 * sizeof(float);
 }
 size_t mfma_acc_bytes(const Dims& D, int P, int DC) {
-  return (size_t)D.BH * P * ((D.nag + 15) / 16) * 2 * DC * 256 * sizeof(float);
+  return (size_t)D.BH * P * mfma_ktc(D.nag) * 2 * DC * 256 * sizeof(float);
 }
 
 // Pooling window geometry: the largest window (tokens) and the number of
@@ -225,7 +231,7 @@ Plan make_plan(const Dims& D, int cus) {
     aggregate_split(D, P.chunk, P.nchunks);
     part_bytes = (size_t)D.BH * P.nchunks * D.nag * (D.d + 2) * sizeof(float);
   } else {
-    P.DC = (D.d + 31) / 32;
+    P.DC = mfma_dc(D.d);
     mfma_split(D, cus, P.P, P.T);
     P.lds = mfma_lds_bytes(P.DC, D.nag);
     P.fused = 1;  // BH*P <= CUs: the whole grid is co-resident
@@ -313,28 +319,16 @@ int launch_broadcast(const Dims& D, const void* q, const float* A, const float* 
 long long* g_trace = nullptr;  // profiling builds: per-workgroup phase stamps
 #endif
 
-// Two register budgets: one workgroup per CU (grid-synchronised groups, at
-// most one workgroup per CU by construction) or two per CU (independent
-// workgroups, P = 1, grids larger than the chip).
-template <int DC>
-int launch_mfma_dc(const aa::MfmaParams& mp, long grid, int lds, hipStream_t st) {
-  if (mp.P > 1)
-    hipLaunchKernelGGL((aa::agent_mfma_kernel<DC, 1>), dim3((unsigned)grid), dim3(aa::kThreads),
-                       (unsigned)lds, st, mp);
-  else
-    hipLaunchKernelGGL((aa::agent_mfma_kernel<DC, 2>), dim3((unsigned)grid), dim3(aa::kThreads),
-                       (unsigned)lds, st, mp);
-  AA_LAUNCH_CHECK("agent attention matrix-core kernel launch");
-  return AGENT_ATTN_OK;
-}
-
-int launch_mfma(int DC, const aa::MfmaParams& mp, long grid, int lds, hipStream_t st) {
+int launch_mfma(int DC, const aa::MfmaParams& mp, long grid, int nag, hipStream_t st) {
+  const int ktc = mfma_ktc(nag);
+  int e;
   switch (DC) {
-    case 1: return launch_mfma_dc<1>(mp, grid, lds, st);
-    case 2: return launch_mfma_dc<2>(mp, grid, lds, st);
-    case 3: return launch_mfma_dc<3>(mp, grid, lds, st);
-    default: return launch_mfma_dc<4>(mp, grid, lds, st);
+    case 1: e = aa::launch_mfma_dc<1>(mp, ktc, grid, st); break;
+    case 2: e = aa::launch_mfma_dc<2>(mp, ktc, grid, st); break;
+    default: e = aa::launch_mfma_dc<4>(mp, ktc, grid, st); break;
   }
+  if (e != hipSuccess) return hip_fail((hipError_t)e, "agent attention matrix-core kernel launch");
+  return AGENT_ATTN_OK;
 }
 
 aa::MfmaParams mfma_params(const Dims& D, int P, int T, float scale) {
@@ -370,7 +364,7 @@ int run_mfma_phases(const Dims& D, aa::MfmaParams mp, int DC, int phases, bool f
   if (fused) {
     mp.phases = phases;
     mp.fused = 1;
-    return launch_mfma(DC, mp, grid, lds, st);
+    return launch_mfma(DC, mp, grid, D.nag, st);
   }
   mp.fused = 0;
   mp.xcd_heads = 0;
@@ -378,7 +372,7 @@ int run_mfma_phases(const Dims& D, aa::MfmaParams mp, int DC, int phases, bool f
     if (!(phases & ph)) continue;
     if (ph == aa::PH_MERGE && mp.P == 1) continue;
     mp.phases = ph;
-    const int rc = launch_mfma(DC, mp, grid, lds, st);
+    const int rc = launch_mfma(DC, mp, grid, D.nag, st);
     if (rc) return rc;
   }
   return AGENT_ATTN_OK;
@@ -489,7 +483,7 @@ size_t aggregate_ws_bytes(const Dims& D) {
   }
   int P, T;
   mfma_split(D, device_cus(), P, T);
-  const int DC = (D.d + 31) / 32;
+  const int DC = mfma_dc(D.d);
   return align_up(mfma_ml_bytes(D, P, DC), 256) + align_up(mfma_acc_bytes(D, P, DC), 256);
 }
 
@@ -558,7 +552,7 @@ int agent_attn_pool(const void* q, float* agents_f32, int B, int H, int h, int w
   aa::MfmaParams mp = mfma_params(D, 1, (int)D.N, 1.0f);
   mp.q = (const aa::bf16_t*)q;
   mp.agents_f32 = agents_f32;
-  return run_mfma_phases(D, mp, (D.d + 31) / 32, aa::PH_POOL, false, st);
+  return run_mfma_phases(D, mp, mfma_dc(D.d), aa::PH_POOL, false, st);
 }
 
 size_t agent_attn_aggregate_workspace_bytes(int B, int H, int N, int d, int n_agents, int dtype) {
@@ -611,8 +605,8 @@ int agent_attn_aggregate(const float* agents_f32, const void* k, const void* v,
   mp.agents_f32_in = agents_f32;
   mp.values_f32 = agent_values_f32;
   mp.part_ml = part;
-  mp.part_acc = (float*)((char*)workspace + align_up(mfma_ml_bytes(D, P, (D.d + 31) / 32), 256));
-  return run_mfma_phases(D, mp, (D.d + 31) / 32, aa::PH_AGG | aa::PH_MERGE, false, st);
+  mp.part_acc = (float*)((char*)workspace + align_up(mfma_ml_bytes(D, P, mfma_dc(D.d)), 256));
+  return run_mfma_phases(D, mp, mfma_dc(D.d), aa::PH_AGG | aa::PH_MERGE, false, st);
 }
 
 int agent_attn_broadcast(const void* q, const float* agents_f32, const float* agent_values_f32,
@@ -644,7 +638,7 @@ int agent_attn_broadcast(const void* q, const float* agents_f32, const float* ag
   mp.out = (aa::bf16_t*)out;
   mp.agents_f32_in = agents_f32;
   mp.values_f32_in = agent_values_f32;
-  return run_mfma_phases(D, mp, (D.d + 31) / 32, aa::PH_BCAST, false, st);
+  return run_mfma_phases(D, mp, mfma_dc(D.d), aa::PH_BCAST, false, st);
 }
 
 void agent_attn_release(void) {

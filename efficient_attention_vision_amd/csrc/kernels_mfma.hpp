@@ -51,9 +51,8 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 enum : int { PH_POOL = 1, PH_AGG = 2, PH_MERGE = 4, PH_BCAST = 8 };
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;                // waves per workgroup
 constexpr int kThreads = 64 * kWaves;
-constexpr int kVtPad = 8;                // LDS row padding (bf16) of staged V^T
 constexpr int kBarriers = 3;
 constexpr int kSyncStride = 32;          // dwords between counters (own 128 B line)
 constexpr long kSpinLimit = 1L << 20;    // bounded waits: ~1 s, then an error
@@ -185,17 +184,21 @@ __device__ __forceinline__ float4 bits_f4(uint4 x) {
                 __uint_as_float(x.w)};
 }
 
-// Barrier of the P workgroups of one head.  Counters start at zero in every
-// launch: the last workgroup to finish the kernel resets them.  Every wave
-// first waits for its own loads and stores to complete, so data stored
-// before the barrier is visible to device-coherent loads after it.
-__device__ __forceinline__ bool group_barrier(unsigned* ctr, unsigned n, int* status) {
-  __shared__ int ok;
+// Barrier of the P workgroups of one head, in two halves so that loads can
+// be issued between the arrival and the wait.  Counters start at zero in
+// every launch: the last workgroup to finish the kernel resets them.  Before
+// arriving, every wave waits for its own loads and stores to complete, so
+// data stored before the barrier is visible to device-coherent loads after
+// it.
+__device__ __forceinline__ void group_arrive(unsigned* ctr) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool group_wait(unsigned* ctr, unsigned n, int* status) {
+  __shared__ int ok;
   if (threadIdx.x == 0) {
     ok = 1;
-    __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     long spins = 0;
     while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < n) {
       if (++spins > kSpinLimit) {
@@ -209,6 +212,10 @@ __device__ __forceinline__ bool group_barrier(unsigned* ctr, unsigned n, int* st
   }
   __syncthreads();
   return ok != 0;
+}
+__device__ __forceinline__ bool group_barrier(unsigned* ctr, unsigned n, int* status) {
+  group_arrive(ctr);
+  return group_wait(ctr, n, status);
 }
 
 // Agent index held at contraction position e (0..7) of lane group g in the
@@ -235,55 +242,42 @@ __device__ __forceinline__ void transpose8x8(const uint4 (&x)[8], uint4 (&y)[8])
   }
 }
 
-// ------------------------------------------------------------ LDS plan
-// Bytes, computed identically on the host by mfma_lds_bytes():
-//   [0, a_bytes)      A fragments [KT][DC][64 lanes] x 8 bf16
-//   [a_bytes, +big)   union of: pooling partial sums; {staged V^T, staged K
-//                     rows} of one round; cross-wave partials; {V_A staging
-//                     rows, V_A fragments}
-template <int DC>
-struct LdsPlan {
-  static constexpr int RT = DC <= 2 ? 256 : 128;   // tokens per round
-  int KT, KC, AG, TG, vparts, stage_lds;
-  int a_bytes, vt_stride, vt_bytes, ks_stride, ks_bytes, comb_bytes, va_bytes, stage_bytes;
-  int big, total;
-  __host__ __device__ LdsPlan(int nag) {
-    constexpr int DPAD = 32 * DC;
-    constexpr int kMaxLds = 160 * 1024 - 64;   // static LDS of the barrier flag
-    KT = (nag + 15) / 16;
-    KC = (nag + 31) / 32;
-    AG = KT <= 4 ? 1 : (KT <= 8 ? 2 : 4);
-    TG = kWaves / AG;
-    a_bytes = KT * DC * 1024;
-    vt_stride = RT + kVtPad;
-    vt_bytes = DPAD * vt_stride * 2;
-    ks_stride = DPAD + 8;
-    ks_bytes = RT * ks_stride * 2;
-    comb_bytes = (TG - 1) * AG * 4 * (2 * DC + 1) * 64 * 16;
-    stage_bytes = KT * 16 * DPAD * 4;
-    const int pool_bytes = kThreads * 8 * 4;
-    // V_A as hi + lo when it fits, staging rows in LDS when they fit
-    vparts = 2;
-    stage_lds = 1;
-    for (;;) {
-      va_bytes = vparts * KC * 2 * DC * 1024;
-      const int need = va_bytes + (stage_lds ? stage_bytes : 0);
-      big = vt_bytes + ks_bytes;
-      if (comb_bytes > big) big = comb_bytes;
-      if (pool_bytes > big) big = pool_bytes;
-      if (need > big) big = need;
-      total = a_bytes + big;
-      if (total <= kMaxLds) break;
-      if (stage_lds) stage_lds = 0;
-      else if (vparts == 2) { vparts = 1; stage_lds = 1; }
-      else break;   // host rejects
-    }
-  }
+// ------------------------------------------------------------ configuration
+// Compile-time shape of one kernel instance: DC 32-channel chunks of the head
+// dimension (DPAD = 32*DC >= d), KTC 16-agent tiles (16*KTC >= agents).
+template <int DC, int KTC>
+struct Cfg {
+  static constexpr int DT = 2 * DC;                // 16-channel output tiles
+  static constexpr int DPAD = 32 * DC;
+  static constexpr int RT = DC <= 2 ? 256 : 128;   // tokens per K/V round
+  static constexpr int AG = KTC < kWaves ? KTC : kWaves;   // agent groups of waves
+  static constexpr int ATW = KTC / AG;             // agent tiles per wave
+  static constexpr int TG = kWaves / AG;           // token groups of waves
+  static constexpr int KC = (KTC + 1) / 2;         // 32-agent chunks
+  static constexpr int VSPLIT = KTC <= 4 ? 2 : 1;  // V_A as bf16 hi + lo
+  // LDS layout: [A fragments][big], big = union of
+  //   pooling sums | {V^T, K rows} of a round | cross-wave partials |
+  //   {V_A staging rows (if they fit), V_A fragments}
+  static constexpr int A_BYTES = KTC * DC * 1024;
+  static constexpr int VT_STRIDE = RT + 8;         // bf16, row = channel
+  static constexpr int VT_BYTES = DPAD * VT_STRIDE * 2;
+  static constexpr int KS_STRIDE = DPAD + 8;       // bf16, row = token
+  static constexpr int KS_BYTES = RT * KS_STRIDE * 2;
+  static constexpr int COMB_BYTES = (TG - 1) * AG * ATW * (DT + 1) * 1024;
+  static constexpr int STAGE_BYTES = KTC * 16 * DPAD * 4;
+  static constexpr int VA_BYTES = VSPLIT * KC * DT * 1024;
+  static constexpr int POOL_BYTES = kThreads * 32;
+  static constexpr int mx(int a, int b) { return a > b ? a : b; }
+  static constexpr int BASE = mx(mx(VT_BYTES + KS_BYTES, COMB_BYTES), POOL_BYTES);
+  static constexpr int kMaxLds = 160 * 1024 - 64;  // static LDS of the barrier flag
+  static constexpr int STAGE_LDS = A_BYTES + mx(BASE, STAGE_BYTES + VA_BYTES) <= kMaxLds;
+  static constexpr int BIG = mx(BASE, (STAGE_LDS ? STAGE_BYTES : 0) + VA_BYTES);
+  static constexpr int TOTAL = A_BYTES + BIG;
 };
 
 // ------------------------------------------------------------------ pooling
 // Agents a = slot + P*m (m < na) of the head.  Work item (m, chunk c, token
-// group tg) sums window tokens tg, tg + TGP, ... (kPoolTok of them) over 8
+// group tg) sums window tokens tg, tg + TGP, ... (kPoolTok per pass) over 8
 // channels; the TGP groups of a (m, c) pair are then added in a fixed order.
 struct PoolGeo {
   int r0, c0, wc, cnt;
@@ -325,94 +319,7 @@ __device__ __forceinline__ void pool_accum(const uint4 (&x)[kPoolTok], float (&a
   }
 }
 
-// ------------------------------------------------------------ aggregation
-// Per wave: agent tiles [4*ag, 4*ag+4) over the token blocks (32 tokens)
-// b = tg, tg+TG, ... of the workgroup's slice.
-template <int DC>
-struct AggState {
-  float m[4], l[4];
-  f32x4 acc[4][2 * DC];
-};
-
-template <int DC>
-__device__ __forceinline__ void agg_block(AggState<DC>& st, const bf16_t* Ks, int ks_stride,
-                                          const bf16x8* Af, const bf16_t* Vt, int vt_stride,
-                                          int blk_col, int ag, int KT, int valid, int d,
-                                          float sl2) {
-  constexpr int DT = 2 * DC;
-  const int lane = threadIdx.x & 63, g = lane >> 4;
-  // K fragments: token row blk_col + 16tt + lane%16, channel chunk DC*g + c
-  // (chunks at or past d are never staged: zero them here)
-  bf16x8 kf[2][DC];
-#pragma unroll
-  for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-    for (int c = 0; c < DC; ++c) {
-      const int ch0 = 8 * (DC * g + c);
-      const bf16x8 x = *reinterpret_cast<const bf16x8*>(
-          Ks + (blk_col + 16 * tt + (lane & 15)) * ks_stride + ch0);
-      kf[tt][c] = ch0 < d ? x : zero_bf16x8();
-    }
-  f32x4 S[2][4];
-#pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const int t = 4 * ag + a;
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) S[tt][a] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (t < KT) {
-#pragma unroll
-      for (int c = 0; c < DC; ++c) {
-        const bf16x8 af = Af[(t * DC + c) * 64 + lane];
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-          S[tt][a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[tt][c], af, S[tt][a], 0, 0, 0);
-      }
-    }
-  }
-#pragma unroll
-  for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (16 * tt + 4 * g + i >= valid)
-#pragma unroll
-        for (int a = 0; a < 4; ++a) S[tt][a][i] = -INFINITY;
-  bf16x8 vf[DT];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
-    const bf16_t* row = Vt + (16 * dt + (lane & 15)) * vt_stride + blk_col + 4 * g;
-    const uint2 lo = *reinterpret_cast<const uint2*>(row);
-    const uint2 hi = *reinterpret_cast<const uint2*>(row + 16);
-    vf[dt] = __builtin_bit_cast(bf16x8, uint4{lo.x, lo.y, hi.x, hi.y});
-  }
-#pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    if (4 * ag + a >= KT) continue;
-    float bm = fmaxf(fmaxf(fmaxf(S[0][a][0], S[0][a][1]), fmaxf(S[0][a][2], S[0][a][3])),
-                     fmaxf(fmaxf(S[1][a][0], S[1][a][1]), fmaxf(S[1][a][2], S[1][a][3])));
-    bm = group4_max(bm);
-    const float mn = fmaxf(st.m[a], bm);
-    const float corr = fast_exp2((st.m[a] - mn) * sl2);
-    const float off = mn * sl2;
-    union { bf16x8 v; __bf16 e[8]; } pf;
-    float ps = 0.f;
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float pv = fast_exp2(fmaf(S[tt][a][i], sl2, -off));
-        ps += pv;
-        pf.e[4 * tt + i] = (__bf16)pv;
-      }
-    st.l[a] = fmaf(st.l[a], corr, ps);
-    st.m[a] = mn;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      st.acc[a][dt] *= corr;
-      st.acc[a][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], pf.v, st.acc[a][dt], 0, 0, 0);
-    }
-  }
-}
-
+// ---------------------------------------------------------- K / V staging
 // 8-token x 8-channel tiles of K or V: tile `it` covers tokens
 // tok0 + 8*(it / DCH) .. +8 and channels 8*(it % DCH) .. +8.  Tokens at or
 // past tok_end load as zeros.
@@ -447,6 +354,83 @@ __device__ __forceinline__ void store_tile_rows(bf16_t* Ks, int ks_stride, const
     *reinterpret_cast<uint4*>(Ks + (8 * t8 + j) * ks_stride + 8 * ch) = x[j];
 }
 
+// ------------------------------------------------------------ aggregation
+// One wave: agent tiles [ATW*ag, ATW*ag + ATW) over its 32-token blocks.
+template <int DC, int ATW>
+struct AggState {
+  float m[ATW], l[ATW];
+  f32x4 acc[ATW][2 * DC];
+};
+
+template <class C, int DC, int ATW>
+__device__ __forceinline__ void agg_block(AggState<DC, ATW>& st, const bf16_t* Ks,
+                                          const bf16x8* Af, const bf16_t* Vt, int blk_col, int ag,
+                                          int valid, int d, float sl2) {
+  constexpr int DT = 2 * DC;
+  const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+  // K fragments: token row blk_col + 16tt + r, channel chunk DC*g + c
+  // (chunks at or past d are never staged: zero them)
+  bf16x8 kf[2][DC];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int c = 0; c < DC; ++c) {
+      const int ch0 = 8 * (DC * g + c);
+      const bf16x8 x = *reinterpret_cast<const bf16x8*>(Ks + (blk_col + 16 * tt + r) * C::KS_STRIDE + ch0);
+      kf[tt][c] = ch0 < d ? x : zero_bf16x8();
+    }
+  // V^T fragments: channel row 16dt + r, tokens {4g..4g+3, 16+4g..16+4g+3}
+  bf16x8 vf[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    const bf16_t* row = Vt + (16 * dt + r) * C::VT_STRIDE + blk_col + 4 * g;
+    const uint2 lo = *reinterpret_cast<const uint2*>(row);
+    const uint2 hi = *reinterpret_cast<const uint2*>(row + 16);
+    vf[dt] = __builtin_bit_cast(bf16x8, uint4{lo.x, lo.y, hi.x, hi.y});
+  }
+#pragma unroll
+  for (int a = 0; a < ATW; ++a) {
+    const int t = ATW * ag + a;
+    f32x4 S0 = f32x4{0.f, 0.f, 0.f, 0.f}, S1 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < DC; ++c) {
+      const bf16x8 af = Af[(t * DC + c) * 64 + lane];
+      S0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0][c], af, S0, 0, 0, 0);
+      S1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][c], af, S1, 0, 0, 0);
+    }
+    if (valid < 32) {   // rows 16tt + 4g + i past the slice end
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (4 * g + i >= valid) S0[i] = -INFINITY;
+        if (16 + 4 * g + i >= valid) S1[i] = -INFINITY;
+      }
+    }
+    float bm = fmaxf(fmaxf(fmaxf(S0[0], S0[1]), fmaxf(S0[2], S0[3])),
+                     fmaxf(fmaxf(S1[0], S1[1]), fmaxf(S1[2], S1[3])));
+    bm = group4_max(bm);
+    const float mn = fmaxf(st.m[a], bm);
+    const float corr = fast_exp2((st.m[a] - mn) * sl2);
+    const float off = mn * sl2;
+    float pv[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pv[i] = fast_exp2(fmaf(S0[i], sl2, -off));
+      pv[4 + i] = fast_exp2(fmaf(S1[i], sl2, -off));
+    }
+    st.l[a] = fmaf(st.l[a], corr,
+                   ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7])));
+    st.m[a] = mn;
+    union { bf16x8 v; unsigned w[4]; } pf;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pf.w[e] = pack_bf16(pv[2 * e], pv[2 * e + 1]);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      st.acc[a][dt] *= corr;
+      st.acc[a][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], pf.v, st.acc[a][dt], 0, 0, 0);
+    }
+  }
+}
+
 // ------------------------------------------------------------ broadcast
 template <int DC>
 __device__ __forceinline__ void load_q_tile(bf16x8 (&qf)[DC], rsrc_t rq, int tok0, int tok_end,
@@ -461,68 +445,57 @@ __device__ __forceinline__ void load_q_tile(bf16x8 (&qf)[DC], rsrc_t rq, int tok
   }
 }
 
-// VAf: [vparts][KC][DT][64] fragments (hi part, then lo part va_stride apart).
-template <int DC>
+// One 16-query tile: S^T = A Q^T over all agents at once, softmax over the
+// agents (lane group reductions), O^T = V_A^T P^T.  VAf: [VSPLIT][KC][DT][64].
+template <class C, int DC, int KTC>
 __device__ __forceinline__ void bcast_tile(const bf16x8 (&qf)[DC], const bf16x8* Af,
-                                           const bf16x8* VAf, int va_stride, int vparts,
-                                           rsrc_t ro, int tok0, int tok_end, int d, int nag,
-                                           float sl2) {
+                                           const bf16x8* VAf, rsrc_t ro, int tok0, int tok_end,
+                                           int d, int nag, float sl2) {
   constexpr int DT = 2 * DC;
+  constexpr int VA_PART = C::KC * DT * 64;
   const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
-  const int KT = (nag + 15) / 16;
-  const int nch = (KT + 3) / 4;
+  f32x4 S[KTC];
+#pragma unroll
+  for (int t = 0; t < KTC; ++t) {
+    S[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < DC; ++c)
+      S[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Af[(t * DC + c) * 64 + lane], qf[c], S[t],
+                                                     0, 0, 0);
+  }
+#pragma unroll
+  for (int t = 0; t < KTC; ++t)
+    if (16 * t + 16 > nag)   // padding agents of this tile
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (16 * t + 4 * g + i >= nag) S[t][i] = -INFINITY;
+  float M = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < KTC; ++t) M = fmaxf(M, fmaxf(fmaxf(S[t][0], S[t][1]), fmaxf(S[t][2], S[t][3])));
+  M = group4_max(M);
+  const float off = M * sl2;
   f32x4 O[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) O[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float M = -INFINITY, L = 0.f;
-  for (int ch = 0; ch < nch; ++ch) {
-    f32x4 S[4];
+  float L = 0.f;
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const int t = 4 * ch + a;
-      S[a] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (t < KT) {
+  for (int j = 0; j < C::KC; ++j) {
+    float pv[8];
 #pragma unroll
-        for (int c = 0; c < DC; ++c)
-          S[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Af[(t * DC + c) * 64 + lane], qf[c], S[a],
-                                                         0, 0, 0);
-      }
+    for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (16 * t + 4 * g + i >= nag) S[a][i] = -INFINITY;
-    }
-    float cm = -INFINITY;
+        pv[4 * h2 + i] = fast_exp2(fmaf(S[2 * j + h2][i], sl2, -off));
+    L += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
+    union { bf16x8 v; unsigned w[4]; } pf;
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
-      cm = fmaxf(cm, fmaxf(fmaxf(S[a][0], S[a][1]), fmaxf(S[a][2], S[a][3])));
-    cm = group4_max(cm);
-    const float mn = fmaxf(M, cm);
-    const float corr = fast_exp2((M - mn) * sl2);
-    const float off = mn * sl2;
-    M = mn;
-    L *= corr;
+    for (int e = 0; e < 4; ++e) pf.w[e] = pack_bf16(pv[2 * e], pv[2 * e + 1]);
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) O[dt] *= corr;
-#pragma unroll
-    for (int j2 = 0; j2 < 2; ++j2) {
-      const int jj = 2 * ch + j2;
-      if (32 * jj >= nag) break;
-      union { bf16x8 v; __bf16 e[8]; } pf;
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float pv = fast_exp2(fmaf(S[2 * j2 + h2][i], sl2, -off));
-          L += pv;
-          pf.e[4 * h2 + i] = (__bf16)pv;
-        }
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int f = (jj * DT + dt) * 64 + lane;
-        O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(VAf[f], pf.v, O[dt], 0, 0, 0);
-        if (vparts > 1)
-          O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(VAf[va_stride + f], pf.v, O[dt], 0, 0, 0);
-      }
+    for (int dt = 0; dt < DT; ++dt) {
+      const int f = (j * DT + dt) * 64 + lane;
+      O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(VAf[f], pf.v, O[dt], 0, 0, 0);
+      if (C::VSPLIT > 1)
+        O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(VAf[VA_PART + f], pf.v, O[dt], 0, 0, 0);
     }
   }
   L = group4_sum(L);
@@ -531,28 +504,30 @@ __device__ __forceinline__ void bcast_tile(const bf16x8 (&qf)[DC], const bf16x8*
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
     const int ch = 16 * dt + 4 * g;
-    const unsigned off = (tok < tok_end && ch < d) ? (unsigned)((tok * d + ch) * 2) : kOOB;
-    bst8<kPlain>(ro, off, uint2{pack_bf16(O[dt][0] * inv, O[dt][1] * inv),
-                                pack_bf16(O[dt][2] * inv, O[dt][3] * inv)});
+    const unsigned off2 = (tok < tok_end && ch < d) ? (unsigned)((tok * d + ch) * 2) : kOOB;
+    bst8<kPlain>(ro, off2, uint2{pack_bf16(O[dt][0] * inv, O[dt][1] * inv),
+                                 pack_bf16(O[dt][2] * inv, O[dt][3] * inv)});
   }
 }
 
 // ------------------------------------------------------------- the kernel
-template <int DC, int MINB>
-__global__ void __launch_bounds__(kThreads, MINB)
+template <int DC, int KTC>
+__global__ void __launch_bounds__(kThreads)
 agent_mfma_kernel(MfmaParams p) {
-  constexpr int DT = 2 * DC;
-  constexpr int DPAD = 32 * DC;
-  constexpr int RT = LdsPlan<DC>::RT;
-  constexpr int QPF = DC <= 2 ? 4 : 2;        // query tiles loaded ahead per wave
+  using C = Cfg<DC, KTC>;
+  constexpr int DT = C::DT;
+  constexpr int DPAD = C::DPAD;
+  constexpr int RT = C::RT;
+  constexpr int ATW = C::ATW;
+  constexpr int A_FRAGS = KTC * DC * 64;          // bf16x8 fragments
+  constexpr int VA_FRAGS = C::KC * DT * 64;       // per hi / lo part
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  const LdsPlan<DC> L(p.nag);
   bf16x8* Af = reinterpret_cast<bf16x8*>(smem);
-  unsigned char* big = smem + L.a_bytes;
+  unsigned char* big = smem + C::A_BYTES;
   bf16_t* Vt = reinterpret_cast<bf16_t*>(big);
-  bf16_t* Ks = reinterpret_cast<bf16_t*>(big + L.vt_bytes);
-  const int a_frags = L.KT * DC * 64;         // bf16x8 fragments
-  const int va_frags = L.KC * DT * 64;        // per hi / lo part
+  bf16_t* Ks = reinterpret_cast<bf16_t*>(big + C::VT_BYTES);
+  float* stage = reinterpret_cast<float*>(big);   // V_A rows [KTC*16][DPAD] (single mode)
+  bf16x8* VAf = reinterpret_cast<bf16x8*>(big + (C::STAGE_LDS ? C::STAGE_BYTES : 0));
 
   // workgroup -> (head, slot)
   int head, slot;
@@ -566,7 +541,8 @@ agent_mfma_kernel(MfmaParams p) {
   }
   if (head >= p.BH) return;
   AA_STAMP(0);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
   const int d = p.d, DCH = d >> 3;
   const int n0 = slot * p.T;
   const int n1 = min(p.N, n0 + p.T);
@@ -588,51 +564,45 @@ agent_mfma_kernel(MfmaParams p) {
   const int pool_chunk = p.pool_tgp * kPoolTok;       // window tokens per item pass
   const int pool_npass = (p.pool_maxcnt + pool_chunk - 1) / pool_chunk;
   uint4 px[kPoolTok];
-  if (p.phases & PH_POOL) pool_issue(p, rq, slot, threadIdx.x, pool_items, 0, px);
+  if (p.phases & PH_POOL) pool_issue(p, rq, slot, tid, pool_items, 0, px);
 
-  // ---- then K and V of the first round (8x8 tiles, one per thread)
-  const int ag = wave % L.AG, tg = wave / L.AG;
+  // ---- then K and V of the first round (one 8x8 tile per thread)
+  const int ag = wave % C::AG, tg = wave / C::AG;
   const int r0cnt = n1 > n0 ? min(RT, n1 - n0) : 0;
-  const int r0pad = (r0cnt + 31) / 32 * 32;
-  const int r0tiles = (r0pad / 8) * DCH;
+  const int r0tiles = ((r0cnt + 31) / 32 * 4) * DCH;
   uint4 kx[8], vx[8];
   if (p.phases & PH_AGG) {
-    const int it = threadIdx.x;
-    const int tend = it < r0tiles ? min(n1, n0 + r0cnt) : -1;
-    load_tile8(kx, rk, it, n0, tend, d);
-    load_tile8(vx, rv, it, n0, tend, d);
+    const int tend = tid < r0tiles ? n0 + r0cnt : -1;
+    load_tile8(kx, rk, tid, n0, tend, d);
+    load_tile8(vx, rv, tid, n0, tend, d);
   }
-  // query tiles of this wave, loaded ahead of the broadcast (registers)
+  // first query tile of this wave, loaded ahead of the broadcast
   const int nqt = n1 > n0 ? (n1 - n0 + 15) / 16 : 0;
-  bf16x8 qf[QPF][DC];
-  auto issue_q = [&]() {
-#pragma unroll
-    for (int u = 0; u < QPF; ++u) load_q_tile<DC>(qf[u], rq, n0 + 16 * (wave + kWaves * u), n1, d);
-  };
-  if ((p.phases & PH_BCAST) && !(p.phases & PH_AGG)) issue_q();
+  bf16x8 qcur[DC];
+  if ((p.phases & PH_BCAST) && !(p.phases & PH_AGG)) load_q_tile<DC>(qcur, rq, n0 + 16 * wave, n1, d);
   AA_STAMP(1);
 
   // ---- POOL
   if (p.phases & PH_POOL) {
     float* red = reinterpret_cast<float*>(big);
     if (single) {
-      for (int f = threadIdx.x; f < a_frags; f += kThreads) Af[f] = zero_bf16x8();
+      for (int f = tid; f < A_FRAGS; f += kThreads) Af[f] = zero_bf16x8();
     }
     const int TGP = p.pool_tgp;
     const float rdch = rcp_approx(DCH);
     for (int b0 = 0; b0 < pool_items; b0 += kThreads) {
       float acc8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
       for (int ps = 0; ps < pool_npass; ++ps) {
-        if (b0 > 0 || ps > 0) pool_issue(p, rq, slot, b0 + threadIdx.x, pool_items, ps * pool_chunk, px);
+        if (b0 > 0 || ps > 0) pool_issue(p, rq, slot, b0 + tid, pool_items, ps * pool_chunk, px);
         pool_accum(px, acc8);
       }
       __syncthreads();   // red free
-      *reinterpret_cast<float4*>(red + threadIdx.x * 8) = float4{acc8[0], acc8[1], acc8[2], acc8[3]};
-      *reinterpret_cast<float4*>(red + threadIdx.x * 8 + 4) = float4{acc8[4], acc8[5], acc8[6], acc8[7]};
+      *reinterpret_cast<float4*>(red + tid * 8) = float4{acc8[0], acc8[1], acc8[2], acc8[3]};
+      *reinterpret_cast<float4*>(red + tid * 8 + 4) = float4{acc8[4], acc8[5], acc8[6], acc8[7]};
       __syncthreads();
       // pairs (m, c) of this batch (TGP divides kThreads)
       const int pr0 = b0 >> p.pool_tgp_log2, npr = min(kThreads, pool_items - b0) >> p.pool_tgp_log2;
-      for (int o = threadIdx.x; o < npr; o += kThreads) {
+      for (int o = tid; o < npr; o += kThreads) {
         const int pr = pr0 + o;
         const int m = idiv(pr, DCH, rdch), c = pr - m * DCH;
         const int a = slot + p.P * m;
@@ -674,37 +644,27 @@ agent_mfma_kernel(MfmaParams p) {
     const float* rows = p.agents_f32_in ? p.agents_f32_in : p.agents_f32;
     const rsrc_t ra = from_rows ? rsrc_of(rows + ahb, arow_bytes)
                                 : rsrc_of(p.agents_in + ahb, (unsigned)(p.nag * d * 2));
-    for (int f0 = 0; f0 < a_frags; f0 += 2 * kThreads) {
-      uint4 x[2][2];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int f = f0 + threadIdx.x + kThreads * u;
-        const int fl = f & 63, c = (f >> 6) % DC, t = (f >> 6) / DC;
-        const int agent = 16 * t + (fl & 15), ch0 = 8 * (DC * (fl >> 4) + c);
-        const bool in = f < a_frags && agent < p.nag && ch0 < d;
-        if (from_rows) {
-          const unsigned off = in ? (unsigned)((agent * d + ch0) * 4) : kOOB;
-          if (sync_group) { x[u][0] = bld16<kCoherent>(ra, off); x[u][1] = bld16<kCoherent>(ra, off + 16); }
-          else { x[u][0] = bld16<kPlain>(ra, off); x[u][1] = bld16<kPlain>(ra, off + 16); }
-        } else {
-          x[u][0] = bld16<kPlain>(ra, in ? (unsigned)((agent * d + ch0) * 2) : kOOB);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int f = f0 + threadIdx.x + kThreads * u;
-        if (f >= a_frags) continue;
-        if (from_rows) {
-          const float4 a0 = bits_f4(x[u][0]), a1 = bits_f4(x[u][1]);
-          union { bf16x8 v; unsigned w[4]; } fr;
-          fr.w[0] = pack_bf16(a0.x, a0.y);
-          fr.w[1] = pack_bf16(a0.z, a0.w);
-          fr.w[2] = pack_bf16(a1.x, a1.y);
-          fr.w[3] = pack_bf16(a1.z, a1.w);
-          Af[f] = fr.v;
-        } else {
-          Af[f] = __builtin_bit_cast(bf16x8, x[u][0]);
-        }
+    for (int f0 = 0; f0 < A_FRAGS; f0 += kThreads) {
+      const int f = f0 + tid;
+      const int fl = f & 63, c = (f >> 6) % DC, t = (f >> 6) / DC;
+      const int agent = 16 * t + (fl & 15), ch0 = 8 * (DC * (fl >> 4) + c);
+      const bool in = f < A_FRAGS && agent < p.nag && ch0 < d;
+      if (from_rows) {
+        const unsigned off = in ? (unsigned)((agent * d + ch0) * 4) : kOOB;
+        uint4 x0, x1;
+        if (sync_group) { x0 = bld16<kCoherent>(ra, off); x1 = bld16<kCoherent>(ra, off + 16); }
+        else { x0 = bld16<kPlain>(ra, off); x1 = bld16<kPlain>(ra, off + 16); }
+        const float4 a0 = bits_f4(x0), a1 = bits_f4(x1);
+        union { bf16x8 v; unsigned w[4]; } fr;
+        fr.w[0] = pack_bf16(a0.x, a0.y);
+        fr.w[1] = pack_bf16(a0.z, a0.w);
+        fr.w[2] = pack_bf16(a1.x, a1.y);
+        fr.w[3] = pack_bf16(a1.z, a1.w);
+        if (f < A_FRAGS) Af[f] = fr.v;
+      } else {
+        const uint4 x = bld16<kPlain>(ra, in ? (unsigned)((agent * d + ch0) * 2) : kOOB);
+        if (f < A_FRAGS) Af[f] = __builtin_bit_cast(bf16x8, x);
       }
     }
   }
@@ -712,12 +672,10 @@ agent_mfma_kernel(MfmaParams p) {
   AA_STAMP(4);
 
   // ---- AGGREGATE
-  bf16x8* VAf = reinterpret_cast<bf16x8*>(big + (L.stage_lds ? L.stage_bytes : 0));
-  float* stage = reinterpret_cast<float*>(big);   // V_A rows [KT*16][DPAD] (single mode)
   if (p.phases & PH_AGG) {
-    AggState<DC> st;
+    AggState<DC, ATW> st;
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
+    for (int a = 0; a < ATW; ++a) {
       st.m[a] = -INFINITY;
       st.l[a] = 0.f;
 #pragma unroll
@@ -725,88 +683,81 @@ agent_mfma_kernel(MfmaParams p) {
     }
     for (int rt0 = n0; rt0 < n1; rt0 += RT) {
       const int rcnt = min(RT, n1 - rt0);
-      const int rpad = (rcnt + 31) / 32 * 32;
-      const int ntile = (rpad / 8) * DCH;
+      const int rblk = (rcnt + 31) / 32;
+      const int ntile = rblk * 4 * DCH;
       __syncthreads();   // previous round (or the pooling sums) fully read
-      if (rt0 == n0) {
-        if (threadIdx.x < ntile) {
-          store_tile_rows(Ks, L.ks_stride, kx, threadIdx.x, d);
-          store_tile_t(Vt, L.vt_stride, vx, threadIdx.x, d);
-        }
-      } else {
-        for (int it0 = 0; it0 < ntile; it0 += kThreads) {
-          const int it = it0 + threadIdx.x;
-          const int tend = it < ntile ? n1 : -1;
-          load_tile8(kx, rk, it, rt0, tend, d);
-          load_tile8(vx, rv, it, rt0, tend, d);
-          if (it < ntile) {
-            store_tile_rows(Ks, L.ks_stride, kx, it, d);
-            store_tile_t(Vt, L.vt_stride, vx, it, d);
-          }
-        }
+      if (rt0 != n0) {
+        const int tend = tid < ntile ? rt0 + rcnt : -1;
+        load_tile8(kx, rk, tid, rt0, tend, d);
+        load_tile8(vx, rv, tid, rt0, tend, d);
+      }
+      if (tid < ntile) {
+        store_tile_rows(Ks, C::KS_STRIDE, kx, tid, d);
+        store_tile_t(Vt, C::VT_STRIDE, vx, tid, d);
       }
       __syncthreads();
-      const int rblk = rpad / 32;
-      for (int b = tg; b < rblk; b += L.TG)
-        agg_block<DC>(st, Ks, L.ks_stride, Af, Vt, L.vt_stride, 32 * b, ag, L.KT,
-                      min(32, n1 - (rt0 + 32 * b)), d, p.sl2);
+      AA_STAMP(12);
+      for (int b = tg; b < rblk; b += C::TG)
+        agg_block<C, DC, ATW>(st, Ks, Af, Vt, 32 * b, ag, min(32, n1 - (rt0 + 32 * b)), d, p.sl2);
     }
     AA_STAMP(5);
-    if (single && (p.phases & PH_BCAST)) issue_q();   // in flight during the combine
+    if (single && (p.phases & PH_BCAST)) load_q_tile<DC>(qcur, rq, n0 + 16 * wave, n1, d);
 #pragma unroll
-    for (int a = 0; a < 4; ++a) st.l[a] = group4_sum(st.l[a]);
+    for (int a = 0; a < ATW; ++a) st.l[a] = group4_sum(st.l[a]);
 
     // combine the TG token groups of each agent group through LDS:
     // records [rec][a][DT acc | 1 (m, l)][64 lanes] x 16 B
-    float4* comb = reinterpret_cast<float4*>(big);
-    constexpr int RQ = DT + 1;
-    __syncthreads();
-    if (tg > 0) {
-      float4* dst = comb + ((tg - 1) * L.AG + ag) * 4 * RQ * 64;
+    if (C::TG > 1) {
+      float4* comb = reinterpret_cast<float4*>(big);
+      constexpr int RQ = DT + 1;
+      __syncthreads();
+      if (tg > 0) {
+        float4* dst = comb + ((tg - 1) * C::AG + ag) * ATW * RQ * 64;
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
+        for (int a = 0; a < ATW; ++a) {
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-          dst[(a * RQ + dt) * 64 + lane] =
-              float4{st.acc[a][dt][0], st.acc[a][dt][1], st.acc[a][dt][2], st.acc[a][dt][3]};
-        dst[(a * RQ + DT) * 64 + lane] = float4{st.m[a], st.l[a], 0.f, 0.f};
+          for (int dt = 0; dt < DT; ++dt)
+            dst[(a * RQ + dt) * 64 + lane] =
+                float4{st.acc[a][dt][0], st.acc[a][dt][1], st.acc[a][dt][2], st.acc[a][dt][3]};
+          dst[(a * RQ + DT) * 64 + lane] = float4{st.m[a], st.l[a], 0.f, 0.f};
+        }
       }
-    }
-    __syncthreads();
-    if (tg == 0) {
-      for (int o = 1; o < L.TG; ++o) {
-        const float4* src = comb + ((o - 1) * L.AG + ag) * 4 * RQ * 64;
+      __syncthreads();
+      if (tg == 0) {
+        for (int o = 1; o < C::TG; ++o) {
+          const float4* src = comb + ((o - 1) * C::AG + ag) * ATW * RQ * 64;
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const float4 ml = src[(a * RQ + DT) * 64 + lane];
-          const float mn = fmaxf(st.m[a], ml.x);
-          const float c1 = (mn == -INFINITY) ? 0.f : fast_exp2((st.m[a] - mn) * p.sl2);
-          const float c2 = (mn == -INFINITY) ? 0.f : fast_exp2((ml.x - mn) * p.sl2);
-          st.l[a] = st.l[a] * c1 + ml.y * c2;
-          st.m[a] = mn;
+          for (int a = 0; a < ATW; ++a) {
+            const float4 ml = src[(a * RQ + DT) * 64 + lane];
+            const float mn = fmaxf(st.m[a], ml.x);
+            const float c1 = (mn == -INFINITY) ? 0.f : fast_exp2((st.m[a] - mn) * p.sl2);
+            const float c2 = (mn == -INFINITY) ? 0.f : fast_exp2((ml.x - mn) * p.sl2);
+            st.l[a] = st.l[a] * c1 + ml.y * c2;
+            st.m[a] = mn;
 #pragma unroll
-          for (int dt = 0; dt < DT; ++dt) {
-            const float4 r = src[(a * RQ + dt) * 64 + lane];
-            st.acc[a][dt][0] = st.acc[a][dt][0] * c1 + r.x * c2;
-            st.acc[a][dt][1] = st.acc[a][dt][1] * c1 + r.y * c2;
-            st.acc[a][dt][2] = st.acc[a][dt][2] * c1 + r.z * c2;
-            st.acc[a][dt][3] = st.acc[a][dt][3] * c1 + r.w * c2;
+            for (int dt = 0; dt < DT; ++dt) {
+              const float4 rr = src[(a * RQ + dt) * 64 + lane];
+              st.acc[a][dt][0] = st.acc[a][dt][0] * c1 + rr.x * c2;
+              st.acc[a][dt][1] = st.acc[a][dt][1] * c1 + rr.y * c2;
+              st.acc[a][dt][2] = st.acc[a][dt][2] * c1 + rr.z * c2;
+              st.acc[a][dt][3] = st.acc[a][dt][3] * c1 + rr.w * c2;
+            }
           }
         }
       }
     }
-    // wave (ag, 0) now holds the workgroup's partial for agent tiles 4ag..4ag+3
+    // wave (ag, 0) now holds the workgroup's partial for its agent tiles
     const int g = lane >> 4;
     if (p.P == 1) {
       // V_A rows: staging (LDS or the fp32 scratch) in single mode, the fp32
       // output otherwise
+      const bool lds_rows = single && C::STAGE_LDS;
       __syncthreads();   // comb fully read (it aliases the staging rows)
       if (tg == 0) {
-        const bool lds_rows = single && L.stage_lds;
         const rsrc_t rvo = rsrc_of(p.values_f32 + ahb, arow_bytes);
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const int agent = 16 * (4 * ag + a) + (lane & 15);
+        for (int a = 0; a < ATW; ++a) {
+          const int agent = 16 * (ATW * ag + a) + (lane & 15);
           const float inv = 1.0f / st.l[a];
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) {
@@ -814,7 +765,7 @@ agent_mfma_kernel(MfmaParams p) {
             const float4 x = float4{st.acc[a][dt][0] * inv, st.acc[a][dt][1] * inv,
                                     st.acc[a][dt][2] * inv, st.acc[a][dt][3] * inv};
             if (lds_rows) {
-              if (4 * ag + a < L.KT) *reinterpret_cast<float4*>(stage + agent * DPAD + ch) = x;
+              *reinterpret_cast<float4*>(stage + agent * DPAD + ch) = x;
             } else {
               const unsigned off = (agent < p.nag && ch < d) ? (unsigned)((agent * d + ch) * 4) : kOOB;
               bst16<kPlain>(rvo, off, f4_bits(x));
@@ -824,13 +775,12 @@ agent_mfma_kernel(MfmaParams p) {
       }
     } else if (tg == 0) {
       // partials in register order: one contiguous 1 KiB row per (tile, dt)
-      const long pbase = ((long)head * p.P + slot) * L.KT;
-      const rsrc_t racc = rsrc_of(p.part_acc + pbase * DT * 256, (unsigned)(L.KT * DT * 1024));
-      const rsrc_t rml = rsrc_of(p.part_ml + pbase * 32, (unsigned)(L.KT * 128));
+      const long pbase = ((long)head * p.P + slot) * KTC;
+      const rsrc_t racc = rsrc_of(p.part_acc + pbase * DT * 256, (unsigned)(KTC * DT * 1024));
+      const rsrc_t rml = rsrc_of(p.part_ml + pbase * 32, (unsigned)(KTC * 128));
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int t = 4 * ag + a;
-        if (t >= L.KT) continue;
+      for (int a = 0; a < ATW; ++a) {
+        const int t = ATW * ag + a;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
           const unsigned off = (unsigned)(((t * DT + dt) * 64 + lane) * 16);
@@ -846,8 +796,14 @@ agent_mfma_kernel(MfmaParams p) {
       }
     }
     AA_STAMP(6);
-    if (sync_group && (p.phases & PH_BCAST)) issue_q();   // in flight during the merge
-    if (sync_group && ok) ok = group_barrier(ctr + 1 * kSyncStride, p.P, p.status);
+    if (sync_group && ok) {
+      group_arrive(ctr + 1 * kSyncStride);
+      // the query tile loads travel while the group gathers
+      if (p.phases & PH_BCAST) load_q_tile<DC>(qcur, rq, n0 + 16 * wave, n1, d);
+      ok = group_wait(ctr + 1 * kSyncStride, p.P, p.status);
+    } else if (sync_group && (p.phases & PH_BCAST)) {
+      load_q_tile<DC>(qcur, rq, n0 + 16 * wave, n1, d);
+    }
     AA_STAMP(7);
   }
 
@@ -855,24 +811,24 @@ agent_mfma_kernel(MfmaParams p) {
   if ((p.phases & PH_MERGE) && p.P > 1 && ok) {
     constexpr int nq = DPAD / 4;
     const int items = pool_na * nq;   // agents slot, slot+P, ... (pool_na of them)
-    const long hbase = (long)head * p.P * L.KT;
-    const rsrc_t racc = rsrc_of(p.part_acc + hbase * DT * 256, (unsigned)(p.P * L.KT * DT * 1024));
-    const rsrc_t rml = rsrc_of(p.part_ml + hbase * 32, (unsigned)(p.P * L.KT * 128));
+    const long hbase = (long)head * p.P * KTC;
+    const rsrc_t racc = rsrc_of(p.part_acc + hbase * DT * 256, (unsigned)(p.P * KTC * DT * 1024));
+    const rsrc_t rml = rsrc_of(p.part_ml + hbase * 32, (unsigned)(p.P * KTC * 128));
     const rsrc_t rvo = rsrc_of(p.values_f32 + ahb, arow_bytes);
-    for (int it = threadIdx.x; it < items; it += kThreads) {
+    for (int it = tid; it < items; it += kThreads) {
       const int m = it / nq, q = it - m * nq;
       const int a = slot + p.P * m;
       const int t = a >> 4, r = a & 15, dt = q >> 2, g = q & 3;
       const unsigned aoff = (unsigned)(((t * DT + dt) * 64 + 16 * g + r) * 16);
       const unsigned moff = (unsigned)((t * 16 + r) * 8);
-      const unsigned sstride_acc = (unsigned)(L.KT * DT * 1024), sstride_ml = (unsigned)(L.KT * 128);
+      constexpr unsigned sstride_acc = KTC * DT * 1024, sstride_ml = KTC * 128;
       float M = -INFINITY, Ls = 0.f;
       float4 acc = float4{0.f, 0.f, 0.f, 0.f};
-      for (int s0 = 0; s0 < p.P; s0 += 8) {
-        uint4 xa[8];
-        u32x2 xm[8];
+      for (int s0 = 0; s0 < p.P; s0 += 16) {
+        uint4 xa[16];
+        u32x2 xm[16];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < 16; ++u) {
           const bool in = s0 + u < p.P;
           const unsigned so = (unsigned)(s0 + u);
           if (sync_group) {
@@ -885,13 +841,13 @@ agent_mfma_kernel(MfmaParams p) {
         }
         float cm = M;
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
+        for (int u = 0; u < 16; ++u)
           if (s0 + u < p.P) cm = fmaxf(cm, __uint_as_float(xm[u][0]));
         const float corr = (cm == -INFINITY) ? 0.f : fast_exp2((M - cm) * p.sl2);
         Ls *= corr;
         acc.x *= corr; acc.y *= corr; acc.z *= corr; acc.w *= corr;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < 16; ++u) {
           if (s0 + u >= p.P) continue;
           const float mu = __uint_as_float(xm[u][0]);
           const float wgt = (mu == -INFINITY) ? 0.f : fast_exp2((mu - cm) * p.sl2);
@@ -920,19 +876,20 @@ agent_mfma_kernel(MfmaParams p) {
   if ((p.phases & PH_BCAST) && ok) {
     // V_A fragments from rows: LDS staging (single mode), the exchanged rows
     // (groups) or the fp32 input (step call); padding positions are zero
-    const bool lds_rows = single && L.stage_lds && (p.phases & PH_AGG);
+    const bool lds_rows = single && C::STAGE_LDS && (p.phases & PH_AGG);
     const float* rows = p.values_f32_in ? p.values_f32_in : p.values_f32;
     const rsrc_t rvr = rsrc_of(rows + ahb, arow_bytes);
     __syncthreads();
-    for (int f0 = 0; f0 < va_frags; f0 += kThreads) {
-      const int f = f0 + threadIdx.x;
+#pragma unroll
+    for (int f0 = 0; f0 < VA_FRAGS; f0 += kThreads) {
+      const int f = f0 + tid;
       const int fl = f & 63, dt = (f >> 6) % DT, j = (f >> 6) / DT;
       const int ch = 16 * dt + (fl & 15), g = fl >> 4;
       float x[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int agent = pair_index(j, g, e);
-        const bool in = f < va_frags && agent < p.nag && ch < d;
+        const bool in = f < VA_FRAGS && agent < p.nag && ch < d;
         if (lds_rows) {
           x[e] = in ? stage[agent * DPAD + ch] : 0.f;
         } else {
@@ -940,33 +897,26 @@ agent_mfma_kernel(MfmaParams p) {
           x[e] = sync_group ? bld4<kCoherent>(rvr, off) : bld4<kPlain>(rvr, off);
         }
       }
-      if (f < va_frags) {
-        union { bf16x8 v; bf16_t e[8]; } hi, lo;
+      union { bf16x8 v; bf16_t e[8]; } hi, lo;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          hi.e[e] = bf16_bits(x[e]);
-          lo.e[e] = bf16_bits(x[e] - bf16_value(hi.e[e]));
-        }
+      for (int e = 0; e < 8; ++e) {
+        hi.e[e] = bf16_bits(x[e]);
+        lo.e[e] = bf16_bits(x[e] - bf16_value(hi.e[e]));
+      }
+      if (f < VA_FRAGS) {
         VAf[f] = hi.v;
-        if (L.vparts > 1) VAf[va_frags + f] = lo.v;
+        if (C::VSPLIT > 1) VAf[VA_FRAGS + f] = lo.v;
       }
     }
     __syncthreads();
     AA_STAMP(10);
     const rsrc_t ro = rsrc_of(p.out + hoff, head_bytes);
-    int u = 0;
-    for (int qt = wave; qt < nqt; qt += kWaves, ++u) {
-      bf16x8 qcur[DC];
-      bool pre = false;
+    for (int qt = wave; qt < nqt; qt += kWaves) {
+      bf16x8 qnext[DC];
+      load_q_tile<DC>(qnext, rq, n0 + 16 * (qt + kWaves), n1, d);   // zeros past the end
+      bcast_tile<C, DC, KTC>(qcur, Af, VAf, ro, n0 + 16 * qt, n1, d, p.nag, p.sl2);
 #pragma unroll
-      for (int uu = 0; uu < QPF; ++uu)
-        if (uu == u) {
-          pre = true;
-#pragma unroll
-          for (int c = 0; c < DC; ++c) qcur[c] = qf[uu][c];
-        }
-      if (!pre) load_q_tile<DC>(qcur, rq, n0 + 16 * qt, n1, d);
-      bcast_tile<DC>(qcur, Af, VAf, va_frags, L.vparts, ro, n0 + 16 * qt, n1, d, p.nag, p.sl2);
+      for (int c = 0; c < DC; ++c) qcur[c] = qnext[c];
     }
   }
   AA_STAMP(11);
@@ -974,7 +924,7 @@ agent_mfma_kernel(MfmaParams p) {
   // ---- reset the group's counters once every workgroup of the group is done
   if (sync_group) {
     __syncthreads();
-    if (threadIdx.x == 0) {
+    if (tid == 0) {
       unsigned* done = ctr + kBarriers * kSyncStride;
       const unsigned old = __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (old == (unsigned)p.P - 1) {
@@ -985,5 +935,12 @@ agent_mfma_kernel(MfmaParams p) {
     }
   }
 }
+
+// Launch helper instantiated per DC in its own translation unit.
+template <int DC>
+int launch_mfma_dc(const MfmaParams& mp, int ktc, long grid, hipStream_t st);
+
+template <int DC, int KTC>
+int mfma_lds_bytes_t() { return Cfg<DC, KTC>::TOTAL; }
 
 }  // namespace aa
