@@ -33,6 +33,7 @@ _SIGNATURES = {
     "agent_attn_aggregate": (_c_int, [_vp] * 4 + [_c_int] * 5 + [_c_float, _c_int, _vp, _c_size,
                                                                  _vp]),
     "agent_attn_broadcast": (_c_int, [_vp] * 4 + [_c_int] * 5 + [_c_float, _c_int, _vp]),
+    "agent_attn_read_faults": (_c_int, [_vp, _vp, ctypes.POINTER(_c_int)]),
     "agent_attn_release": (None, []),
     "agent_attn_status_string": (ctypes.c_char_p, [_c_int]),
     "agent_attn_last_error": (ctypes.c_char_p, []),
@@ -266,6 +267,34 @@ def agent_attn_broadcast(q, agents_f32, agent_values_f32, scale, out=None):
                                     _stream(q.device))
     _check(rc)
     return out
+
+
+FAULT_BARRIER, FAULT_XCD = 1, 2
+
+
+def agent_attn_read_faults(workspace=None, device=None) -> int:
+    """Wait for torch's current stream, then read and clear the fault word
+    (AGENT_ATTN_FAULT_* bits; 0 = every forward since the last read ran
+    normally) of `workspace`; with no workspace, of both this module's
+    cached workspace for the current stream and the library's own scratch."""
+    L = lib()
+    if workspace is not None:
+        device = workspace.device
+    device = torch.device(device if device is not None else "cuda")
+    if device.index is None:
+        device = torch.device("cuda", torch.cuda.current_device())
+    if workspace is not None:
+        targets = [workspace]
+    else:
+        cached = _ws_cache.get((device.index, torch.cuda.current_stream(device).cuda_stream))
+        targets = ([cached] if cached is not None else []) + [None]
+    word = 0
+    with torch.cuda.device(device):
+        for t in targets:
+            f = _c_int(0)
+            _check(L.agent_attn_read_faults(_ptr(t), _stream(device), ctypes.byref(f)))
+            word |= f.value
+    return word
 
 
 def agent_attn_release() -> None:

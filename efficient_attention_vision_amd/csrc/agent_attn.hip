@@ -210,6 +210,43 @@ int device_cus() {
   return cache[dev];
 }
 
+// Records the XCD of every workgroup of a 1024-workgroup launch.
+__global__ void __launch_bounds__(512) xcd_probe_kernel(int* out) {
+  if (threadIdx.x == 0) out[blockIdx.x] = aa::xcc_id();
+}
+
+// Whether the current device runs workgroup b on XCD b % 8, checked once per
+// device with a probe launch.  Groups of workgroups placed on one XCD by that
+// rule exchange their data through the XCD's L2 instead of device-coherent
+// memory.  The probe synchronises, so it is not run while `st` is being
+// captured into a graph (the answer is then "no" for that call).
+bool xcd_round_robin(hipStream_t st) {
+  static std::mutex mu;
+  static std::vector<int> cache;   // -1 unknown, 0 no, 1 yes
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)cache.size() <= dev) cache.resize(dev + 1, -1);
+  if (cache[dev] >= 0) return cache[dev] == 1;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
+    return false;
+  constexpr int kProbe = 1024;
+  int* d_out = nullptr;
+  if (hipMalloc(&d_out, kProbe * sizeof(int)) != hipSuccess) return false;
+  std::vector<int> h(kProbe, -1);
+  bool ok = false;
+  hipLaunchKernelGGL(xcd_probe_kernel, dim3(kProbe), dim3(512), 0, nullptr, d_out);
+  if (hipGetLastError() == hipSuccess &&
+      hipMemcpy(h.data(), d_out, kProbe * sizeof(int), hipMemcpyDeviceToHost) == hipSuccess) {
+    ok = true;
+    for (int b = 0; b < kProbe; ++b) ok = ok && h[b] == b % 8;
+  }
+  (void)hipFree(d_out);
+  cache[dev] = ok ? 1 : 0;
+  return ok;
+}
+
 // Split of each head over P workgroups of T tokens (T a multiple of 16):
 // P = floor(CUs / BH), so that the P workgroups of every head fit on the
 // chip at once (one per compute unit) and can meet at group barriers.
@@ -392,7 +429,7 @@ int run_forward_mfma(const Dims& D, const Plan& P, const void* q, const void* k,
   mp.part_acc = (float*)(ws + P.off_part);
   mp.sync = (unsigned*)(ws + P.off_sync);
   mp.status = (int*)(ws + P.off_status);
-  mp.xcd_heads = P.xcd_heads;
+  mp.xcd_heads = (P.xcd_heads > 0 && xcd_round_robin(st)) ? P.xcd_heads : 0;
 #ifdef AGENT_ATTN_PHASE_TRACE
   mp.trace = g_trace;
 #endif
@@ -639,6 +676,31 @@ int agent_attn_broadcast(const void* q, const float* agents_f32, const float* ag
   mp.agents_f32_in = agents_f32;
   mp.values_f32_in = agent_values_f32;
   return run_mfma_phases(D, mp, mfma_dc(D.d), aa::PH_BCAST, false, st);
+}
+
+int agent_attn_read_faults(void* workspace, void* stream, int* faults) {
+  if (!faults) return fail(AGENT_ATTN_ERR_NULL, "faults must be non-NULL");
+  *faults = 0;
+  char* ws = (char*)workspace;
+  if (!ws) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    if ((int)g_ws.size() > dev) ws = (char*)g_ws[dev].first;
+  }
+  if (!ws) return AGENT_ATTN_OK;   // no fused launch has run on this device
+  hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  unsigned word = 0;
+  e = hipMemcpy(&word, ws + kSyncRegionBytes, sizeof(word), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpy of the fault word");
+  if (word) {
+    e = hipMemset(ws + kSyncRegionBytes, 0, sizeof(word));
+    if (e != hipSuccess) return hip_fail(e, "hipMemset of the fault word");
+  }
+  *faults = (int)word;
+  return AGENT_ATTN_OK;
 }
 
 void agent_attn_release(void) {

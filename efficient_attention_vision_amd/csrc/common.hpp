@@ -31,4 +31,14 @@ __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Index of the XCD (accelerator complex die) the calling wave runs on: the
+// XCC_ID hardware register (id 20), bits [3:0].
+__device__ __forceinline__ int xcc_id() {
+  return __builtin_amdgcn_s_getreg((20) | (0 << 6) | ((4 - 1) << 11));
+}
+
+// Bits of the fault word that the fused kernel leaves in its workspace.
+constexpr unsigned kFaultBarrier = 1u;   // a group barrier gave up waiting
+constexpr unsigned kFaultXcd = 2u;       // a workgroup ran off its planned XCD
+
 }  // namespace aa

@@ -72,7 +72,7 @@ struct MfmaParams {
   float* part_acc;              // partials [BH][P][KT][DT][64][4]
   float* part_ml;               // partial max and sum [BH][P][KT][16][2]
   unsigned* sync;               // group counters, zero between launches
-  int* status;                  // nonzero after a barrier timed out
+  int* status;                  // fault word (kFault* bits)
   int BH, N, h, w, d, s, nag;
   int P, T;                     // workgroups per head, tokens per workgroup
   int pool_tgp;                 // pooling token groups per (agent, chunk): power of 2
@@ -144,11 +144,19 @@ __device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {
   return (unsigned)bf16_bits(lo) | ((unsigned)bf16_bits(hi) << 16);
 }
 
-// Buffer accesses.  CPol: kPlain = default caching; kCoherent = sc1, the
-// device-coherent policy of agent-scope atomics (used for data that other
-// workgroups, possibly on another XCD, read after a group barrier).
+// Buffer accesses.  CPol: kPlain = default caching; kL2 = sc0, which skips
+// the CU's vector cache and is served by the XCD's L2 (coherent among the
+// workgroups of one XCD); kCoherent = sc1, the device-coherent policy of
+// agent-scope atomics (coherent across XCDs).
 constexpr int kPlain = 0;
+constexpr int kL2 = 1;
 constexpr int kCoherent = 16;
+constexpr int kStream = 2;   // nt: output written once and not read again here
+
+// Policy of data that other workgroups of the group read after a barrier:
+// 0 = no group (only this workgroup reads it), 1 = the group lives on one
+// XCD (exchange through that XCD's L2), 2 = the group spans XCDs.
+enum XPol { kXNone = 0, kXL2 = 1, kXDevice = 2 };
 
 __device__ __forceinline__ rsrc_t rsrc_of(const void* base, unsigned bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
@@ -174,6 +182,29 @@ __device__ __forceinline__ void bst8(rsrc_t r, unsigned off, uint2 x) {
 template <int POL>
 __device__ __forceinline__ void bst4(rsrc_t r, unsigned off, float x) {
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, (int)off, 0, POL);
+}
+// Runs f with the cache policy of exchange policy xp as a compile-time
+// constant, so that loops of loads are instantiated per policy rather than
+// branching around every load.
+template <int V>
+struct PolC {
+  static constexpr int value = V;
+};
+template <class F>
+__device__ __forceinline__ void with_pol(int xp, F&& f) {
+  if (xp == kXDevice) f(PolC<kCoherent>{});
+  else if (xp == kXL2) f(PolC<kL2>{});
+  else f(PolC<kPlain>{});
+}
+__device__ __forceinline__ void xst16(int xp, rsrc_t r, unsigned off, uint4 x) {
+  if (xp == kXDevice) bst16<kCoherent>(r, off, x);
+  else if (xp == kXL2) bst16<kL2>(r, off, x);
+  else bst16<kPlain>(r, off, x);
+}
+__device__ __forceinline__ void xst8(int xp, rsrc_t r, unsigned off, uint2 x) {
+  if (xp == kXDevice) bst8<kCoherent>(r, off, x);
+  else if (xp == kXL2) bst8<kL2>(r, off, x);
+  else bst8<kPlain>(r, off, x);
 }
 __device__ __forceinline__ uint4 f4_bits(float4 x) {
   return uint4{__float_as_uint(x.x), __float_as_uint(x.y), __float_as_uint(x.z),
@@ -203,8 +234,8 @@ __device__ __forceinline__ bool group_wait(unsigned* ctr, unsigned n, int* statu
     while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < n) {
       if (++spins > kSpinLimit) {
         ok = 0;
-        __hip_atomic_store(reinterpret_cast<unsigned*>(status), 1u, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_or(reinterpret_cast<unsigned*>(status), kFaultBarrier, __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
       __builtin_amdgcn_s_sleep(1);
@@ -505,7 +536,7 @@ __device__ __forceinline__ void bcast_tile(const bf16x8 (&qf)[DC], const bf16x8*
   for (int dt = 0; dt < DT; ++dt) {
     const int ch = 16 * dt + 4 * g;
     const unsigned off2 = (tok < tok_end && ch < d) ? (unsigned)((tok * d + ch) * 2) : kOOB;
-    bst8<kPlain>(ro, off2, uint2{pack_bf16(O[dt][0] * inv, O[dt][1] * inv),
+    bst8<kStream>(ro, off2, uint2{pack_bf16(O[dt][0] * inv, O[dt][1] * inv),
                                  pack_bf16(O[dt][2] * inv, O[dt][3] * inv)});
   }
 }
@@ -551,7 +582,15 @@ agent_mfma_kernel(MfmaParams p) {
   unsigned* ctr = p.sync + (long)head * (kBarriers + 1) * kSyncStride;
   const bool sync_group = p.fused && p.P > 1;
   const bool single = p.fused && p.P == 1;   // whole head in this workgroup
+  const int xp = sync_group ? (p.xcd_heads > 0 ? kXL2 : kXDevice) : kXNone;
   bool ok = true;
+  // groups placed on one XCD rely on workgroup b running on XCD b % 8
+  if (xp == kXL2 && tid == 0 && xcc_id() != (int)(blockIdx.x & 7))
+    __hip_atomic_fetch_or(reinterpret_cast<unsigned*>(p.status), kFaultXcd, __ATOMIC_RELAXED,
+                          __HIP_MEMORY_SCOPE_AGENT);
+#ifdef AGENT_ATTN_PHASE_TRACE
+  if (p.trace && tid == 0) p.trace[(long)blockIdx.x * 16 + 14] = xp * 100 + xcc_id();
+#endif
   const rsrc_t rq = rsrc_of(p.q + hoff, head_bytes);
   const rsrc_t rk = rsrc_of(p.k + hoff, head_bytes);
   const rsrc_t rv = rsrc_of(p.v + hoff, head_bytes);
@@ -579,6 +618,7 @@ agent_mfma_kernel(MfmaParams p) {
   // first query tile of this wave, loaded ahead of the broadcast
   const int nqt = n1 > n0 ? (n1 - n0 + 15) / 16 : 0;
   bf16x8 qcur[DC];
+  bool staged0 = false;   // first round already in LDS
   if ((p.phases & PH_BCAST) && !(p.phases & PH_AGG)) load_q_tile<DC>(qcur, rq, n0 + 16 * wave, n1, d);
   AA_STAMP(1);
 
@@ -628,13 +668,22 @@ agent_mfma_kernel(MfmaParams p) {
           const unsigned off = (unsigned)((a * d + 8 * c) * 4);
           const uint4 lo = f4_bits(float4{s8[0], s8[1], s8[2], s8[3]});
           const uint4 hi = f4_bits(float4{s8[4], s8[5], s8[6], s8[7]});
-          if (sync_group) { bst16<kCoherent>(ra, off, lo); bst16<kCoherent>(ra, off + 16, hi); }
-          else { bst16<kPlain>(ra, off, lo); bst16<kPlain>(ra, off + 16, hi); }
+          xst16(xp, ra, off, lo);
+          xst16(xp, ra, off + 16, hi);
         }
       }
     }
     AA_STAMP(2);
-    if (sync_group) ok = group_barrier(ctr + 0 * kSyncStride, p.P, p.status);
+    if (sync_group) {
+      group_arrive(ctr + 0 * kSyncStride);
+      // the first round's key and value tiles go to LDS while the group gathers
+      if ((p.phases & PH_AGG) && tid < r0tiles) {
+        store_tile_rows(Ks, C::KS_STRIDE, kx, tid, d);
+        store_tile_t(Vt, C::VT_STRIDE, vx, tid, d);
+      }
+      staged0 = (p.phases & PH_AGG) != 0;
+      ok = group_wait(ctr + 0 * kSyncStride, p.P, p.status);
+    }
     AA_STAMP(3);
   }
 
@@ -644,6 +693,8 @@ agent_mfma_kernel(MfmaParams p) {
     const float* rows = p.agents_f32_in ? p.agents_f32_in : p.agents_f32;
     const rsrc_t ra = from_rows ? rsrc_of(rows + ahb, arow_bytes)
                                 : rsrc_of(p.agents_in + ahb, (unsigned)(p.nag * d * 2));
+    with_pol(xp, [&](auto pc) {
+    constexpr int POL = decltype(pc)::value;
 #pragma unroll
     for (int f0 = 0; f0 < A_FRAGS; f0 += kThreads) {
       const int f = f0 + tid;
@@ -653,8 +704,8 @@ agent_mfma_kernel(MfmaParams p) {
       if (from_rows) {
         const unsigned off = in ? (unsigned)((agent * d + ch0) * 4) : kOOB;
         uint4 x0, x1;
-        if (sync_group) { x0 = bld16<kCoherent>(ra, off); x1 = bld16<kCoherent>(ra, off + 16); }
-        else { x0 = bld16<kPlain>(ra, off); x1 = bld16<kPlain>(ra, off + 16); }
+        x0 = bld16<POL>(ra, off);
+        x1 = bld16<POL>(ra, off + 16);
         const float4 a0 = bits_f4(x0), a1 = bits_f4(x1);
         union { bf16x8 v; unsigned w[4]; } fr;
         fr.w[0] = pack_bf16(a0.x, a0.y);
@@ -667,6 +718,7 @@ agent_mfma_kernel(MfmaParams p) {
         if (f < A_FRAGS) Af[f] = __builtin_bit_cast(bf16x8, x);
       }
     }
+    });
   }
   __syncthreads();
   AA_STAMP(4);
@@ -691,7 +743,7 @@ agent_mfma_kernel(MfmaParams p) {
         load_tile8(kx, rk, tid, rt0, tend, d);
         load_tile8(vx, rv, tid, rt0, tend, d);
       }
-      if (tid < ntile) {
+      if (tid < ntile && !(staged0 && rt0 == n0)) {
         store_tile_rows(Ks, C::KS_STRIDE, kx, tid, d);
         store_tile_t(Vt, C::VT_STRIDE, vx, tid, d);
       }
@@ -786,13 +838,11 @@ agent_mfma_kernel(MfmaParams p) {
           const unsigned off = (unsigned)(((t * DT + dt) * 64 + lane) * 16);
           const uint4 x = f4_bits(float4{st.acc[a][dt][0], st.acc[a][dt][1], st.acc[a][dt][2],
                                          st.acc[a][dt][3]});
-          if (sync_group) bst16<kCoherent>(racc, off, x);
-          else bst16<kPlain>(racc, off, x);
+          xst16(xp, racc, off, x);
         }
         const unsigned moff = g == 0 ? (unsigned)((t * 16 + (lane & 15)) * 8) : kOOB;
         const uint2 ml = uint2{__float_as_uint(st.m[a]), __float_as_uint(st.l[a])};
-        if (sync_group) bst8<kCoherent>(rml, moff, ml);
-        else bst8<kPlain>(rml, moff, ml);
+        xst8(xp, rml, moff, ml);
       }
     }
     AA_STAMP(6);
@@ -815,6 +865,8 @@ agent_mfma_kernel(MfmaParams p) {
     const rsrc_t racc = rsrc_of(p.part_acc + hbase * DT * 256, (unsigned)(p.P * KTC * DT * 1024));
     const rsrc_t rml = rsrc_of(p.part_ml + hbase * 32, (unsigned)(p.P * KTC * 128));
     const rsrc_t rvo = rsrc_of(p.values_f32 + ahb, arow_bytes);
+    with_pol(xp, [&](auto pc) {
+    constexpr int POL = decltype(pc)::value;
     for (int it = tid; it < items; it += kThreads) {
       const int m = it / nq, q = it - m * nq;
       const int a = slot + p.P * m;
@@ -831,13 +883,9 @@ agent_mfma_kernel(MfmaParams p) {
         for (int u = 0; u < 16; ++u) {
           const bool in = s0 + u < p.P;
           const unsigned so = (unsigned)(s0 + u);
-          if (sync_group) {
-            xa[u] = bld16<kCoherent>(racc, in ? aoff + so * sstride_acc : kOOB);
-            xm[u] = __builtin_amdgcn_raw_buffer_load_b64(rml, (int)(in ? moff + so * sstride_ml : kOOB), 0, kCoherent);
-          } else {
-            xa[u] = bld16<kPlain>(racc, in ? aoff + so * sstride_acc : kOOB);
-            xm[u] = __builtin_amdgcn_raw_buffer_load_b64(rml, (int)(in ? moff + so * sstride_ml : kOOB), 0, kPlain);
-          }
+          xa[u] = bld16<POL>(racc, in ? aoff + so * sstride_acc : kOOB);
+          xm[u] = __builtin_amdgcn_raw_buffer_load_b64(
+              rml, (int)(in ? moff + so * sstride_ml : kOOB), 0, POL);
         }
         float cm = M;
 #pragma unroll
@@ -864,9 +912,9 @@ agent_mfma_kernel(MfmaParams p) {
       const int ch = 16 * dt + 4 * g;
       const unsigned off = (a < p.nag && ch < d) ? (unsigned)((a * d + ch) * 4) : kOOB;
       const uint4 x = f4_bits(float4{acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv});
-      if (sync_group) bst16<kCoherent>(rvo, off, x);
-      else bst16<kPlain>(rvo, off, x);
+      bst16<POL>(rvo, off, x);
     }
+    });
     AA_STAMP(8);
     if (sync_group && ok) ok = group_barrier(ctr + 2 * kSyncStride, p.P, p.status);
     AA_STAMP(9);
@@ -880,6 +928,8 @@ agent_mfma_kernel(MfmaParams p) {
     const float* rows = p.values_f32_in ? p.values_f32_in : p.values_f32;
     const rsrc_t rvr = rsrc_of(rows + ahb, arow_bytes);
     __syncthreads();
+    with_pol(xp, [&](auto pc) {
+    constexpr int POL = decltype(pc)::value;
 #pragma unroll
     for (int f0 = 0; f0 < VA_FRAGS; f0 += kThreads) {
       const int f = f0 + tid;
@@ -894,7 +944,7 @@ agent_mfma_kernel(MfmaParams p) {
           x[e] = in ? stage[agent * DPAD + ch] : 0.f;
         } else {
           const unsigned off = in ? (unsigned)((agent * d + ch) * 4) : kOOB;
-          x[e] = sync_group ? bld4<kCoherent>(rvr, off) : bld4<kPlain>(rvr, off);
+          x[e] = bld4<POL>(rvr, off);
         }
       }
       union { bf16x8 v; bf16_t e[8]; } hi, lo;
@@ -908,6 +958,7 @@ agent_mfma_kernel(MfmaParams p) {
         if (C::VSPLIT > 1) VAf[VA_FRAGS + f] = lo.v;
       }
     }
+    });
     __syncthreads();
     AA_STAMP(10);
     const rsrc_t ro = rsrc_of(p.out + hoff, head_bytes);
@@ -934,6 +985,10 @@ agent_mfma_kernel(MfmaParams p) {
       }
     }
   }
+#ifdef AGENT_ATTN_PHASE_TRACE
+  __builtin_amdgcn_s_waitcnt(0);
+  AA_STAMP(13);
+#endif
 }
 
 // Launch helper instantiated per DC in its own translation unit.

@@ -130,6 +130,20 @@ int agent_attn_broadcast(const void* q, const float* agents_f32,
                          int H, int N, int d, int n_agents, float scale,
                          int dtype, void* stream);
 
+/* Bits of the fault word that fused launches leave in their workspace. */
+#define AGENT_ATTN_FAULT_BARRIER 1 /* a workgroup barrier gave up waiting */
+#define AGENT_ATTN_FAULT_XCD 2     /* a workgroup ran off its planned XCD */
+
+/* Waits for the work on `stream`, then reads and clears the fault word of
+ * `workspace` (a workspace given to agent_attn_forward_ws), or of the
+ * library's scratch of the current device when workspace is NULL.  *faults
+ * receives 0 when every forward launched on it since the last read ran
+ * normally; otherwise a set of AGENT_ATTN_FAULT_* bits, and the outputs of
+ * those launches are not valid.  Device-side waits are bounded, so a fault
+ * ends the launch instead of hanging it.  Returns AGENT_ATTN_ERR_NULL when
+ * faults is NULL, AGENT_ATTN_ERR_HIP when a HIP call fails. */
+int agent_attn_read_faults(void* workspace, void* stream, int* faults);
+
 /* Frees the library's cached per-device scratch buffers. */
 void agent_attn_release(void);
 

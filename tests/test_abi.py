@@ -117,3 +117,7 @@ def test_python_binding_rejects_cpu_tensors():
     q = torch.zeros(1, 1, 4, 8)
     with pytest.raises(ValueError):
         eav.agent_attn_forward(q, q, q, (2, 2), 1)
+
+
+def test_read_faults_needs_an_output(L):
+    assert L.agent_attn_read_faults(WS, None, None) == ERR_NULL

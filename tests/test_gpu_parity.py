@@ -31,6 +31,7 @@ def run_case(wl, seed, kind, cached=False):
     O, _, _ = oracle.forward(inp.Q.exact, inp.K.exact, inp.V.exact, wl.h, wl.w, wl.s, wl.scale,
                              A=None if inp.A is None else inp.A.exact)
     got = to_host_f64(out)
+    assert eav.agent_attn_read_faults() == 0
     a_err, r_err = parity.errors(got, O)
     say(f"       max-abs {a_err:.3e}  relative {r_err:.3e}")
     parity.assert_close(got, O, wl.dtype, wl.name, kind=kind)
@@ -182,6 +183,7 @@ def test_fused_counters_return_to_zero():
         parity.assert_close(to_host_f64(out), O, "bf16", wl.name, kind="discriminating")
     torch.cuda.synchronize()
     assert int(ws[: 512 * 512].count_nonzero()) == 0     # counters
+    assert eav.agent_attn_read_faults(ws) == 0
 
 
 def test_shared_workspace_across_shapes():
