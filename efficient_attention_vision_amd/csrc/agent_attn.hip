@@ -135,7 +135,7 @@ struct Plan {
 int mfma_dc(int d) { return d <= 32 ? 1 : (d <= 64 ? 2 : 4); }
 int mfma_ktc(int nag) { return nag <= 64 ? 4 : (nag <= 128 ? 8 : 16); }
 
-constexpr size_t kSyncBytesPerHead = (aa::kBarriers + 1) * aa::kSyncStride * sizeof(unsigned);
+constexpr size_t kSyncBytesPerHead = aa::kSyncDwords * sizeof(unsigned);
 // Heads that can own group counters: P > 1 needs B*H*P <= CUs, so at most
 // CUs/2 heads.  The counters live in a fixed-size prefix of every workspace
 // so that calls of different shapes sharing one workspace never place other
@@ -252,6 +252,7 @@ bool xcd_round_robin(hipStream_t st) {
 // chip at once (one per compute unit) and can meet at group barriers.
 void mfma_split(const Dims& D, int cus, int& P, int& T) {
   long p = (D.BH >= cus || D.BH > kMaxSyncHeads) ? 1 : cus / D.BH;
+  if (p > aa::kMaxGroup) p = aa::kMaxGroup;
   const long maxp = (D.N + 15) / 16;
   if (p > maxp) p = maxp;
   if (p < 1) p = 1;

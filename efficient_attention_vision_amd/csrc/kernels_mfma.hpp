@@ -54,7 +54,14 @@ enum : int { PH_POOL = 1, PH_AGG = 2, PH_MERGE = 4, PH_BCAST = 8 };
 constexpr int kWaves = 8;                // waves per workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBarriers = 3;
-constexpr int kSyncStride = 32;          // dwords between counters (own 128 B line)
+// Per-head synchronisation block (512 B): one flag byte per workgroup of the
+// group (flag barriers), then the counters of the counting barriers and the
+// counter of finished workgroups.
+constexpr int kSyncDwords = 128;
+constexpr int kMaxGroup = 256;           // flag bytes: at most 256 workgroups per head
+constexpr int kCtrDword = 64;            // counters at dwords 64, 80, 96
+constexpr int kCtrStride = 16;
+constexpr int kDoneDword = kCtrDword + kBarriers * kCtrStride;
 constexpr long kSpinLimit = 1L << 20;    // bounded waits: ~1 s, then an error
 constexpr int kPoolTok = 8;              // window tokens per pooling work item
 constexpr unsigned kOOB = 0x7ffffff0u;   // an offset past every buffer range
@@ -183,17 +190,19 @@ template <int POL>
 __device__ __forceinline__ void bst4(rsrc_t r, unsigned off, float x) {
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, (int)off, 0, POL);
 }
-// Runs f with the cache policy of exchange policy xp as a compile-time
-// constant, so that loops of loads are instantiated per policy rather than
-// branching around every load.
+// Runs f with the cache policy of the loads of exchange policy xp as a
+// compile-time constant, so that loops of loads are instantiated per policy
+// rather than branching around every load.
 template <int V>
 struct PolC {
   static constexpr int value = V;
 };
+// Loads of exchanged data are device-coherent (sc1) for both kinds of
+// group: they skip the CU's vector cache, which may hold stale lines, and
+// are served by the L2 when the writer is on the same XCD.
 template <class F>
 __device__ __forceinline__ void with_pol(int xp, F&& f) {
-  if (xp == kXDevice) f(PolC<kCoherent>{});
-  else if (xp == kXL2) f(PolC<kL2>{});
+  if (xp != kXNone) f(PolC<kCoherent>{});
   else f(PolC<kPlain>{});
 }
 __device__ __forceinline__ void xst16(int xp, rsrc_t r, unsigned off, uint4 x) {
@@ -216,26 +225,75 @@ __device__ __forceinline__ float4 bits_f4(uint4 x) {
 }
 
 // Barrier of the P workgroups of one head, in two halves so that loads can
-// be issued between the arrival and the wait.  Counters start at zero in
-// every launch: the last workgroup to finish the kernel resets them.  Before
-// arriving, every wave waits for its own loads and stores to complete, so
-// data stored before the barrier is visible to device-coherent loads after
-// it.
-__device__ __forceinline__ void group_arrive(unsigned* ctr) {
+// be issued between the arrival and the wait.  Before arriving, every wave
+// waits for its own loads and stores to complete, so data stored before the
+// barrier is visible to the device-coherent (sc1) loads made after it.
+//  - Group on one XCD: workgroup `slot` writes barrier number k+1 into its
+//    flag byte through the XCD's L2; waiters read all P flags with sc1 loads
+//    (one dword of four flags per lane of wave 0), which the L2 serves.
+//  - Group over several XCDs: agent-scope atomic counter per barrier.
+// Flags and counters are zero at the start of every launch: the last
+// workgroup of the group to finish clears them.  Waits are bounded: on
+// timeout the fault word gets kFaultBarrier and the workgroup stops.
+struct GroupSync {
+  unsigned* blk;   // this head's synchronisation block
+  int slot, P;
+  bool flags;      // flag barrier (group on one XCD)
+  int* status;
+};
+__device__ __forceinline__ void group_arrive(const GroupSync& g, int k) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (threadIdx.x == 0) __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ bool group_wait(unsigned* ctr, unsigned n, int* status) {
-  __shared__ int ok;
   if (threadIdx.x == 0) {
+    if (g.flags) {
+      const rsrc_t r = rsrc_of(g.blk, kMaxGroup);
+      __builtin_amdgcn_raw_buffer_store_b8((unsigned char)(k + 1), r, g.slot, 0, kL2);
+    } else {
+      __hip_atomic_fetch_add(g.blk + kCtrDword + k * kCtrStride, 1u, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+__device__ __forceinline__ bool group_wait(const GroupSync& g, int k) {
+  __shared__ int ok;
+  if (g.flags) {
+    if (threadIdx.x < 64) {
+      const int lane = threadIdx.x;
+      const rsrc_t r = rsrc_of(g.blk, kMaxGroup);
+      const int nw = (g.P + 3) >> 2;
+      // bytes past P count as arrived
+      const int past = 4 * lane + 4 - g.P;
+      const unsigned pad = past <= 0 ? 0u : (past >= 4 ? 0xffffffffu : (0xffffffffu << (8 * (4 - past))));
+      const unsigned want = 0x01010101u * (unsigned)(k + 1);
+      long spins = 0;
+      bool good = true;
+      while (true) {
+        const unsigned w = lane < nw ? (__builtin_amdgcn_raw_buffer_load_b32(r, 4 * lane, 0, kCoherent) | pad)
+                                     : 0xffffffffu;
+        // every byte >= k+1 (flags only ever hold 0..kBarriers)
+        const unsigned lo = (w | 0x80808080u) - want;
+        const bool arrived = ((~w & 0x80808080u) & ~lo) == 0u;
+        if (__all(arrived)) break;
+        if (++spins > kSpinLimit) {
+          good = false;
+          if (lane == 0)
+            __hip_atomic_fetch_or(reinterpret_cast<unsigned*>(g.status), kFaultBarrier,
+                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      if (lane == 0) ok = good ? 1 : 0;
+    }
+  } else if (threadIdx.x == 0) {
     ok = 1;
     long spins = 0;
-    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < n) {
+    unsigned* c = g.blk + kCtrDword + k * kCtrStride;
+    while (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (unsigned)g.P) {
       if (++spins > kSpinLimit) {
         ok = 0;
-        __hip_atomic_fetch_or(reinterpret_cast<unsigned*>(status), kFaultBarrier, __ATOMIC_RELAXED,
-                              __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_or(reinterpret_cast<unsigned*>(g.status), kFaultBarrier,
+                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
       __builtin_amdgcn_s_sleep(1);
@@ -244,9 +302,30 @@ __device__ __forceinline__ bool group_wait(unsigned* ctr, unsigned n, int* statu
   __syncthreads();
   return ok != 0;
 }
-__device__ __forceinline__ bool group_barrier(unsigned* ctr, unsigned n, int* status) {
-  group_arrive(ctr);
-  return group_wait(ctr, n, status);
+__device__ __forceinline__ bool group_barrier(const GroupSync& g, int k) {
+  group_arrive(g, k);
+  return group_wait(g, k);
+}
+// Called by every workgroup after its last barrier: the last one to get here
+// clears the group's flags and counters for the next launch.
+__device__ __forceinline__ void group_finish(const GroupSync& g) {
+  __syncthreads();
+  __shared__ int last;
+  if (threadIdx.x == 0) {
+    const unsigned old = __hip_atomic_fetch_add(g.blk + kDoneDword, 1u, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+    last = old == (unsigned)g.P - 1;
+  }
+  __syncthreads();
+  if (last && threadIdx.x < 64) {
+    const rsrc_t r = rsrc_of(g.blk, kSyncDwords * 4);
+    // flag dwords, the counters and the finished count (all of dwords 0..127
+    // that are in use); device-coherent stores so any XCD sees them next time
+    const int lane = threadIdx.x;
+    bst4<kCoherent>(r, 4 * lane, 0.f);                                  // flags
+    if (lane < kBarriers) bst4<kCoherent>(r, 4 * (kCtrDword + lane * kCtrStride), 0.f);
+    if (lane == kBarriers) bst4<kCoherent>(r, 4 * kDoneDword, 0.f);
+  }
 }
 
 // Agent index held at contraction position e (0..7) of lane group g in the
@@ -579,10 +658,11 @@ agent_mfma_kernel(MfmaParams p) {
   const int n1 = min(p.N, n0 + p.T);
   const long hoff = (long)head * p.N * d;
   const unsigned head_bytes = (unsigned)(p.N * d * 2);
-  unsigned* ctr = p.sync + (long)head * (kBarriers + 1) * kSyncStride;
+  GroupSync gs{p.sync + (long)head * kSyncDwords, slot, p.P, false, p.status};
   const bool sync_group = p.fused && p.P > 1;
   const bool single = p.fused && p.P == 1;   // whole head in this workgroup
   const int xp = sync_group ? (p.xcd_heads > 0 ? kXL2 : kXDevice) : kXNone;
+  gs.flags = xp == kXL2;
   bool ok = true;
   // groups placed on one XCD rely on workgroup b running on XCD b % 8
   if (xp == kXL2 && tid == 0 && xcc_id() != (int)(blockIdx.x & 7))
@@ -675,14 +755,14 @@ agent_mfma_kernel(MfmaParams p) {
     }
     AA_STAMP(2);
     if (sync_group) {
-      group_arrive(ctr + 0 * kSyncStride);
+      group_arrive(gs, 0);
       // the first round's key and value tiles go to LDS while the group gathers
       if ((p.phases & PH_AGG) && tid < r0tiles) {
         store_tile_rows(Ks, C::KS_STRIDE, kx, tid, d);
         store_tile_t(Vt, C::VT_STRIDE, vx, tid, d);
       }
       staged0 = (p.phases & PH_AGG) != 0;
-      ok = group_wait(ctr + 0 * kSyncStride, p.P, p.status);
+      ok = group_wait(gs, 0);
     }
     AA_STAMP(3);
   }
@@ -847,10 +927,10 @@ agent_mfma_kernel(MfmaParams p) {
     }
     AA_STAMP(6);
     if (sync_group && ok) {
-      group_arrive(ctr + 1 * kSyncStride);
+      group_arrive(gs, 1);
       // the query tile loads travel while the group gathers
       if (p.phases & PH_BCAST) load_q_tile<DC>(qcur, rq, n0 + 16 * wave, n1, d);
-      ok = group_wait(ctr + 1 * kSyncStride, p.P, p.status);
+      ok = group_wait(gs, 1);
     } else if (sync_group && (p.phases & PH_BCAST)) {
       load_q_tile<DC>(qcur, rq, n0 + 16 * wave, n1, d);
     }
@@ -916,7 +996,7 @@ agent_mfma_kernel(MfmaParams p) {
     }
     });
     AA_STAMP(8);
-    if (sync_group && ok) ok = group_barrier(ctr + 2 * kSyncStride, p.P, p.status);
+    if (sync_group && ok) ok = group_barrier(gs, 2);
     AA_STAMP(9);
   }
 
@@ -972,19 +1052,8 @@ agent_mfma_kernel(MfmaParams p) {
   }
   AA_STAMP(11);
 
-  // ---- reset the group's counters once every workgroup of the group is done
-  if (sync_group) {
-    __syncthreads();
-    if (tid == 0) {
-      unsigned* done = ctr + kBarriers * kSyncStride;
-      const unsigned old = __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (old == (unsigned)p.P - 1) {
-        for (int b = 0; b < kBarriers; ++b)
-          __hip_atomic_store(ctr + b * kSyncStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-  }
+  // ---- the last workgroup of the group clears the barrier state
+  if (sync_group) group_finish(gs);
 #ifdef AGENT_ATTN_PHASE_TRACE
   __builtin_amdgcn_s_waitcnt(0);
   AA_STAMP(13);
