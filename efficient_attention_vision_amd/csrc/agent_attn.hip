@@ -210,16 +210,67 @@ int device_cus() {
   return cache[dev];
 }
 
-// Records the XCD of every workgroup of a 1024-workgroup launch.
-__global__ void __launch_bounds__(512) xcd_probe_kernel(int* out) {
-  if (threadIdx.x == 0) out[blockIdx.x] = aa::xcc_id();
+// One-time check, per device, of the two facts that the one-XCD exchange of
+// the fused kernel relies on:
+//  1. workgroup b runs on XCD b % 8 (XCC_ID register);
+//  2. data stored with sc0 by one workgroup is returned, after a flag
+//     barrier, by sc1 loads of another workgroup on the same XCD, even when
+//     the reader's CU cache holds an older copy of those lines (the probe
+//     plants one by reading the region before it is written).
+// 256 workgroups of 256 threads: member m = b / 8 of XCD x = b % 8's group.
+constexpr int kProbeWGs = 256, kProbeWords = 1024;
+
+__global__ void __launch_bounds__(256)
+xcd_probe_kernel(int* xcc, unsigned* flags, unsigned* data, unsigned* errors) {
+  const int b = blockIdx.x, x = b % 8, m = b / 8, members = kProbeWGs / 8;
+  const int nb = (m + 1) % members;
+  if (threadIdx.x == 0) xcc[b] = aa::xcc_id();
+  unsigned* region = data + (long)x * members * kProbeWords;
+  const aa::rsrc_t rd = aa::rsrc_of(region, members * kProbeWords * 4);
+  const aa::rsrc_t rf = aa::rsrc_of(flags + x * members, members * 4);
+  // plant a stale copy of the neighbour's lines in this CU's cache
+  unsigned seen = 0;
+  for (int i = threadIdx.x; i < kProbeWords; i += 256)
+    seen += __builtin_amdgcn_raw_buffer_load_b32(rd, (nb * kProbeWords + i) * 4, 0, aa::kPlain);
+  for (int i = threadIdx.x; i < kProbeWords; i += 256)
+    __builtin_amdgcn_raw_buffer_store_b32(0x40000000u + (unsigned)(b * kProbeWords + i), rd,
+                                          (m * kProbeWords + i) * 4, 0, aa::kL2);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  __shared__ int ok;
+  if (threadIdx.x == 0) __builtin_amdgcn_raw_buffer_store_b32(1u, rf, m * 4, 0, aa::kL2);
+  if (threadIdx.x < 64) {
+    long spins = 0;
+    bool good = true;
+    while (true) {
+      const unsigned f = threadIdx.x < members
+                             ? __builtin_amdgcn_raw_buffer_load_b32(rf, threadIdx.x * 4, 0, aa::kCoherent)
+                             : 1u;
+      if (__all(f == 1u)) break;
+      if (++spins > aa::kSpinLimit) { good = false; break; }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    if (threadIdx.x == 0) ok = good;
+  }
+  __syncthreads();
+  unsigned bad = ok ? 0u : (1u << 20);
+  if (ok) {
+    const unsigned base = 0x40000000u + (unsigned)((x + 8 * nb) * kProbeWords);
+    for (int i = threadIdx.x; i < kProbeWords; i += 256) {
+      const unsigned v = __builtin_amdgcn_raw_buffer_load_b32(rd, (nb * kProbeWords + i) * 4, 0,
+                                                              aa::kCoherent);
+      bad += v != base + (unsigned)i;
+    }
+  }
+  bad += seen == 0xffffffffu;   // keeps the planting loads
+  if (bad) atomicAdd(errors, bad);
 }
 
-// Whether the current device runs workgroup b on XCD b % 8, checked once per
-// device with a probe launch.  Groups of workgroups placed on one XCD by that
-// rule exchange their data through the XCD's L2 instead of device-coherent
-// memory.  The probe synchronises, so it is not run while `st` is being
-// captured into a graph (the answer is then "no" for that call).
+// Whether the one-XCD exchange may be used on the current device: both facts
+// above hold, checked once per device with the probe launch.  The probe
+// synchronises, so it is not run while `st` is being captured into a graph
+// (the answer is then "no" for that call, and the check waits for a later
+// call).  A failed check selects the device-coherent exchange.
 bool xcd_round_robin(hipStream_t st) {
   static std::mutex mu;
   static std::vector<int> cache;   // -1 unknown, 0 no, 1 yes
@@ -231,18 +282,28 @@ bool xcd_round_robin(hipStream_t st) {
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
   if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
     return false;
-  constexpr int kProbe = 1024;
-  int* d_out = nullptr;
-  if (hipMalloc(&d_out, kProbe * sizeof(int)) != hipSuccess) return false;
-  std::vector<int> h(kProbe, -1);
+  const size_t n_xcc = kProbeWGs, n_flags = kProbeWGs, n_data = (size_t)kProbeWGs * kProbeWords;
+  const size_t bytes = (n_xcc + n_flags + n_data + 1) * 4;
+  char* buf = nullptr;
+  if (hipMalloc(&buf, bytes) != hipSuccess) return false;
+  int* d_xcc = (int*)buf;
+  unsigned* d_flags = (unsigned*)(buf + n_xcc * 4);
+  unsigned* d_data = (unsigned*)(buf + (n_xcc + n_flags) * 4);
+  unsigned* d_err = (unsigned*)(buf + (n_xcc + n_flags + n_data) * 4);
+  std::vector<int> h(n_xcc, -1);
+  unsigned errors = 1;
   bool ok = false;
-  hipLaunchKernelGGL(xcd_probe_kernel, dim3(kProbe), dim3(512), 0, nullptr, d_out);
-  if (hipGetLastError() == hipSuccess &&
-      hipMemcpy(h.data(), d_out, kProbe * sizeof(int), hipMemcpyDeviceToHost) == hipSuccess) {
-    ok = true;
-    for (int b = 0; b < kProbe; ++b) ok = ok && h[b] == b % 8;
+  if (hipMemset(buf, 0, bytes) == hipSuccess) {
+    hipLaunchKernelGGL(xcd_probe_kernel, dim3(kProbeWGs), dim3(256), 0, nullptr, d_xcc, d_flags,
+                       d_data, d_err);
+    if (hipGetLastError() == hipSuccess &&
+        hipMemcpy(h.data(), d_xcc, n_xcc * 4, hipMemcpyDeviceToHost) == hipSuccess &&
+        hipMemcpy(&errors, d_err, 4, hipMemcpyDeviceToHost) == hipSuccess) {
+      ok = errors == 0;
+      for (int b = 0; b < kProbeWGs; ++b) ok = ok && h[b] == b % 8;
+    }
   }
-  (void)hipFree(d_out);
+  (void)hipFree(buf);
   cache[dev] = ok ? 1 : 0;
   return ok;
 }
