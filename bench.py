@@ -65,6 +65,23 @@ def cpu_baseline(wl, min_seconds=10.0):
             "seconds": el}
 
 
+COPY_BYTES = 64 << 20
+
+
+def copy_calibration(torch, steps):
+    """Plain device-to-device copies of COPY_BYTES each, over rotating
+    buffers (> 1 GiB in total), so that an HBM counter read per dispatch can
+    be divided by the known COPY_BYTES read and written."""
+    dev = torch.device("cuda:0")
+    n = COPY_BYTES // 4
+    bufs = [torch.ones(n, dtype=torch.float32, device=dev) for _ in range(20)]
+    for i in range(steps):
+        bufs[(2 * i + 1) % 20].copy_(bufs[(2 * i) % 20])
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read": COPY_BYTES, "bytes_written": COPY_BYTES,
+                                           "copies": steps}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -73,14 +90,19 @@ def main():
     ap.add_argument("--workload", default="pvt_stage1")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only plain device copies of known size (for scaling HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the forward shards over heads with no communication; see DESIGN.md)",
+              "(heads are independent: each GPU would run this same forward on its share of B*H)",
               file=sys.stderr)
         sys.exit(2)
 
     import torch
+    if args.copy_calibration:
+        copy_calibration(torch, args.steps)
+        return
     import efficient_attention_vision_amd as eav
     from efficient_attention_vision_amd import _binding, inputs
 

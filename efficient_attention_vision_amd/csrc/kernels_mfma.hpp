@@ -611,13 +611,35 @@ __device__ __forceinline__ void bcast_tile(const bf16x8 (&qf)[DC], const bf16x8*
   L = group4_sum(L);
   const float inv = 1.0f / L;
   const int tok = tok0 + r;
+  // Lane (r, g) holds channels 16 dt + 4 g .. +3 of token r for every dt.
+  // Two 2 x 2 transposes between lane groups (permlane32_swap exchanges
+  // lane-group bit 1 with the dt bit 0, permlane16_swap then exchanges
+  // lane-group bit 0 with the source group's bit 1) leave lane (r, g) with
+  // channels 64 q + 32 s + 8 g .. +7, so every store instruction writes
+  // whole 64-byte segments of 16 rows instead of 8-byte pieces.
+  unsigned pk[DT][2];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
-    const int ch = 16 * dt + 4 * g;
-    const unsigned off2 = (tok < tok_end && ch < d) ? (unsigned)((tok * d + ch) * 2) : kOOB;
-    bst8<kStream>(ro, off2, uint2{pack_bf16(O[dt][0] * inv, O[dt][1] * inv),
-                                 pack_bf16(O[dt][2] * inv, O[dt][3] * inv)});
+    pk[dt][0] = pack_bf16(O[dt][0] * inv, O[dt][1] * inv);
+    pk[dt][1] = pack_bf16(O[dt][2] * inv, O[dt][3] * inv);
   }
+  constexpr int NS = DT >= 4 ? 2 : 1;
+#pragma unroll
+  for (int q = 0; q < (DT + 3) / 4; ++q)
+#pragma unroll
+    for (int s2 = 0; s2 < NS; ++s2) {
+      const int d0 = 4 * q + 2 * s2, d1 = d0 + 1;
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        const u32x2 x = __builtin_amdgcn_permlane32_swap(pk[d0][w], pk[d1][w], false, false);
+        const u32x2 y = __builtin_amdgcn_permlane16_swap(x[0], x[1], false, false);
+        pk[d0][w] = y[0];
+        pk[d1][w] = y[1];
+      }
+      const int c0 = 64 * q + 32 * s2 + 8 * g;
+      const unsigned off2 = (tok < tok_end && c0 < d) ? (unsigned)((tok * d + c0) * 2) : kOOB;
+      bst16<kStream>(ro, off2, uint4{pk[d0][0], pk[d0][1], pk[d1][0], pk[d1][1]});
+    }
 }
 
 // ------------------------------------------------------------- the kernel
