@@ -564,21 +564,32 @@ __device__ __forceinline__ void bcast_tile(const bf16x8 (&qf)[DC], const bf16x8*
   constexpr int DT = 2 * DC;
   constexpr int VA_PART = C::KC * DT * 64;
   const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+  // When the agent and V_A fragments need more than 128 registers they
+  // cannot all stay in registers across the caller's tile loop: the LDS
+  // index and agent count are then made opaque per tile so that the fragment
+  // reads and the padding compares are redone per tile instead of being
+  // hoisted (and spilled).
+  constexpr int kFragRegs = 4 * (KTC * DC + C::KC * DT * C::VSPLIT);
+  int fl = lane, nag_t = nag;
+  if (kFragRegs > 128 || KTC >= 16) {
+    asm volatile("" : "+v"(fl));
+    asm volatile("" : "+s"(nag_t));
+  }
   f32x4 S[KTC];
 #pragma unroll
   for (int t = 0; t < KTC; ++t) {
     S[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < DC; ++c)
-      S[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Af[(t * DC + c) * 64 + lane], qf[c], S[t],
+      S[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Af[(t * DC + c) * 64 + fl], qf[c], S[t],
                                                      0, 0, 0);
   }
 #pragma unroll
   for (int t = 0; t < KTC; ++t)
-    if (16 * t + 16 > nag)   // padding agents of this tile
+    if (16 * t + 16 > nag_t)   // padding agents of this tile
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (16 * t + 4 * g + i >= nag) S[t][i] = -INFINITY;
+        if (16 * t + 4 * g + i >= nag_t) S[t][i] = -INFINITY;
   float M = -INFINITY;
 #pragma unroll
   for (int t = 0; t < KTC; ++t) M = fmaxf(M, fmaxf(fmaxf(S[t][0], S[t][1]), fmaxf(S[t][2], S[t][3])));
@@ -602,7 +613,7 @@ __device__ __forceinline__ void bcast_tile(const bf16x8 (&qf)[DC], const bf16x8*
     for (int e = 0; e < 4; ++e) pf.w[e] = pack_bf16(pv[2 * e], pv[2 * e + 1]);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      const int f = (j * DT + dt) * 64 + lane;
+      const int f = (j * DT + dt) * 64 + fl;
       O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(VAf[f], pf.v, O[dt], 0, 0, 0);
       if (C::VSPLIT > 1)
         O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(VAf[VA_PART + f], pf.v, O[dt], 0, 0, 0);
