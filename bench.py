@@ -26,6 +26,180 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 matrix cores
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "efficient_attention_vision_amd", "csrc")
+FUSED_KERNEL = "agent_mfma_kernel"
+
+# rocprofv3 runs whose output the summaries below are made from (run from
+# /tmp with TMPDIR=/tmp; R = repository root)
+TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/kt_{w} -o run "
+             "-- python3 $R/bench.py --workload {w} --no-cpu-baseline --steps 50 --warmup 5")
+PMC_CMD = ("timeout -s KILL 120 rocprofv3 --pmc {c} --output-format csv -d $R/gpurun_out/{d} -o run "
+           "-- python3 $R/bench.py {a}")
+
+
+def kernel_sources_sha256() -> str:
+    """Hash of the HIP sources and the ABI header: HBM counters taken on an
+    older kernel are not reported."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.hpp")))
+    files.append(os.path.join(ROOT, "include", "agent_attn.h"))
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def counters_file(wl_name: str) -> str:
+    return os.path.join(PROFILES, f"{FUSED_KERNEL}_{wl_name}_hbm_counters.md")
+
+
+def read_key_values(path):
+    out = {}
+    with open(path) as fh:
+        for line in fh:
+            line = line.strip().lstrip("-* ").strip()
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                out[k.strip().strip("`")] = v.strip().strip("`")
+    return out
+
+
+def measured_traffic(wl_name: str):
+    """HBM bytes per launch of the fused kernel from the committed counter
+    summary, or None when there is none or the kernel has changed since."""
+    path = counters_file(wl_name)
+    if not os.path.exists(path):
+        return None
+    kv = read_key_values(path)
+    if kv.get("kernel_sources_sha256") != kernel_sources_sha256():
+        return None
+    try:
+        return int(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def _counter_means(csv_path, name_part):
+    import csv
+    vals = {}
+    with open(csv_path) as fh:
+        for r in csv.DictReader(fh):
+            if name_part in r["Kernel_Name"]:
+                vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in vals.items()}, {k: len(v) for k, v in vals.items()}
+
+
+def write_counter_summary(wl, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
+    """profiles/<kernel>_<workload>_hbm_counters.md from four rocprofv3 --pmc
+    runs: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the fused kernel,
+    each scaled by what the same counter reads for plain copies of
+    COPY_BYTES."""
+    def one(d, name):
+        m, n = _counter_means(os.path.join(d, "run_counter_collection.csv"), name)
+        return m, n
+    f_k, nf = one(fetch_dir, FUSED_KERNEL)
+    w_k, nw = one(write_dir, FUSED_KERNEL)
+    f_c, _ = one(copy_fetch_dir, "copyBuffer")
+    w_c, _ = one(copy_write_dir, "copyBuffer")
+    kib = COPY_BYTES / 1024
+    f_scale = kib / f_c["FETCH_SIZE"]
+    w_scale = kib / w_c["WRITE_SIZE"]
+    fetch_b = f_k["FETCH_SIZE"] * 1024 * f_scale
+    write_b = w_k["WRITE_SIZE"] * 1024 * w_scale
+    total = int(round(fetch_b + write_b))
+    alg = algorithmic_bytes(wl)
+    rows = [
+        f"# HBM counters: {FUSED_KERNEL}, workload {wl.name}",
+        "",
+        f"Workload: B={wl.B} H={wl.H} grid {wl.h}x{wl.w} (N={wl.N}) d={wl.d} k={wl.k} {wl.dtype}.",
+        "Commands (from /tmp with TMPDIR=/tmp, R = repository root), one counter per run:",
+        "",
+        "    " + PMC_CMD.format(c="FETCH_SIZE", d=os.path.basename(fetch_dir),
+                                a=f"--workload {wl.name} --no-cpu-baseline --steps 10 --warmup 2"),
+        "    " + PMC_CMD.format(c="WRITE_SIZE", d=os.path.basename(write_dir),
+                                a=f"--workload {wl.name} --no-cpu-baseline --steps 10 --warmup 2"),
+        "    " + PMC_CMD.format(c="FETCH_SIZE", d=os.path.basename(copy_fetch_dir),
+                                a="--copy-calibration --steps 10"),
+        "    " + PMC_CMD.format(c="WRITE_SIZE", d=os.path.basename(copy_write_dir),
+                                a="--copy-calibration --steps 10"),
+        "    python3 bench.py --workload " + wl.name + " --pmc-summary <the four -d folders>",
+        "",
+        "Calibration: plain device copies (`__amd_rocclr_copyBuffer`) of "
+        f"{COPY_BYTES} bytes read and written per dispatch.",
+        "",
+        f"- copy FETCH_SIZE KiB per dispatch: {f_c['FETCH_SIZE']:.1f}",
+        f"- copy WRITE_SIZE KiB per dispatch: {w_c['WRITE_SIZE']:.1f}",
+        f"- fetch_scale: {f_scale:.4f}",
+        f"- write_scale: {w_scale:.4f}",
+        f"- fused kernel dispatches sampled: {nf.get('FETCH_SIZE', 0)} / {nw.get('WRITE_SIZE', 0)}",
+        f"- fused FETCH_SIZE KiB per dispatch: {f_k['FETCH_SIZE']:.1f}",
+        f"- fused WRITE_SIZE KiB per dispatch: {w_k['WRITE_SIZE']:.1f}",
+        f"- fetch_bytes_per_launch: {int(round(fetch_b))}",
+        f"- write_bytes_per_launch: {int(round(write_b))}",
+        f"- traffic_bytes_per_launch: {total}",
+        f"- algorithmic_bytes_per_launch: {alg}",
+        f"- traffic / algorithmic: {total / alg:.3f}",
+        f"- kernel_sources_sha256: {kernel_sources_sha256()}",
+        "",
+    ]
+    path = counters_file(wl.name)
+    with open(path, "w") as fh:
+        fh.write("\n".join(rows))
+    print(path)
+
+
+def write_trace_summary(wl, trace_dir):
+    """profiles/<kernel>_<workload>_kernel_trace.md from a rocprofv3
+    --kernel-trace --stats run of this benchmark."""
+    import csv
+    import statistics
+    stats = list(csv.DictReader(open(os.path.join(trace_dir, "run_kernel_stats.csv"))))
+    trace = [r for r in csv.DictReader(open(os.path.join(trace_dir, "run_kernel_trace.csv")))
+             if FUSED_KERNEL in r["Kernel_Name"]]
+    dur = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in trace]
+    starts = [int(r["Start_Timestamp"]) for r in trace]
+    n = len(dur)
+    rows = [
+        f"# Kernel trace: {FUSED_KERNEL}, workload {wl.name}",
+        "",
+        f"Workload: B={wl.B} H={wl.H} grid {wl.h}x{wl.w} (N={wl.N}) d={wl.d} k={wl.k} {wl.dtype}.",
+        "Command (from /tmp with TMPDIR=/tmp, R = repository root):",
+        "",
+        "    " + TRACE_CMD.format(w=wl.name),
+        "    python3 bench.py --workload " + wl.name + " --trace-summary $R/gpurun_out/kt_" + wl.name,
+        "",
+        "The run makes 5 warm-up launches, 50 event-bracketed eager launches, then a graph of",
+        "50 launches replayed twice.",
+        "",
+        "| kernel | calls | average ns | min ns | max ns |",
+        "|---|---|---|---|---|",
+    ]
+    for r in stats[:8]:
+        name = r["Name"]
+        name = name if len(name) < 70 else name[:67] + "..."
+        rows.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | "
+                    f"{r['MaxNs']} |")
+    if n:
+        k = trace[0]
+        rows += [
+            "",
+            f"- {FUSED_KERNEL} launches: {n}; grid {k['Grid_Size_X']} threads, workgroup "
+            f"{k['Workgroup_Size_X']}, VGPR {k['VGPR_Count']}, scratch {k['Scratch_Size']} B",
+            f"- average duration, all launches: {statistics.mean(dur):.2f} us",
+            f"- average duration, graph-replayed launches (last {min(100, n)}): "
+            f"{statistics.mean(dur[-100:]):.2f} us",
+        ]
+        if n > 100:
+            gaps = [(starts[i + 1] - starts[i]) / 1e3 for i in range(n - 100, n - 1)]
+            rows.append(f"- median start-to-start in the graph replays: {statistics.median(gaps):.2f} us")
+    path = os.path.join(PROFILES, f"{FUSED_KERNEL}_{wl.name}_kernel_trace.md")
+    with open(path, "w") as fh:
+        fh.write("\n".join(rows) + "\n")
+    print(path)
 
 
 def algorithmic_bytes(wl) -> int:
@@ -58,10 +232,19 @@ def cpu_baseline(wl, min_seconds=10.0):
         if el >= min_seconds and reps >= 2:
             break
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    cpu = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     tokens = wl.B * wl.H * wl.N * reps
     return {"value": tokens / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{reps} full forwards of the {wl.name} workload (float64 numpy) in "
-                      f"{el:.1f} s on {os.cpu_count()} visible host CPUs ({platform.processor() or platform.machine()})",
+                      f"{el:.1f} s with {threads} BLAS threads on {os.cpu_count()} visible host CPUs ({cpu})",
             "seconds": el}
 
 
@@ -92,7 +275,22 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only plain device copies of known size (for scaling HBM counters)")
+    ap.add_argument("--pmc-summary", nargs=4, metavar="DIR",
+                    help="write the HBM counter summary of --workload from four rocprofv3 --pmc "
+                         "output folders (kernel FETCH_SIZE, kernel WRITE_SIZE, copy FETCH_SIZE, "
+                         "copy WRITE_SIZE) and exit")
+    ap.add_argument("--trace-summary", metavar="DIR",
+                    help="write the kernel-trace summary of --workload from a rocprofv3 "
+                         "--kernel-trace --stats output folder and exit")
     args = ap.parse_args()
+    if args.pmc_summary or args.trace_summary:
+        from efficient_attention_vision_amd import inputs
+        wl = inputs.WORKLOADS[args.workload]
+        if args.pmc_summary:
+            write_counter_summary(wl, *args.pmc_summary)
+        if args.trace_summary:
+            write_trace_summary(wl, args.trace_summary)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
               "(heads are independent: each GPU would run this same forward on its share of B*H)",
@@ -136,7 +334,8 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # eager run: every launch bracketed by events on the launch stream
+    # eager launches, each bracketed by events on the launch stream: the
+    # spread of single-launch latencies (event overhead included)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
     for i in range(args.steps):
@@ -144,12 +343,13 @@ def main():
         step(i)
         evs[i][1].record(stream)
     torch.cuda.synchronize()
-    launch_ms = [a.elapsed_time(b) for a, b in evs]
-    launch_ms_sorted = sorted(launch_ms)
-    kernel_us = 1e3 * sum(launch_ms) / len(launch_ms)
-    kernel_us_median = 1e3 * launch_ms_sorted[len(launch_ms) // 2]
+    eager_us = sorted(1e3 * a.elapsed_time(b) for a, b in evs)
 
-    # graph of exactly K steps, replayed once in the timed region
+    def pct(p):
+        return eager_us[min(len(eager_us) - 1, int(p * len(eager_us)))]
+
+    # graph of exactly K steps; the timed region is one replay of it, with
+    # events recorded on the stream the kernels run on
     g = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream(dev)
     side.wait_stream(stream)
@@ -160,11 +360,15 @@ def main():
     stream.wait_stream(side)
     g.replay()   # warm replay
     torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    e0.record(stream)
     g.replay()
+    e1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = 1e3 * (t1 - t0) / args.steps
+    kernel_us = 1e3 * e0.elapsed_time(e1) / args.steps   # one launch per step
 
     tokens = wl.B * wl.H * wl.N
     value = tokens / (ms_per_step * 1e-3)
@@ -172,12 +376,13 @@ def main():
     aflops = algorithmic_flops(wl)
     achieved_gbs = abytes / (kernel_us * 1e-6) / 1e9
     achieved_tflops = aflops / (kernel_us * 1e-6) / 1e12
+    traffic = measured_traffic(wl.name)
     if wl.k >= 256:
         roof = {"bound": "mfma", "achieved": achieved_tflops, "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": achieved_tflops / BF16_PEAK_TFLOPS, "traffic": None}
+                "unit": "TFLOP/s", "frac": achieved_tflops / BF16_PEAK_TFLOPS, "traffic": traffic}
     else:
         roof = {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": None}
+                "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": traffic}
     line = {
         "metric": "agent-attn fwd tokens/s (B*H*N/s) + achieved HBM GB/s at N=3136,k=49 bf16",
         "value": value,
@@ -195,8 +400,8 @@ def main():
                    "d": wl.d, "agents": wl.k, "agent_grid": [wl.s, wl.s],
                    "supplied_agents": wl.supplied_agents, "rotating_sets": R},
         "roofline": roof,
-        "kernel_us_mean": kernel_us,
-        "kernel_us_median": kernel_us_median,
+        "kernel_us_per_launch": kernel_us,
+        "eager_launch_us": {"median": pct(0.5), "p10": pct(0.1), "p90": pct(0.9)},
         "achieved_hbm_gbs": achieved_gbs,
         "achieved_tflops": achieved_tflops,
         "algorithmic_bytes": abytes,
