@@ -557,19 +557,19 @@ __device__ __forceinline__ void load_q_tile(bf16x8 (&qf)[DC], rsrc_t rq, int tok
 
 // One 16-query tile: S^T = A Q^T over all agents at once, softmax over the
 // agents (lane group reductions), O^T = V_A^T P^T.  VAf: [VSPLIT][KC][DT][64].
+// Broadcast logits and softmax of one 16-token query tile: P2 = softmax over
+// the agents of scale * Q A^T, as bf16 B-operand fragments pf[j] (agent pairs
+// of chunk j, see pair_index) and the reciprocal of the row sum.
 template <class C, int DC, int KTC>
-__device__ __forceinline__ void bcast_tile(const bf16x8 (&qf)[DC], const bf16x8* Af,
-                                           const bf16x8* VAf, rsrc_t ro, int tok0, int tok_end,
-                                           int d, int nag, float sl2) {
-  constexpr int DT = 2 * DC;
-  constexpr int VA_PART = C::KC * DT * 64;
-  const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+__device__ __forceinline__ void bcast_probs(const bf16x8 (&qf)[DC], const bf16x8* Af, int nag,
+                                            float sl2, bf16x8 (&pf)[C::KC], float& inv) {
+  const int lane = threadIdx.x & 63, g = lane >> 4;
   // When the agent and V_A fragments need more than 128 registers they
   // cannot all stay in registers across the caller's tile loop: the LDS
   // index and agent count are then made opaque per tile so that the fragment
   // reads and the padding compares are redone per tile instead of being
   // hoisted (and spilled).
-  constexpr int kFragRegs = 4 * (KTC * DC + C::KC * DT * C::VSPLIT);
+  constexpr int kFragRegs = 4 * (KTC * DC + C::KC * 2 * DC * C::VSPLIT);
   int fl = lane, nag_t = nag;
   if (kFragRegs > 128 || KTC >= 16) {
     asm volatile("" : "+v"(fl));
@@ -595,9 +595,6 @@ __device__ __forceinline__ void bcast_tile(const bf16x8 (&qf)[DC], const bf16x8*
   for (int t = 0; t < KTC; ++t) M = fmaxf(M, fmaxf(fmaxf(S[t][0], S[t][1]), fmaxf(S[t][2], S[t][3])));
   M = group4_max(M);
   const float off = M * sl2;
-  f32x4 O[DT];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) O[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float L = 0.f;
 #pragma unroll
   for (int j = 0; j < C::KC; ++j) {
@@ -608,19 +605,37 @@ __device__ __forceinline__ void bcast_tile(const bf16x8 (&qf)[DC], const bf16x8*
       for (int i = 0; i < 4; ++i)
         pv[4 * h2 + i] = fast_exp2(fmaf(S[2 * j + h2][i], sl2, -off));
     L += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
-    union { bf16x8 v; unsigned w[4]; } pf;
+    union { bf16x8 v; unsigned w[4]; } u;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) pf.w[e] = pack_bf16(pv[2 * e], pv[2 * e + 1]);
+    for (int e = 0; e < 4; ++e) u.w[e] = pack_bf16(pv[2 * e], pv[2 * e + 1]);
+    pf[j] = u.v;
+  }
+  inv = 1.0f / group4_sum(L);
+}
+
+// Broadcast output of one query tile: O = P2 V_A (V_A as bf16 hi + lo when
+// VSPLIT = 2), normalised, rounded to bf16 and stored.
+template <class C, int DC, int KTC>
+__device__ __forceinline__ void bcast_out(const bf16x8 (&pf)[C::KC], float inv, const bf16x8* VAf,
+                                          rsrc_t ro, int tok0, int tok_end, int d) {
+  constexpr int DT = 2 * DC;
+  constexpr int VA_PART = C::KC * DT * 64;
+  const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+  constexpr int kFragRegs = 4 * (KTC * DC + C::KC * DT * C::VSPLIT);
+  int fl = lane;
+  if (kFragRegs > 128 || KTC >= 16) asm volatile("" : "+v"(fl));
+  f32x4 O[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) O[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < C::KC; ++j)
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       const int f = (j * DT + dt) * 64 + fl;
-      O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(VAf[f], pf.v, O[dt], 0, 0, 0);
+      O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(VAf[f], pf[j], O[dt], 0, 0, 0);
       if (C::VSPLIT > 1)
-        O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(VAf[VA_PART + f], pf.v, O[dt], 0, 0, 0);
+        O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(VAf[VA_PART + f], pf[j], O[dt], 0, 0, 0);
     }
-  }
-  L = group4_sum(L);
-  const float inv = 1.0f / L;
   const int tok = tok0 + r;
   // Lane (r, g) holds channels 16 dt + 4 g .. +3 of token r for every dt.
   // Two 2 x 2 transposes between lane groups (permlane32_swap exchanges
@@ -651,6 +666,16 @@ __device__ __forceinline__ void bcast_tile(const bf16x8 (&qf)[DC], const bf16x8*
       const unsigned off2 = (tok < tok_end && c0 < d) ? (unsigned)((tok * d + c0) * 2) : kOOB;
       bst16<kStream>(ro, off2, uint4{pk[d0][0], pk[d0][1], pk[d1][0], pk[d1][1]});
     }
+}
+
+template <class C, int DC, int KTC>
+__device__ __forceinline__ void bcast_tile(const bf16x8 (&qf)[DC], const bf16x8* Af,
+                                           const bf16x8* VAf, rsrc_t ro, int tok0, int tok_end,
+                                           int d, int nag, float sl2) {
+  bf16x8 pf[C::KC];
+  float inv;
+  bcast_probs<C, DC, KTC>(qf, Af, nag, sl2, pf, inv);
+  bcast_out<C, DC, KTC>(pf, inv, VAf, ro, tok0, tok_end, d);
 }
 
 // ------------------------------------------------------------- the kernel
@@ -732,6 +757,14 @@ agent_mfma_kernel(MfmaParams p) {
   const int nqt = n1 > n0 ? (n1 - n0 + 15) / 16 : 0;
   bf16x8 qcur[DC];
   bool staged0 = false;   // first round already in LDS
+  // With up to 64 agents, the broadcast probabilities of up to kEarly tiles
+  // per wave are computed while the group gathers at barrier 1 (they need
+  // only A and Q); only P2 V_A is left after V_A arrives.
+  constexpr int kEarly = KTC <= 4 ? 2 : 1;
+  bf16x8 epf[kEarly][C::KC];
+  bf16x8 qe[kEarly][DC];
+  float einv[kEarly];
+  bool early = false;
   if ((p.phases & PH_BCAST) && !(p.phases & PH_AGG)) load_q_tile<DC>(qcur, rq, n0 + 16 * wave, n1, d);
   AA_STAMP(1);
 
@@ -961,8 +994,17 @@ agent_mfma_kernel(MfmaParams p) {
     AA_STAMP(6);
     if (sync_group && ok) {
       group_arrive(gs, 1);
-      // the query tile loads travel while the group gathers
-      if (p.phases & PH_BCAST) load_q_tile<DC>(qcur, rq, n0 + 16 * wave, n1, d);
+      early = KTC <= 4 && (p.phases & PH_BCAST) && (p.phases & PH_MERGE) &&
+              nqt <= kEarly * kWaves;
+      if (early) {
+        // query tiles of the early probabilities (computed during the merge)
+#pragma unroll
+        for (int i = 0; i < kEarly; ++i)
+          load_q_tile<DC>(qe[i], rq, n0 + 16 * (wave + kWaves * i), n1, d);
+      } else if (p.phases & PH_BCAST) {
+        // the query tile loads travel while the group gathers
+        load_q_tile<DC>(qcur, rq, n0 + 16 * wave, n1, d);
+      }
       ok = group_wait(gs, 1);
     } else if (sync_group && (p.phases & PH_BCAST)) {
       load_q_tile<DC>(qcur, rq, n0 + 16 * wave, n1, d);
@@ -978,9 +1020,21 @@ agent_mfma_kernel(MfmaParams p) {
     const rsrc_t racc = rsrc_of(p.part_acc + hbase * DT * 256, (unsigned)(p.P * KTC * DT * 1024));
     const rsrc_t rml = rsrc_of(p.part_ml + hbase * 32, (unsigned)(p.P * KTC * 128));
     const rsrc_t rvo = rsrc_of(p.values_f32 + ahb, arow_bytes);
+    // Waves without merge items compute their broadcast probabilities now;
+    // the merging waves do so between arriving at barrier 2 and waiting.
+    // merge items run on the last waves, which hold the fewest query tiles
+    const int mtid = kThreads - 1 - tid;
+    const bool merge_wave = (kWaves - 1 - wave) * 64 < items;
+    auto early_probs = [&]() {
+#pragma unroll
+      for (int i = 0; i < kEarly; ++i)
+        if (wave + kWaves * i < nqt)
+          bcast_probs<C, DC, KTC>(qe[i], Af, p.nag, p.sl2, epf[i], einv[i]);
+    };
+    if (early && !merge_wave) early_probs();
     with_pol(xp, [&](auto pc) {
     constexpr int POL = decltype(pc)::value;
-    for (int it = tid; it < items; it += kThreads) {
+    for (int it = mtid; it < items; it += kThreads) {
       const int m = it / nq, q = it - m * nq;
       const int a = slot + p.P * m;
       const int t = a >> 4, r = a & 15, dt = q >> 2, g = q & 3;
@@ -1029,7 +1083,13 @@ agent_mfma_kernel(MfmaParams p) {
     }
     });
     AA_STAMP(8);
-    if (sync_group && ok) ok = group_barrier(gs, 2);
+    if (sync_group && ok) {
+      group_arrive(gs, 2);
+      if (early && merge_wave) early_probs();
+      ok = group_wait(gs, 2);
+    } else if (early && merge_wave) {
+      early_probs();
+    }
     AA_STAMP(9);
   }
 
@@ -1075,6 +1135,13 @@ agent_mfma_kernel(MfmaParams p) {
     __syncthreads();
     AA_STAMP(10);
     const rsrc_t ro = rsrc_of(p.out + hoff, head_bytes);
+    if (early) {
+#pragma unroll
+      for (int i = 0; i < kEarly; ++i) {
+        const int qt = wave + kWaves * i;
+        if (qt < nqt) bcast_out<C, DC, KTC>(epf[i], einv[i], VAf, ro, n0 + 16 * qt, n1, d);
+      }
+    } else
     for (int qt = wave; qt < nqt; qt += kWaves) {
       bf16x8 qnext[DC];
       load_q_tile<DC>(qnext, rq, n0 + 16 * (qt + kWaves), n1, d);   // zeros past the end
