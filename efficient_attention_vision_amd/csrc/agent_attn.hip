@@ -3,6 +3,7 @@
 // caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -337,12 +338,19 @@ Plan make_plan(const Dims& D, int cus) {
     P.xcd_heads = (P.P > 1 && D.BH % 8 == 0 && cus % 8 == 0) ? (int)(D.BH / 8) : 0;
     part_bytes = 0;  // set with the fragment regions below
   }
-  const size_t ad = (size_t)D.BH * D.nag * D.d * sizeof(float);
+  // A and V_A regions: fp32 rows, or in the fused path the bf16 MFMA
+  // fragment sets that the group exchanges (whichever is larger)
+  size_t a_bytes = (size_t)D.BH * D.nag * D.d * sizeof(float), va_bytes = a_bytes;
+  if (D.dtype != AGENT_ATTN_F32) {
+    const int ktc = mfma_ktc(D.nag);
+    a_bytes = std::max(a_bytes, (size_t)D.BH * aa::a_frag_bytes(ktc, P.DC));
+    va_bytes = std::max(va_bytes, (size_t)D.BH * aa::va_frag_bytes(ktc, P.DC));
+  }
   P.off_sync = 0;
   P.off_status = kSyncRegionBytes;
   P.off_A = P.off_status + 256;
-  P.off_VA = align_up(P.off_A + ad, 256);
-  P.off_part = align_up(P.off_VA + ad, 256);
+  P.off_VA = align_up(P.off_A + a_bytes, 256);
+  P.off_part = align_up(P.off_VA + va_bytes, 256);
   if (D.dtype != AGENT_ATTN_F32) {
     P.off_ml = P.off_part;
     P.off_part = align_up(P.off_ml + mfma_ml_bytes(D, P.P, P.DC), 256);

@@ -355,6 +355,13 @@ __device__ __forceinline__ void transpose8x8(const uint4 (&x)[8], uint4 (&y)[8])
 // ------------------------------------------------------------ configuration
 // Compile-time shape of one kernel instance: DC 32-channel chunks of the head
 // dimension (DPAD = 32*DC >= d), KTC 16-agent tiles (16*KTC >= agents).
+// V_A enters the broadcast products as bf16 hi + lo when there are at most
+// 64 agents (registers allow it), as bf16 alone otherwise.
+constexpr int vsplit_of(int ktc) { return ktc <= 4 ? 2 : 1; }
+// Bytes per head of the agent and V_A fragment sets (bf16x8 per lane).
+constexpr long a_frag_bytes(int ktc, int dc) { return (long)ktc * dc * 1024; }
+constexpr long va_frag_bytes(int ktc, int dc) { return (long)vsplit_of(ktc) * (ktc / 2) * (2 * dc) * 1024; }
+
 template <int DC, int KTC>
 struct Cfg {
   static constexpr int DT = 2 * DC;                // 16-channel output tiles
@@ -364,7 +371,7 @@ struct Cfg {
   static constexpr int ATW = KTC / AG;             // agent tiles per wave
   static constexpr int TG = kWaves / AG;           // token groups of waves
   static constexpr int KC = (KTC + 1) / 2;         // 32-agent chunks
-  static constexpr int VSPLIT = KTC <= 4 ? 2 : 1;  // V_A as bf16 hi + lo
+  static constexpr int VSPLIT = vsplit_of(KTC);    // V_A as bf16 hi + lo
   // LDS layout: [A fragments][big], big = union of
   //   pooling sums | {V^T, K rows} of a round | cross-wave partials |
   //   {V_A staging rows (if they fit), V_A fragments}
@@ -809,6 +816,16 @@ agent_mfma_kernel(MfmaParams p) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) fr.u[e] = pack_bf16(s8[2 * e], s8[2 * e + 1]);
           Af[(t16 * DC + cc) * 64 + 16 * g + r] = fr.v;
+        } else if (sync_group) {
+          // the group exchanges A as bf16 MFMA fragments: one 16-byte
+          // fragment per (agent, 8-channel chunk)
+          const int t16 = a >> 4, r = a & 15, g = c / DC, cc = c - g * DC;
+          union { uint4 v; unsigned u[4]; } fr;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) fr.u[e] = pack_bf16(s8[2 * e], s8[2 * e + 1]);
+          const rsrc_t rf = rsrc_of(reinterpret_cast<char*>(p.agents_f32) + head * C::A_BYTES,
+                                    C::A_BYTES);
+          xst16(xp, rf, (unsigned)(((t16 * DC + cc) * 64 + 16 * g + r) * 16), fr.v);
         } else {
           const rsrc_t ra = rsrc_of(p.agents_f32 + ahb, arow_bytes);
           const unsigned off = (unsigned)((a * d + 8 * c) * 4);
@@ -834,7 +851,19 @@ agent_mfma_kernel(MfmaParams p) {
   }
 
   // ---- agents -> LDS fragments (zero for padding agents and channels)
-  if ((p.phases & (PH_AGG | PH_BCAST)) && !(single && (p.phases & PH_POOL))) {
+  if (sync_group && !p.agents_in && (p.phases & PH_POOL)) {
+    // fragments exchanged by the pooling workgroups (padding ones read zero)
+    const rsrc_t rf = rsrc_of(reinterpret_cast<char*>(p.agents_f32) + head * C::A_BYTES, C::A_BYTES);
+#pragma unroll
+    for (int f0 = 0; f0 < A_FRAGS; f0 += kThreads) {
+      const int f = f0 + tid;
+      const int fl = f & 63, c = (f >> 6) % DC, t = (f >> 6) / DC;
+      const int agent = 16 * t + (fl & 15), ch0 = 8 * (DC * (fl >> 4) + c);
+      const bool in = f < A_FRAGS && agent < p.nag && ch0 < d;
+      const uint4 x = bld16<kCoherent>(rf, in ? (unsigned)(f * 16) : kOOB);
+      if (f < A_FRAGS) Af[f] = __builtin_bit_cast(bf16x8, x);
+    }
+  } else if ((p.phases & (PH_AGG | PH_BCAST)) && !(single && (p.phases & PH_POOL))) {
     const bool from_rows = !p.agents_in;
     const float* rows = p.agents_f32_in ? p.agents_f32_in : p.agents_f32;
     const rsrc_t ra = from_rows ? rsrc_of(rows + ahb, arow_bytes)
@@ -981,12 +1010,15 @@ agent_mfma_kernel(MfmaParams p) {
         const int t = ATW * ag + a;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          const unsigned off = (unsigned)(((t * DT + dt) * 64 + lane) * 16);
+          // rows of padding agents are never merged: not stored
+          const bool real = 16 * t + (lane & 15) < p.nag;
+          const unsigned off = real ? (unsigned)(((t * DT + dt) * 64 + lane) * 16) : kOOB;
           const uint4 x = f4_bits(float4{st.acc[a][dt][0], st.acc[a][dt][1], st.acc[a][dt][2],
                                          st.acc[a][dt][3]});
           xst16(xp, racc, off, x);
         }
-        const unsigned moff = g == 0 ? (unsigned)((t * 16 + (lane & 15)) * 8) : kOOB;
+        const unsigned moff = (g == 0 && 16 * t + (lane & 15) < p.nag)
+                                  ? (unsigned)((t * 16 + (lane & 15)) * 8) : kOOB;
         const uint2 ml = uint2{__float_as_uint(st.m[a]), __float_as_uint(st.l[a])};
         xst8(xp, rml, moff, ml);
       }
@@ -1077,9 +1109,36 @@ agent_mfma_kernel(MfmaParams p) {
       }
       const float inv = 1.0f / Ls;
       const int ch = 16 * dt + 4 * g;
-      const unsigned off = (a < p.nag && ch < d) ? (unsigned)((a * d + ch) * 4) : kOOB;
-      const uint4 x = f4_bits(float4{acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv});
-      bst16<POL>(rvo, off, x);
+      if (sync_group) {
+        // V_A goes to the group as bf16 fragments (hi, and lo when VSPLIT
+        // = 2) at the positions bcast_out reads: agent a is element e of
+        // lane group gg in chunk j, channel ch+i is lane row (ch+i) % 16
+        const float v4[4] = {acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv};
+        const rsrc_t rvf = rsrc_of(reinterpret_cast<char*>(p.values_f32) + head * C::VA_BYTES,
+                                   C::VA_BYTES);
+        const int u = a & 31, j = a >> 5;
+        const int gg = (u & 15) >> 2, e = (u & 3) + (u >= 16 ? 4 : 0);
+        const bool keep = a < p.nag && ch < d;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int c = ch + i;
+          const int f = (j * DT + (c >> 4)) * 64 + 16 * gg + (c & 15);
+          const bf16_t hi = bf16_bits(v4[i]);
+          const unsigned off = keep ? (unsigned)((f * 8 + e) * 2) : kOOB;
+          if (xp == kXL2) __builtin_amdgcn_raw_buffer_store_b16(hi, rvf, (int)off, 0, kL2);
+          else __builtin_amdgcn_raw_buffer_store_b16(hi, rvf, (int)off, 0, kCoherent);
+          if (C::VSPLIT > 1) {
+            const bf16_t lo = bf16_bits(v4[i] - bf16_value(hi));
+            const unsigned offl = keep ? (unsigned)(((VA_FRAGS + f) * 8 + e) * 2) : kOOB;
+            if (xp == kXL2) __builtin_amdgcn_raw_buffer_store_b16(lo, rvf, (int)offl, 0, kL2);
+            else __builtin_amdgcn_raw_buffer_store_b16(lo, rvf, (int)offl, 0, kCoherent);
+          }
+        }
+      } else {
+        const unsigned off = (a < p.nag && ch < d) ? (unsigned)((a * d + ch) * 4) : kOOB;
+        const uint4 x = f4_bits(float4{acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv});
+        bst16<POL>(rvo, off, x);
+      }
     }
     });
     AA_STAMP(8);
@@ -1101,6 +1160,28 @@ agent_mfma_kernel(MfmaParams p) {
     const float* rows = p.values_f32_in ? p.values_f32_in : p.values_f32;
     const rsrc_t rvr = rsrc_of(rows + ahb, arow_bytes);
     __syncthreads();
+    if (sync_group && (p.phases & PH_MERGE)) {
+      // fragments written by the merging workgroups; elements of padding
+      // agents were never written and are cleared here
+      const rsrc_t rvf = rsrc_of(reinterpret_cast<char*>(p.values_f32) + head * C::VA_BYTES,
+                                 C::VA_BYTES);
+#pragma unroll
+      for (int f0 = 0; f0 < VA_FRAGS * C::VSPLIT; f0 += kThreads) {
+        const int f = f0 + tid;
+        const int fh = f % VA_FRAGS;
+        const int fl = fh & 63, dt = (fh >> 6) % DT, j = (fh >> 6) / DT;
+        const int ch = 16 * dt + (fl & 15), g = fl >> 4;
+        const bool in = f < VA_FRAGS * C::VSPLIT && ch < d;
+        union { uint4 v; unsigned w[4]; } x;
+        x.v = bld16<kCoherent>(rvf, in ? (unsigned)(f * 16) : kOOB);
+        if (32 * j + 32 > p.nag) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (pair_index(j, g, e) >= p.nag) x.w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+        }
+        if (f < VA_FRAGS * C::VSPLIT) VAf[f] = __builtin_bit_cast(bf16x8, x.v);
+      }
+    } else {
     with_pol(xp, [&](auto pc) {
     constexpr int POL = decltype(pc)::value;
 #pragma unroll
@@ -1132,6 +1213,7 @@ agent_mfma_kernel(MfmaParams p) {
       }
     }
     });
+    }
     __syncthreads();
     AA_STAMP(10);
     const rsrc_t ro = rsrc_of(p.out + hoff, head_bytes);
