@@ -76,7 +76,7 @@ struct MfmaParams {
   const float* values_f32_in;   // V_A [BH, nag, d] fp32 (step calls) or null
   float* agents_f32;            // agents [BH, nag, d] (exchange, or step output)
   float* values_f32;            // V_A [BH, nag, d] (exchange, staging, or step output)
-  float* part_acc;              // partials [BH][P][KT][DT][64][4]
+  float* part_acc;              // partials [BH][P] x (KT*16 x DPAD), see Cfg::ROW_PARTIALS
   float* part_ml;               // partial max and sum [BH][P][KT][16][2]
   unsigned* sync;               // group counters, zero between launches
   int* status;                  // fault word (kFault* bits)
@@ -100,9 +100,17 @@ struct MfmaParams {
     if (p.trace && threadIdx.x == 0)                                           \
       p.trace[(long)blockIdx.x * 16 + (i)] = (long long)wall_clock64();        \
   } while (0)
+#define AA_STAMP_BY(i, thread)                                                 \
+  do {                                                                         \
+    if (p.trace && threadIdx.x == (thread))                                    \
+      p.trace[(long)blockIdx.x * 16 + (i)] = (long long)wall_clock64();        \
+  } while (0)
 #else
 #define AA_STAMP(i) \
   do {              \
+  } while (0)
+#define AA_STAMP_BY(i, thread) \
+  do {                         \
   } while (0)
 #endif
 
@@ -372,6 +380,10 @@ struct Cfg {
   static constexpr int TG = kWaves / AG;           // token groups of waves
   static constexpr int KC = (KTC + 1) / 2;         // 32-agent chunks
   static constexpr int VSPLIT = vsplit_of(KTC);    // V_A as bf16 hi + lo
+  // Partial accumulators as agent rows (coalesced merge reads; measured
+  // faster from 128 agents) or in register order (up to 64 agents, where
+  // the row addressing costs the kernel more registers than it saves).
+  static constexpr bool ROW_PARTIALS = KTC >= 8;
   // LDS layout: [A fragments][big], big = union of
   //   pooling sums | {V^T, K rows} of a round | cross-wave partials |
   //   {V_A staging rows (if they fit), V_A fragments}
@@ -733,9 +745,7 @@ agent_mfma_kernel(MfmaParams p) {
   if (xp == kXL2 && tid == 0 && xcc_id() != (int)(blockIdx.x & 7))
     __hip_atomic_fetch_or(reinterpret_cast<unsigned*>(p.status), kFaultXcd, __ATOMIC_RELAXED,
                           __HIP_MEMORY_SCOPE_AGENT);
-#ifdef AGENT_ATTN_PHASE_TRACE
-  if (p.trace && tid == 0) p.trace[(long)blockIdx.x * 16 + 14] = xp * 100 + xcc_id();
-#endif
+
   const rsrc_t rq = rsrc_of(p.q + hoff, head_bytes);
   const rsrc_t rk = rsrc_of(p.k + hoff, head_bytes);
   const rsrc_t rv = rsrc_of(p.v + hoff, head_bytes);
@@ -1001,7 +1011,8 @@ agent_mfma_kernel(MfmaParams p) {
         }
       }
     } else if (tg == 0) {
-      // partials in register order: one contiguous 1 KiB row per (tile, dt)
+      // partials: agent rows of DPAD channels (the merge reads whole rows)
+      // or, with up to 64 agents, register order (1 KiB per tile and dt)
       const long pbase = ((long)head * p.P + slot) * KTC;
       const rsrc_t racc = rsrc_of(p.part_acc + pbase * DT * 256, (unsigned)(KTC * DT * 1024));
       const rsrc_t rml = rsrc_of(p.part_ml + pbase * 32, (unsigned)(KTC * 128));
@@ -1012,7 +1023,10 @@ agent_mfma_kernel(MfmaParams p) {
         for (int dt = 0; dt < DT; ++dt) {
           // rows of padding agents are never merged: not stored
           const bool real = 16 * t + (lane & 15) < p.nag;
-          const unsigned off = real ? (unsigned)(((t * DT + dt) * 64 + lane) * 16) : kOOB;
+          const unsigned off =
+              !real ? kOOB
+              : C::ROW_PARTIALS ? (unsigned)(((16 * t + (lane & 15)) * DPAD + 16 * dt + 4 * g) * 4)
+                                : (unsigned)(((t * DT + dt) * 64 + lane) * 16);
           const uint4 x = f4_bits(float4{st.acc[a][dt][0], st.acc[a][dt][1], st.acc[a][dt][2],
                                          st.acc[a][dt][3]});
           xst16(xp, racc, off, x);
@@ -1064,13 +1078,15 @@ agent_mfma_kernel(MfmaParams p) {
           bcast_probs<C, DC, KTC>(qe[i], Af, p.nag, p.sl2, epf[i], einv[i]);
     };
     if (early && !merge_wave) early_probs();
+    AA_STAMP_BY(15, 0);
     with_pol(xp, [&](auto pc) {
     constexpr int POL = decltype(pc)::value;
     for (int it = mtid; it < items; it += kThreads) {
       const int m = it / nq, q = it - m * nq;
       const int a = slot + p.P * m;
       const int t = a >> 4, r = a & 15, dt = q >> 2, g = q & 3;
-      const unsigned aoff = (unsigned)(((t * DT + dt) * 64 + 16 * g + r) * 16);
+      const unsigned aoff = C::ROW_PARTIALS ? (unsigned)((a * DPAD + 4 * q) * 4)
+                                            : (unsigned)(((t * DT + dt) * 64 + 16 * g + r) * 16);
       const unsigned moff = (unsigned)((t * 16 + r) * 8);
       constexpr unsigned sstride_acc = KTC * DT * 1024, sstride_ml = KTC * 128;
       float M = -INFINITY, Ls = 0.f;
@@ -1141,6 +1157,7 @@ agent_mfma_kernel(MfmaParams p) {
       }
     }
     });
+    AA_STAMP_BY(14, kThreads - 1);
     AA_STAMP(8);
     if (sync_group && ok) {
       group_arrive(gs, 2);
