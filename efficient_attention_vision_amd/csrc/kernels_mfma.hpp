@@ -537,26 +537,34 @@ __device__ __forceinline__ void agg_block(AggState<DC, ATW>& st, const bf16_t* K
     float bm = fmaxf(fmaxf(fmaxf(S0[0], S0[1]), fmaxf(S0[2], S0[3])),
                      fmaxf(fmaxf(S1[0], S1[1]), fmaxf(S1[2], S1[3])));
     bm = group4_max(bm);
-    const float mn = fmaxf(st.m[a], bm);
-    const float corr = fast_exp2((st.m[a] - mn) * sl2);
-    const float off = mn * sl2;
+    // Lazy rescaling: the reference max m of a row moves (and the running
+    // sum and accumulators are rescaled) only when a block's max exceeds it
+    // by more than 8 in the log2 domain, so probabilities stay below 2^8:
+    // exact in the fp32 sums, and no loss in bf16, whose precision is
+    // relative.  The first block always sets m (m starts at -inf).
+    const bool grow = (bm - st.m[a]) * sl2 > 8.f;
+    if (__any(grow)) {
+      const float mn = grow ? bm : st.m[a];
+      const float corr = grow ? fast_exp2((st.m[a] - mn) * sl2) : 1.f;
+      st.l[a] *= corr;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) st.acc[a][dt] *= corr;
+      st.m[a] = mn;
+    }
+    const float off = st.m[a] * sl2;
     float pv[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       pv[i] = fast_exp2(fmaf(S0[i], sl2, -off));
       pv[4 + i] = fast_exp2(fmaf(S1[i], sl2, -off));
     }
-    st.l[a] = fmaf(st.l[a], corr,
-                   ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7])));
-    st.m[a] = mn;
+    st.l[a] += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
     union { bf16x8 v; unsigned w[4]; } pf;
 #pragma unroll
     for (int e = 0; e < 4; ++e) pf.w[e] = pack_bf16(pv[2 * e], pv[2 * e + 1]);
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      st.acc[a][dt] *= corr;
+    for (int dt = 0; dt < DT; ++dt)
       st.acc[a][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], pf.v, st.acc[a][dt], 0, 0, 0);
-    }
   }
 }
 
