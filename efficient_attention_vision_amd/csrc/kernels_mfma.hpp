@@ -773,11 +773,15 @@ agent_mfma_kernel(MfmaParams p) {
   const int r0cnt = n1 > n0 ? min(RT, n1 - n0) : 0;
   const int r0tiles = ((r0cnt + 31) / 32 * 4) * DCH;
   uint4 kx[8], vx[8];
-  if (p.phases & PH_AGG) {
+  // Without pooling they are issued now; with pooling, once the pooling's
+  // query loads have landed, so that they do not delay the pooling and
+  // arrive during the pooling, barrier 0 and the agent fragments.
+  auto load_kv0 = [&]() {
     const int tend = tid < r0tiles ? n0 + r0cnt : -1;
     load_tile8(kx, rk, tid, n0, tend, d);
     load_tile8(vx, rv, tid, n0, tend, d);
-  }
+  };
+  if ((p.phases & PH_AGG) && !(p.phases & PH_POOL)) load_kv0();
   // first query tile of this wave, loaded ahead of the broadcast
   const int nqt = n1 > n0 ? (n1 - n0 + 15) / 16 : 0;
   bf16x8 qcur[DC];
@@ -806,6 +810,7 @@ agent_mfma_kernel(MfmaParams p) {
       for (int ps = 0; ps < pool_npass; ++ps) {
         if (b0 > 0 || ps > 0) pool_issue(p, rq, slot, b0 + tid, pool_items, ps * pool_chunk, px);
         pool_accum(px, acc8);
+        if (b0 == 0 && ps == 0 && (p.phases & PH_AGG)) load_kv0();
       }
       __syncthreads();   // red free
       *reinterpret_cast<float4*>(red + tid * 8) = float4{acc8[0], acc8[1], acc8[2], acc8[3]};
@@ -854,6 +859,7 @@ agent_mfma_kernel(MfmaParams p) {
         }
       }
     }
+    if (pool_items == 0 && (p.phases & PH_AGG)) load_kv0();
     AA_STAMP(2);
     if (sync_group) {
       group_arrive(gs, 0);
