@@ -34,6 +34,7 @@ _SIGNATURES = {
                                                                  _vp]),
     "agent_attn_broadcast": (_c_int, [_vp] * 4 + [_c_int] * 5 + [_c_float, _c_int, _vp]),
     "agent_attn_read_faults": (_c_int, [_vp, _vp, ctypes.POINTER(_c_int)]),
+    "agent_attn_set_wait_limit": (ctypes.c_long, [ctypes.c_long]),
     "agent_attn_release": (None, []),
     "agent_attn_status_string": (ctypes.c_char_p, [_c_int]),
     "agent_attn_last_error": (ctypes.c_char_p, []),
@@ -295,6 +296,12 @@ def agent_attn_read_faults(workspace=None, device=None) -> int:
             _check(L.agent_attn_read_faults(_ptr(t), _stream(device), ctypes.byref(f)))
             word |= f.value
     return word
+
+
+def agent_attn_set_wait_limit(polls: int) -> int:
+    """Polls at a group barrier before a workgroup gives up (negative: only
+    query); returns the previous value."""
+    return int(lib().agent_attn_set_wait_limit(int(polls)))
 
 
 def agent_attn_release() -> None:

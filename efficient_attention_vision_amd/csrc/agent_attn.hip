@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -425,6 +426,7 @@ int launch_broadcast(const Dims& D, const void* q, const float* A, const float* 
 #ifdef AGENT_ATTN_PHASE_TRACE
 long long* g_trace = nullptr;  // profiling builds: per-workgroup phase stamps
 #endif
+std::atomic<long> g_spin_limit{aa::kSpinLimit};   // polls before a group wait gives up
 
 int launch_mfma(int DC, const aa::MfmaParams& mp, long grid, int nag, hipStream_t st) {
   const int ktc = mfma_ktc(nag);
@@ -440,6 +442,7 @@ int launch_mfma(int DC, const aa::MfmaParams& mp, long grid, int nag, hipStream_
 
 aa::MfmaParams mfma_params(const Dims& D, int P, int T, float scale) {
   aa::MfmaParams mp{};
+  mp.spin_limit = g_spin_limit.load();
   mp.BH = (int)D.BH;
   mp.N = (int)D.N;
   mp.h = D.h;
@@ -746,6 +749,12 @@ int agent_attn_broadcast(const void* q, const float* agents_f32, const float* ag
   mp.agents_f32_in = agents_f32;
   mp.values_f32_in = agent_values_f32;
   return run_mfma_phases(D, mp, mfma_dc(D.d), aa::PH_BCAST, false, st);
+}
+
+long agent_attn_set_wait_limit(long polls) {
+  const long prev = g_spin_limit.load();
+  if (polls >= 0) g_spin_limit.store(polls);
+  return prev;
 }
 
 int agent_attn_read_faults(void* workspace, void* stream, int* faults) {

@@ -89,6 +89,7 @@ struct MfmaParams {
   int phases;
   int fused;
   int xcd_heads;                // >0: heads per XCD for the XCD-aware mapping
+  long spin_limit;              // polls before a group wait gives up (kSpinLimit)
   long long* trace;             // phase timestamps (trace builds only)
 };
 
@@ -248,6 +249,7 @@ struct GroupSync {
   int slot, P;
   bool flags;      // flag barrier (group on one XCD)
   int* status;
+  long spin_limit; // polls before a wait gives up
 };
 __device__ __forceinline__ void group_arrive(const GroupSync& g, int k) {
   __builtin_amdgcn_s_waitcnt(0);
@@ -282,7 +284,7 @@ __device__ __forceinline__ bool group_wait(const GroupSync& g, int k) {
         const unsigned lo = (w | 0x80808080u) - want;
         const bool arrived = ((~w & 0x80808080u) & ~lo) == 0u;
         if (__all(arrived)) break;
-        if (++spins > kSpinLimit) {
+        if (++spins > g.spin_limit) {
           good = false;
           if (lane == 0)
             __hip_atomic_fetch_or(reinterpret_cast<unsigned*>(g.status), kFaultBarrier,
@@ -298,7 +300,7 @@ __device__ __forceinline__ bool group_wait(const GroupSync& g, int k) {
     long spins = 0;
     unsigned* c = g.blk + kCtrDword + k * kCtrStride;
     while (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (unsigned)g.P) {
-      if (++spins > kSpinLimit) {
+      if (++spins > g.spin_limit) {
         ok = 0;
         __hip_atomic_fetch_or(reinterpret_cast<unsigned*>(g.status), kFaultBarrier,
                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -743,7 +745,7 @@ agent_mfma_kernel(MfmaParams p) {
   const int n1 = min(p.N, n0 + p.T);
   const long hoff = (long)head * p.N * d;
   const unsigned head_bytes = (unsigned)(p.N * d * 2);
-  GroupSync gs{p.sync + (long)head * kSyncDwords, slot, p.P, false, p.status};
+  GroupSync gs{p.sync + (long)head * kSyncDwords, slot, p.P, false, p.status, p.spin_limit};
   const bool sync_group = p.fused && p.P > 1;
   const bool single = p.fused && p.P == 1;   // whole head in this workgroup
   const int xp = sync_group ? (p.xcd_heads > 0 ? kXL2 : kXDevice) : kXNone;

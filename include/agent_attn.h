@@ -144,6 +144,14 @@ int agent_attn_broadcast(const void* q, const float* agents_f32,
  * faults is NULL, AGENT_ATTN_ERR_HIP when a HIP call fails. */
 int agent_attn_read_faults(void* workspace, void* stream, int* faults);
 
+/* Sets how many times a workgroup polls at a group barrier before it gives
+ * up (default 1 << 20 polls, about a second) and returns the previous value;
+ * a negative argument only returns it.  Applies to forwards enqueued
+ * afterwards by this process.  A launch whose wait gives up sets
+ * AGENT_ATTN_FAULT_BARRIER in its fault word and ends normally, so a small
+ * value makes that path testable from the host. */
+long agent_attn_set_wait_limit(long polls);
+
 /* Frees the library's cached per-device scratch buffers. */
 void agent_attn_release(void);
 

@@ -121,3 +121,11 @@ def test_python_binding_rejects_cpu_tensors():
 
 def test_read_faults_needs_an_output(L):
     assert L.agent_attn_read_faults(WS, None, None) == ERR_NULL
+
+
+def test_wait_limit_query_and_set(L):
+    prev = L.agent_attn_set_wait_limit(-1)
+    assert prev > 0
+    assert L.agent_attn_set_wait_limit(123) == prev
+    assert L.agent_attn_set_wait_limit(prev) == 123
+    assert L.agent_attn_set_wait_limit(-1) == prev

@@ -194,3 +194,29 @@ def test_shared_workspace_across_shapes():
            inputs.WORKLOADS["sd_unet"], inputs.WORKLOADS["pvt_stage1"]]
     for i, wl in enumerate(seq):
         run_case(wl, 20 + i, "discriminating")
+
+
+def test_barrier_timeout_is_reported_and_recovers():
+    """With the barrier wait limit forced to zero from the host, a grouped
+    forward gives up at a barrier, ends normally and reports
+    AGENT_ATTN_FAULT_BARRIER; the next forward with the default limit is
+    correct again (the group state was cleared)."""
+    from efficient_attention_vision_amd import _binding
+    wl = inputs.WORKLOADS["pvt_stage1"]
+    inp = inputs.make_inputs(wl, 7, "discriminating")
+    q, k, v = (to_device(x) for x in (inp.Q, inp.K, inp.V))
+    assert eav.agent_attn_read_faults() == 0
+    prev = eav.agent_attn_set_wait_limit(0)
+    try:
+        say("[timeout] forward with a zero wait limit")
+        eav.agent_attn_forward(q, k, v, (wl.h, wl.w), wl.s, wl.scale)
+        faults = eav.agent_attn_read_faults()
+    finally:
+        eav.agent_attn_set_wait_limit(prev)
+    assert faults & _binding.FAULT_BARRIER, faults
+    assert eav.agent_attn_set_wait_limit(-1) == prev
+    say("[timeout] forward with the default limit")
+    out = eav.agent_attn_forward(q, k, v, (wl.h, wl.w), wl.s, wl.scale)
+    assert eav.agent_attn_read_faults() == 0
+    O, _, _ = oracle.forward(inp.Q.exact, inp.K.exact, inp.V.exact, wl.h, wl.w, wl.s, wl.scale)
+    parity.assert_close(to_host_f64(out), O, wl.dtype, "after timeout", kind="discriminating")
