@@ -70,6 +70,13 @@ EDGE = [
     # long thin grid and a long sequence
     inputs.custom("thin_2x300", B=1, H=2, h=2, w=300, d=64, s=2),
     inputs.custom("long_96x96", B=1, H=2, h=96, w=96, d=64, s=12),
+    # grouping regimes: two workgroups per head on one XCD (B*H = 128), two
+    # per head across XCDs (B*H = 100), one per head just above the CU count
+    inputs.custom("bh128_p2", B=16, H=8, h=24, w=24, d=64, s=6),
+    inputs.custom("bh100_p2", B=25, H=4, h=20, w=20, d=32, s=5),
+    inputs.custom("bh260_p1", B=26, H=10, h=8, w=8, d=64, s=4),
+    # a long sequence: 256 x 256 grid, 256 agents
+    inputs.custom("long_256x256", B=1, H=2, h=256, w=256, d=64, s=16),
     # caller-supplied agents with ragged counts
     inputs.custom("supplied_s3", B=2, H=2, h=10, w=10, d=64, s=3, supplied_agents=True),
     inputs.custom("supplied_f32", B=1, H=2, h=10, w=12, d=48, s=2, dtype="f32",
