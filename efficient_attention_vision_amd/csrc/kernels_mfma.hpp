@@ -850,7 +850,9 @@ agent_mfma_kernel(MfmaParams p) {
           for (int e = 0; e < 4; ++e) fr.u[e] = pack_bf16(s8[2 * e], s8[2 * e + 1]);
           const rsrc_t rf = rsrc_of(reinterpret_cast<char*>(p.agents_f32) + head * C::A_BYTES,
                                     C::A_BYTES);
-          xst16(xp, rf, (unsigned)(((t16 * DC + cc) * 64 + 16 * g + r) * 16), fr.v);
+          const unsigned off = (unsigned)(((t16 * DC + cc) * 64 + 16 * g + r) * 16);
+          if (xp == kXL2 && !C::ROW_PARTIALS) bst16<kL2 | kStream>(rf, off, fr.v);   // see partials
+          else xst16(xp, rf, off, fr.v);
         } else {
           const rsrc_t ra = rsrc_of(p.agents_f32 + ahb, arow_bytes);
           const unsigned off = (unsigned)((a * d + 8 * c) * 4);
@@ -1045,7 +1047,11 @@ agent_mfma_kernel(MfmaParams p) {
                                 : (unsigned)(((t * DT + dt) * 64 + lane) * 16);
           const uint4 x = f4_bits(float4{st.acc[a][dt][0], st.acc[a][dt][1], st.acc[a][dt][2],
                                          st.acc[a][dt][3]});
-          xst16(xp, racc, off, x);
+          // small partial sets (up to 64 agents) are streamed (nt), so the
+          // L2 writes them back during the kernel rather than at its end;
+          // large ones stay cached for the merge
+          if (xp == kXL2 && !C::ROW_PARTIALS) bst16<kL2 | kStream>(racc, off, x);
+          else xst16(xp, racc, off, x);
         }
         const unsigned moff = (g == 0 && 16 * t + (lane & 15) < p.nag)
                                   ? (unsigned)((t * 16 + (lane & 15)) * 8) : kOOB;
@@ -1157,12 +1163,16 @@ agent_mfma_kernel(MfmaParams p) {
           const int f = (j * DT + (c >> 4)) * 64 + 16 * gg + (c & 15);
           const bf16_t hi = bf16_bits(v4[i]);
           const unsigned off = keep ? (unsigned)((f * 8 + e) * 2) : kOOB;
-          if (xp == kXL2) __builtin_amdgcn_raw_buffer_store_b16(hi, rvf, (int)off, 0, kL2);
+          if (xp == kXL2 && !C::ROW_PARTIALS)   // streamed like the partials
+            __builtin_amdgcn_raw_buffer_store_b16(hi, rvf, (int)off, 0, kL2 | kStream);
+          else if (xp == kXL2) __builtin_amdgcn_raw_buffer_store_b16(hi, rvf, (int)off, 0, kL2);
           else __builtin_amdgcn_raw_buffer_store_b16(hi, rvf, (int)off, 0, kCoherent);
           if (C::VSPLIT > 1) {
             const bf16_t lo = bf16_bits(v4[i] - bf16_value(hi));
             const unsigned offl = keep ? (unsigned)(((VA_FRAGS + f) * 8 + e) * 2) : kOOB;
-            if (xp == kXL2) __builtin_amdgcn_raw_buffer_store_b16(lo, rvf, (int)offl, 0, kL2);
+            if (xp == kXL2 && !C::ROW_PARTIALS)
+              __builtin_amdgcn_raw_buffer_store_b16(lo, rvf, (int)offl, 0, kL2 | kStream);
+            else if (xp == kXL2) __builtin_amdgcn_raw_buffer_store_b16(lo, rvf, (int)offl, 0, kL2);
             else __builtin_amdgcn_raw_buffer_store_b16(lo, rvf, (int)offl, 0, kCoherent);
           }
         }
