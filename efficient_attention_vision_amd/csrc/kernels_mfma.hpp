@@ -1041,17 +1041,24 @@ agent_mfma_kernel(MfmaParams p) {
         for (int dt = 0; dt < DT; ++dt) {
           // rows of padding agents are never merged: not stored
           const bool real = 16 * t + (lane & 15) < p.nag;
-          const unsigned off =
-              !real ? kOOB
-              : C::ROW_PARTIALS ? (unsigned)(((16 * t + (lane & 15)) * DPAD + 16 * dt + 4 * g) * 4)
-                                : (unsigned)(((t * DT + dt) * 64 + lane) * 16);
-          const uint4 x = f4_bits(float4{st.acc[a][dt][0], st.acc[a][dt][1], st.acc[a][dt][2],
-                                         st.acc[a][dt][3]});
-          // small partial sets (up to 64 agents) are streamed (nt), so the
-          // L2 writes them back during the kernel rather than at its end;
-          // large ones stay cached for the merge
-          if (xp == kXL2 && !C::ROW_PARTIALS) bst16<kL2 | kStream>(racc, off, x);
-          else xst16(xp, racc, off, x);
+          if (C::ROW_PARTIALS) {
+            // bf16 agent rows: V_A itself enters the broadcast as bf16 here
+            // (VSPLIT = 1), and rounding the partials adds no measurable
+            // error, while it halves the partial traffic
+            const unsigned off =
+                real ? (unsigned)(((16 * t + (lane & 15)) * DPAD + 16 * dt + 4 * g) * 2) : kOOB;
+            xst8(xp, racc, off, uint2{pack_bf16(st.acc[a][dt][0], st.acc[a][dt][1]),
+                                      pack_bf16(st.acc[a][dt][2], st.acc[a][dt][3])});
+          } else {
+            const unsigned off = real ? (unsigned)(((t * DT + dt) * 64 + lane) * 16) : kOOB;
+            const uint4 x = f4_bits(float4{st.acc[a][dt][0], st.acc[a][dt][1], st.acc[a][dt][2],
+                                           st.acc[a][dt][3]});
+            // small partial sets (up to 64 agents) are streamed (nt), so the
+            // L2 writes them back during the kernel rather than at its end;
+            // large ones stay cached for the merge
+            if (xp == kXL2) bst16<kL2 | kStream>(racc, off, x);
+            else xst16(xp, racc, off, x);
+          }
         }
         const unsigned moff = (g == 0 && 16 * t + (lane & 15) < p.nag)
                                   ? (unsigned)((t * 16 + (lane & 15)) * 8) : kOOB;
@@ -1107,7 +1114,7 @@ agent_mfma_kernel(MfmaParams p) {
       const int m = it / nq, q = it - m * nq;
       const int a = slot + p.P * m;
       const int t = a >> 4, r = a & 15, dt = q >> 2, g = q & 3;
-      const unsigned aoff = C::ROW_PARTIALS ? (unsigned)((a * DPAD + 4 * q) * 4)
+      const unsigned aoff = C::ROW_PARTIALS ? (unsigned)((a * DPAD + 4 * q) * 2)
                                             : (unsigned)(((t * DT + dt) * 64 + 16 * g + r) * 16);
       const unsigned moff = (unsigned)((t * 16 + r) * 8);
       constexpr unsigned sstride_acc = KTC * DT * 1024, sstride_ml = KTC * 128;
@@ -1120,7 +1127,13 @@ agent_mfma_kernel(MfmaParams p) {
         for (int u = 0; u < 16; ++u) {
           const bool in = s0 + u < p.P;
           const unsigned so = (unsigned)(s0 + u);
-          xa[u] = bld16<POL>(racc, in ? aoff + so * sstride_acc : kOOB);
+          if (C::ROW_PARTIALS) {
+            const u32x2 h = __builtin_amdgcn_raw_buffer_load_b64(
+                racc, (int)(in ? aoff + so * sstride_acc : kOOB), 0, POL);
+            xa[u] = uint4{h[0], h[1], 0u, 0u};
+          } else {
+            xa[u] = bld16<POL>(racc, in ? aoff + so * sstride_acc : kOOB);
+          }
           xm[u] = __builtin_amdgcn_raw_buffer_load_b64(
               rml, (int)(in ? moff + so * sstride_ml : kOOB), 0, POL);
         }
@@ -1136,7 +1149,12 @@ agent_mfma_kernel(MfmaParams p) {
           if (s0 + u >= p.P) continue;
           const float mu = __uint_as_float(xm[u][0]);
           const float wgt = (mu == -INFINITY) ? 0.f : fast_exp2((mu - cm) * p.sl2);
-          const float4 av = bits_f4(xa[u]);
+          const float4 av = C::ROW_PARTIALS
+                                ? float4{bf16_value((bf16_t)(xa[u].x & 0xffffu)),
+                                         bf16_value((bf16_t)(xa[u].x >> 16)),
+                                         bf16_value((bf16_t)(xa[u].y & 0xffffu)),
+                                         bf16_value((bf16_t)(xa[u].y >> 16))}
+                                : bits_f4(xa[u]);
           Ls = fmaf(__uint_as_float(xm[u][1]), wgt, Ls);
           acc.x = fmaf(av.x, wgt, acc.x);
           acc.y = fmaf(av.y, wgt, acc.y);
