@@ -1098,8 +1098,13 @@ agent_mfma_kernel(MfmaParams p) {
     // Waves without merge items compute their broadcast probabilities now;
     // the merging waves do so between arriving at barrier 2 and waiting.
     // merge items run on the last waves, which hold the fewest query tiles
+    // From 128 agents (where groups have up to 32 slots), two adjacent lanes
+    // share an item (even and odd slots) and combine their partial merges
+    // with one lane exchange, which halves the chain of dependent loads.
+    constexpr int nsplit = C::ROW_PARTIALS ? 2 : 1;
+    const int units = items * nsplit;
     const int mtid = kThreads - 1 - tid;
-    const bool merge_wave = (kWaves - 1 - wave) * 64 < items;
+    const bool merge_wave = (kWaves - 1 - wave) * 64 < units;
     auto early_probs = [&]() {
 #pragma unroll
       for (int i = 0; i < kEarly; ++i)
@@ -1110,7 +1115,8 @@ agent_mfma_kernel(MfmaParams p) {
     AA_STAMP_BY(15, 0);
     with_pol(xp, [&](auto pc) {
     constexpr int POL = decltype(pc)::value;
-    for (int it = mtid; it < items; it += kThreads) {
+    for (int un = mtid; un < units; un += kThreads) {
+      const int it = un / nsplit, part = un - it * nsplit;
       const int m = it / nq, q = it - m * nq;
       const int a = slot + p.P * m;
       const int t = a >> 4, r = a & 15, dt = q >> 2, g = q & 3;
@@ -1120,13 +1126,14 @@ agent_mfma_kernel(MfmaParams p) {
       constexpr unsigned sstride_acc = KTC * DT * 1024, sstride_ml = KTC * 128;
       float M = -INFINITY, Ls = 0.f;
       float4 acc = float4{0.f, 0.f, 0.f, 0.f};
-      for (int s0 = 0; s0 < p.P; s0 += 16) {
+      for (int s0 = 0; s0 < p.P; s0 += 16 * nsplit) {
         uint4 xa[16];
         u32x2 xm[16];
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
-          const bool in = s0 + u < p.P;
-          const unsigned so = (unsigned)(s0 + u);
+          const int sl = s0 + nsplit * u + part;   // this lane's slot
+          const bool in = sl < p.P;
+          const unsigned so = (unsigned)sl;
           if (C::ROW_PARTIALS) {
             const u32x2 h = __builtin_amdgcn_raw_buffer_load_b64(
                 racc, (int)(in ? aoff + so * sstride_acc : kOOB), 0, POL);
@@ -1140,13 +1147,13 @@ agent_mfma_kernel(MfmaParams p) {
         float cm = M;
 #pragma unroll
         for (int u = 0; u < 16; ++u)
-          if (s0 + u < p.P) cm = fmaxf(cm, __uint_as_float(xm[u][0]));
+          if (s0 + nsplit * u + part < p.P) cm = fmaxf(cm, __uint_as_float(xm[u][0]));
         const float corr = (cm == -INFINITY) ? 0.f : fast_exp2((M - cm) * p.sl2);
         Ls *= corr;
         acc.x *= corr; acc.y *= corr; acc.z *= corr; acc.w *= corr;
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
-          if (s0 + u >= p.P) continue;
+          if (s0 + nsplit * u + part >= p.P) continue;
           const float mu = __uint_as_float(xm[u][0]);
           const float wgt = (mu == -INFINITY) ? 0.f : fast_exp2((mu - cm) * p.sl2);
           const float4 av = C::ROW_PARTIALS
@@ -1163,6 +1170,17 @@ agent_mfma_kernel(MfmaParams p) {
         }
         M = cm;
       }
+      if constexpr (nsplit > 1) {   // both lanes of a pair are active (units come in pairs)
+        const float Mo = __shfl_xor(M, 1), Lo = __shfl_xor(Ls, 1);
+        const float ax = __shfl_xor(acc.x, 1), ay = __shfl_xor(acc.y, 1);
+        const float az = __shfl_xor(acc.z, 1), aw = __shfl_xor(acc.w, 1);
+        const float Mn = fmaxf(M, Mo);
+        const float w0 = (M == -INFINITY) ? 0.f : fast_exp2((M - Mn) * p.sl2);
+        const float w1 = (Mo == -INFINITY) ? 0.f : fast_exp2((Mo - Mn) * p.sl2);
+        Ls = Ls * w0 + Lo * w1;
+        acc = float4{acc.x * w0 + ax * w1, acc.y * w0 + ay * w1, acc.z * w0 + az * w1,
+                     acc.w * w0 + aw * w1};
+      }
       const float inv = 1.0f / Ls;
       const int ch = 16 * dt + 4 * g;
       if (sync_group) {
@@ -1174,7 +1192,7 @@ agent_mfma_kernel(MfmaParams p) {
                                    C::VA_BYTES);
         const int u = a & 31, j = a >> 5;
         const int gg = (u & 15) >> 2, e = (u & 3) + (u >= 16 ? 4 : 0);
-        const bool keep = a < p.nag && ch < d;
+        const bool keep = part == 0 && a < p.nag && ch < d;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int c = ch + i;
@@ -1195,7 +1213,8 @@ agent_mfma_kernel(MfmaParams p) {
           }
         }
       } else {
-        const unsigned off = (a < p.nag && ch < d) ? (unsigned)((a * d + ch) * 4) : kOOB;
+        const unsigned off =
+            (part == 0 && a < p.nag && ch < d) ? (unsigned)((a * d + ch) * 4) : kOOB;
         const uint4 x = f4_bits(float4{acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv});
         bst16<POL>(rvo, off, x);
       }
