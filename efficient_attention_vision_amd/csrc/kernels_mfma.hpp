@@ -93,18 +93,18 @@ struct MfmaParams {
   long long* trace;             // phase timestamps (trace builds only)
 };
 
-// Phase timestamps for profiling builds (-DAGENT_ATTN_PHASE_TRACE): 16
+// Phase timestamps for profiling builds (-DAGENT_ATTN_PHASE_TRACE): 32
 // wall-clock stamps per workgroup.  Compiled out otherwise.
 #ifdef AGENT_ATTN_PHASE_TRACE
 #define AA_STAMP(i)                                                            \
   do {                                                                         \
     if (p.trace && threadIdx.x == 0)                                           \
-      p.trace[(long)blockIdx.x * 16 + (i)] = (long long)wall_clock64();        \
+      p.trace[(long)blockIdx.x * 32 + (i)] = (long long)wall_clock64();        \
   } while (0)
 #define AA_STAMP_BY(i, thread)                                                 \
   do {                                                                         \
     if (p.trace && threadIdx.x == (thread))                                    \
-      p.trace[(long)blockIdx.x * 16 + (i)] = (long long)wall_clock64();        \
+      p.trace[(long)blockIdx.x * 32 + (i)] = (long long)wall_clock64();        \
   } while (0)
 #else
 #define AA_STAMP(i) \
@@ -116,6 +116,11 @@ struct MfmaParams {
 #endif
 
 // ------------------------------------------------------------ small helpers
+// Eight bf16 ones: the A operand that turns a matrix-core product into
+// column sums of the B operand.
+__device__ __forceinline__ bf16x8 ones_bf16x8() {
+  return __builtin_bit_cast(bf16x8, uint4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
+}
 __device__ __forceinline__ bf16x8 zero_bf16x8() {
   return __builtin_bit_cast(bf16x8, uint4{0u, 0u, 0u, 0u});
 }
@@ -491,6 +496,7 @@ template <int DC, int ATW>
 struct AggState {
   float m[ATW], l[ATW];
   f32x4 acc[ATW][2 * DC];
+  f32x4 lacc[ATW];   // row sums of the probabilities, on the matrix cores
 };
 
 template <class C, int DC, int ATW>
@@ -548,7 +554,7 @@ __device__ __forceinline__ void agg_block(AggState<DC, ATW>& st, const bf16_t* K
     if (__any(grow)) {
       const float mn = grow ? bm : st.m[a];
       const float corr = grow ? fast_exp2((st.m[a] - mn) * sl2) : 1.f;
-      st.l[a] *= corr;
+      st.lacc[a] *= corr;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) st.acc[a][dt] *= corr;
       st.m[a] = mn;
@@ -560,10 +566,12 @@ __device__ __forceinline__ void agg_block(AggState<DC, ATW>& st, const bf16_t* K
       pv[i] = fast_exp2(fmaf(S0[i], sl2, -off));
       pv[4 + i] = fast_exp2(fmaf(S1[i], sl2, -off));
     }
-    st.l[a] += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
     union { bf16x8 v; unsigned w[4]; } pf;
 #pragma unroll
     for (int e = 0; e < 4; ++e) pf.w[e] = pack_bf16(pv[2 * e], pv[2 * e + 1]);
+    // the sum over the block's tokens of the same bf16 probabilities that
+    // enter P V (every row of the result holds it)
+    st.lacc[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_bf16x8(), pf.v, st.lacc[a], 0, 0, 0);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
       st.acc[a][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], pf.v, st.acc[a][dt], 0, 0, 0);
@@ -624,7 +632,9 @@ __device__ __forceinline__ void bcast_probs(const bf16x8 (&qf)[DC], const bf16x8
   for (int t = 0; t < KTC; ++t) M = fmaxf(M, fmaxf(fmaxf(S[t][0], S[t][1]), fmaxf(S[t][2], S[t][3])));
   M = group4_max(M);
   const float off = M * sl2;
-  float L = 0.f;
+  // row sums of the same bf16 probabilities that enter P V, on the matrix
+  // cores (every row of the result holds the token's sum)
+  f32x4 Lacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < C::KC; ++j) {
     float pv[8];
@@ -633,13 +643,13 @@ __device__ __forceinline__ void bcast_probs(const bf16x8 (&qf)[DC], const bf16x8
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         pv[4 * h2 + i] = fast_exp2(fmaf(S[2 * j + h2][i], sl2, -off));
-    L += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
     union { bf16x8 v; unsigned w[4]; } u;
 #pragma unroll
     for (int e = 0; e < 4; ++e) u.w[e] = pack_bf16(pv[2 * e], pv[2 * e + 1]);
     pf[j] = u.v;
+    Lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_bf16x8(), u.v, Lacc, 0, 0, 0);
   }
-  inv = 1.0f / group4_sum(L);
+  inv = 1.0f / Lacc[0];
 }
 
 // Broadcast output of one query tile: O = P2 V_A (V_A as bf16 hi + lo when
@@ -933,6 +943,7 @@ agent_mfma_kernel(MfmaParams p) {
     for (int a = 0; a < ATW; ++a) {
       st.m[a] = -INFINITY;
       st.l[a] = 0.f;
+      st.lacc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) st.acc[a][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
@@ -958,7 +969,7 @@ agent_mfma_kernel(MfmaParams p) {
     AA_STAMP(5);
     if (single && (p.phases & PH_BCAST)) load_q_tile<DC>(qcur, rq, n0 + 16 * wave, n1, d);
 #pragma unroll
-    for (int a = 0; a < ATW; ++a) st.l[a] = group4_sum(st.l[a]);
+    for (int a = 0; a < ATW; ++a) st.l[a] = st.lacc[a][0];
 
     // combine the TG token groups of each agent group through LDS:
     // records [rec][a][DT acc | 1 (m, l)][64 lanes] x 16 B
