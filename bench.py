@@ -271,6 +271,9 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="pvt_stage1")
+    ap.add_argument("--layout", choices=("bhnd", "bnhd"), default="bhnd",
+                    help="q/k/v/out as dense [B,H,N,d] (default) or as [B,N,H,d] storage "
+                         "(strided views, as a head-split projection leaves them)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -314,12 +317,16 @@ def main():
     gen = torch.Generator(device=dev)
     gen.manual_seed(0)
     sets = []
+    store = (wl.B, wl.N, wl.H, wl.d) if args.layout == "bnhd" else shape
     for _ in range(R):
-        q, k, v = (torch.randn(shape, generator=gen, device=dev, dtype=torch.float32)
+        q, k, v = (torch.randn(store, generator=gen, device=dev, dtype=torch.float32)
                    .mul_(wl.sigma).to(dt) for _ in range(3))
+        if args.layout == "bnhd":
+            q, k, v = (t.transpose(1, 2) for t in (q, k, v))
         a = (torch.randn((wl.B, wl.H, wl.k, wl.d), generator=gen, device=dev).to(dt)
              if wl.supplied_agents else None)
-        sets.append((q, k, v, a, torch.empty_like(q)))
+        out = torch.empty_strided(q.shape, q.stride(), dtype=dt, device=dev)
+        sets.append((q, k, v, a, out))
     need = _binding.agent_attn_workspace_bytes(wl.B, wl.H, wl.h, wl.w, wl.d, wl.s,
                                                0 if wl.dtype == "f32" else 1)
     ws = torch.zeros(need, dtype=torch.uint8, device=dev)
@@ -398,7 +405,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "grid": [wl.h, wl.w], "N": wl.N,
                    "d": wl.d, "agents": wl.k, "agent_grid": [wl.s, wl.s],
-                   "supplied_agents": wl.supplied_agents, "rotating_sets": R},
+                   "supplied_agents": wl.supplied_agents, "rotating_sets": R,
+                   "layout": "[B,N,H,d] storage" if args.layout == "bnhd" else "[B,H,N,d]"},
         "roofline": roof,
         "kernel_us_per_launch": kernel_us,
         "eager_launch_us": {"median": pct(0.5), "p10": pct(0.1), "p90": pct(0.9)},

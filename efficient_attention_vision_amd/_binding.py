@@ -28,6 +28,8 @@ _SIGNATURES = {
     "agent_attn_forward": (_c_int, [_vp] * 5 + [_c_int] * 6 + [_c_float, _c_int, _vp]),
     "agent_attn_forward_ws": (_c_int, [_vp] * 5 + [_c_int] * 6 + [_c_float, _c_int, _vp, _c_size,
                                                                   _vp]),
+    "agent_attn_forward_strided": (_c_int, [_vp] * 5 + [_c_int] * 6 + [ctypes.c_longlong] * 3 +
+                                   [_c_float, _c_int, _vp, _c_size, _vp]),
     "agent_attn_pool": (_c_int, [_vp, _vp] + [_c_int] * 7 + [_vp]),
     "agent_attn_aggregate_workspace_bytes": (_c_size, [_c_int] * 6),
     "agent_attn_aggregate": (_c_int, [_vp] * 4 + [_c_int] * 5 + [_c_float, _c_int, _vp, _c_size,
@@ -134,32 +136,55 @@ def agent_attn_workspace_bytes(B, H, h, w, d, s, dtype_code) -> int:
     return int(lib().agent_attn_workspace_bytes(B, H, h, w, d, s, dtype_code))
 
 
+def _strided_view(t, name):
+    """A [B, H, N, d] GPU tensor whose channels are contiguous (any strides
+    for the other three dimensions, e.g. a [B, N, H, d] tensor transposed)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dim() != 4:
+        raise ValueError(f"{name} must have 4 dimensions, got shape {tuple(t.shape)}")
+    if t.stride(3) != 1 and t.shape[3] > 1:
+        raise ValueError(f"{name} must have contiguous channels (stride 1 in the last dimension)")
+    return t
+
+
 def agent_attn_forward(q, k, v, grid_hw, s, scale=None, agents=None, out=None, workspace=None):
     """O = softmax(scale Q A^T) softmax(scale A K^T) V with A = 2-D average
     pool of Q to s x s agents (or `agents` [B, H, s*s, d]).
 
     q, k, v: [B, H, h*w, d] float32 or bfloat16 GPU tensors; grid_hw = (h, w).
-    Runs on torch's current stream; returns `out` ([B, H, h*w, d], q's dtype).
+    Dense tensors use agent_attn_forward_ws; views with contiguous channels
+    and the same strides for q, k, v (for example x.view(B, N, H, d)
+    .transpose(1, 2)) use agent_attn_forward_strided, with `out` given those
+    strides too.  Runs on torch's current stream; returns `out`.
     """
     L = lib()
-    _dev_tensor(q, "q")
+    _strided_view(q, "q")
     B, H, N, d = q.shape
     h, w = (int(x) for x in grid_hw)
     if h * w != N:
         raise ValueError(f"grid {h}x{w} does not match N={N}")
+    dense = q.is_contiguous()
     for name, t in (("k", k), ("v", v)):
-        _dev_tensor(t, name)
+        _strided_view(t, name)
         _same(q, t, name, q.shape, q.dtype)
+        if dense != t.is_contiguous() or (not dense and t.stride() != q.stride()):
+            raise ValueError(f"{name} must have q's strides {q.stride()}, got {t.stride()}")
     if agents is not None:
         _dev_tensor(agents, "agents")
         _same(q, agents, "agents", (B, H, int(s) * int(s), d), q.dtype)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty_like(q) if dense else torch.empty_strided(
+            q.shape, q.stride(), dtype=q.dtype, device=q.device)
     else:
-        _dev_tensor(out, "out")
+        _strided_view(out, "out")
         _same(q, out, "out", q.shape, q.dtype)
+        if dense != out.is_contiguous() or (not dense and out.stride() != q.stride()):
+            raise ValueError(f"out must have q's strides {q.stride()}, got {out.stride()}")
     code = _dtype_code(q)
     with torch.cuda.device(q.device):
         need = L.agent_attn_workspace_bytes(B, H, h, w, d, int(s), code)
@@ -168,9 +193,15 @@ def agent_attn_forward(q, k, v, grid_hw, s, scale=None, agents=None, out=None, w
             if workspace is None:
                 workspace = cached_workspace(q.device, need)
             ws_ptr, ws_size = _ptr(workspace), workspace.numel() * workspace.element_size()
-        rc = L.agent_attn_forward_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(agents), B, H, h,
-                                     w, d, int(s), float(scale), code, ws_ptr, ws_size,
-                                     _stream(q.device))
+        if dense:
+            rc = L.agent_attn_forward_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(agents), B, H,
+                                         h, w, d, int(s), float(scale), code, ws_ptr, ws_size,
+                                         _stream(q.device))
+        else:
+            sb, sh, sn, _ = q.stride()
+            rc = L.agent_attn_forward_strided(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(agents),
+                                              B, H, h, w, d, int(s), sb, sh, sn, float(scale),
+                                              code, ws_ptr, ws_size, _stream(q.device))
     _check(rc)
     return out
 

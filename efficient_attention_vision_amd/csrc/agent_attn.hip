@@ -53,6 +53,10 @@ struct Dims {
   long B = 0, H = 0, BH = 0;
   long N = 0;
   int h = 0, w = 0, d = 0, s = 0, nag = 0, dtype = 0;
+  long sb = 0, sh = 0, sn = 0;   // element strides of q/k/v/out (contiguous by default)
+  aa::Strides strides() const { return aa::Strides{sb, sh, sn, (int)(H > 0 ? H : 1)}; }
+  // elements from the first to one past the last element of a tensor
+  long span() const { return BH == 0 ? 0 : (B - 1) * sb + (H - 1) * sh + (N - 1) * sn + d; }
 };
 
 int check_dtype(int dtype) {
@@ -88,6 +92,9 @@ int check_core(Dims& D, int B, int H, long N, int d, int nag, int dtype) {
   D.d = d;
   D.nag = nag;
   D.dtype = dtype;
+  D.sn = d;
+  D.sh = N * d;
+  D.sb = (long)H * N * d;
   return AGENT_ATTN_OK;
 }
 
@@ -372,7 +379,7 @@ template <typename T>
 int launch_pool(const Dims& D, const void* q, float* A, hipStream_t st) {
   const long blocks = D.BH * D.nag;
   hipLaunchKernelGGL(aa::pool_kernel<T>, dim3((unsigned)blocks), dim3(256), 0, st,
-                     (const T*)q, A, D.h, D.w, D.d, D.s);
+                     (const T*)q, A, D.h, D.w, D.d, D.s, D.strides());
   AA_LAUNCH_CHECK("agent_pool launch");
   return AGENT_ATTN_OK;
 }
@@ -395,11 +402,11 @@ int launch_aggregate(const Dims& D, const float* A, const void* k, const void* v
   if (D.d <= 64)
     hipLaunchKernelGGL((aa::aggregate_partial_scalar<T, 64>), dim3((unsigned)blocks), dim3(256), 0,
                        st, A, (const T*)k, (const T*)v, part, (int)D.N, D.d, D.nag, sl2, chunk,
-                       nchunks);
+                       nchunks, D.strides());
   else
     hipLaunchKernelGGL((aa::aggregate_partial_scalar<T, 128>), dim3((unsigned)blocks), dim3(256),
                        0, st, A, (const T*)k, (const T*)v, part, (int)D.N, D.d, D.nag, sl2, chunk,
-                       nchunks);
+                       nchunks, D.strides());
   AA_LAUNCH_CHECK("agent_aggregate launch");
   hipLaunchKernelGGL(aa::merge_partials_kernel, dim3((unsigned)(D.BH * D.nag)), dim3(128), 0, st,
                      part, VA, D.d, D.nag, nchunks);
@@ -414,10 +421,10 @@ int launch_broadcast(const Dims& D, const void* q, const float* A, const float* 
   const long blocks = D.BH * nqblk;
   if (D.d <= 64)
     hipLaunchKernelGGL((aa::broadcast_scalar<T, 64>), dim3((unsigned)blocks), dim3(256), 0, st,
-                       (const T*)q, A, VA, (T*)out, (int)D.N, D.d, D.nag, sl2, nqblk);
+                       (const T*)q, A, VA, (T*)out, (int)D.N, D.d, D.nag, sl2, nqblk, D.strides());
   else
     hipLaunchKernelGGL((aa::broadcast_scalar<T, 128>), dim3((unsigned)blocks), dim3(256), 0, st,
-                       (const T*)q, A, VA, (T*)out, (int)D.N, D.d, D.nag, sl2, nqblk);
+                       (const T*)q, A, VA, (T*)out, (int)D.N, D.d, D.nag, sl2, nqblk, D.strides());
   AA_LAUNCH_CHECK("agent_broadcast launch");
   return AGENT_ATTN_OK;
 }
@@ -429,12 +436,15 @@ long long* g_trace = nullptr;  // profiling builds: per-workgroup phase stamps
 std::atomic<long> g_spin_limit{aa::kSpinLimit};   // polls before a group wait gives up
 
 int launch_mfma(int DC, const aa::MfmaParams& mp, long grid, int nag, hipStream_t st) {
+  // the dense [B, H, N, d] layout has its own kernel instance
+  const bool strided = !(mp.sn == mp.d && mp.sh == (long)mp.N * mp.d &&
+                         mp.sb == (long)mp.H * mp.N * mp.d);
   const int ktc = mfma_ktc(nag);
   int e;
   switch (DC) {
-    case 1: e = aa::launch_mfma_dc<1>(mp, ktc, grid, st); break;
-    case 2: e = aa::launch_mfma_dc<2>(mp, ktc, grid, st); break;
-    default: e = aa::launch_mfma_dc<4>(mp, ktc, grid, st); break;
+    case 1: e = aa::launch_mfma_dc<1>(mp, ktc, strided, grid, st); break;
+    case 2: e = aa::launch_mfma_dc<2>(mp, ktc, strided, grid, st); break;
+    default: e = aa::launch_mfma_dc<4>(mp, ktc, strided, grid, st); break;
   }
   if (e != hipSuccess) return hip_fail((hipError_t)e, "agent attention matrix-core kernel launch");
   return AGENT_ATTN_OK;
@@ -450,6 +460,10 @@ aa::MfmaParams mfma_params(const Dims& D, int P, int T, float scale) {
   mp.d = D.d;
   mp.s = D.s;
   mp.nag = D.nag;
+  mp.H = (int)(D.H > 0 ? D.H : 1);
+  mp.sb = D.sb;
+  mp.sh = D.sh;
+  mp.sn = (int)D.sn;
   mp.P = P;
   mp.T = T;
   mp.sl2 = scale * aa::kLog2e;
@@ -467,9 +481,9 @@ int run_mfma_phases(const Dims& D, aa::MfmaParams mp, int DC, int phases, bool f
   if (lds > 160 * 1024 - 64)
     return fail(AGENT_ATTN_ERR_UNSUPPORTED, "d=%d with %d agents needs %d bytes of LDS", D.d,
                 D.nag, lds);
-  if (D.N * (long)D.d * 2 > (long)aa::kOOB)
-    return fail(AGENT_ATTN_ERR_SHAPE, "N*d=%ld exceeds the per-head limit of 2^30 elements",
-                D.N * (long)D.d);
+  if (((D.N - 1) * D.sn + D.d) * 2 >= (long)aa::kOOB)
+    return fail(AGENT_ATTN_ERR_SHAPE, "one head spans %ld elements, above the limit of 2^30",
+                (D.N - 1) * D.sn + D.d);
   const long grid = D.BH * mp.P;
   if (fused) {
     mp.phases = phases;
@@ -525,19 +539,60 @@ int run_forward(const Dims& D, const Plan& P, const void* q, const void* k, cons
   return launch_broadcast<T>(D, q, A, VA, out, sl2, st);
 }
 
+// Element strides (batch, head, token) of q/k/v/out: positive multiples of
+// 8 elements (16-byte aligned rows), at least d between tokens, and no two
+// (b, h, n, c) positions on the same element: sorted by stride, the
+// dimensions of extent > 1 must nest (each stride at least the previous
+// stride times its extent, the first at least d).
+int set_strides(Dims& D, long long sb, long long sh, long long sn) {
+  if (sb < 1 || sh < 1 || sn < 1)
+    return fail(AGENT_ATTN_ERR_SHAPE, "strides %lld, %lld, %lld must be >= 1", sb, sh, sn);
+  if (sb % 8 || sh % 8 || sn % 8)
+    return fail(AGENT_ATTN_ERR_ALIGN, "strides %lld, %lld, %lld must be multiples of 8 elements",
+                sb, sh, sn);
+  if (sn < D.d)
+    return fail(AGENT_ATTN_ERR_SHAPE, "token stride %lld is below the head dim %d", sn, D.d);
+  struct Ext {
+    long long st, n;
+  } e[3] = {{sn, D.N}, {sh, D.H}, {sb, D.B}};
+  std::sort(e, e + 3, [](const Ext& a, const Ext& b) { return a.st < b.st; });
+  long long need = D.d;
+  for (const Ext& x : e) {
+    if (x.n <= 1) continue;
+    if (x.st < need)
+      return fail(AGENT_ATTN_ERR_SHAPE, "strides %lld, %lld, %lld make elements overlap", sb, sh,
+                  sn);
+    need = x.st * x.n;
+  }
+  // byte offsets inside one head are 32-bit in the matrix-core kernels
+  if (((D.N - 1) * sn + D.d) * (long long)elem_size(D.dtype) >= (long long)aa::kOOB)
+    return fail(AGENT_ATTN_ERR_SHAPE, "one head spans more than 2^31 bytes with token stride %lld",
+                sn);
+  D.sb = (long)sb;
+  D.sh = (long)sh;
+  D.sn = (long)sn;
+  if (D.span() >= (1L << 40))
+    return fail(AGENT_ATTN_ERR_SHAPE, "tensors span more than 2^40 elements");
+  return AGENT_ATTN_OK;
+}
+
 int validate_forward(Dims& D, const void* q, const void* k, const void* v, void* out,
                      const void* agents, int B, int H, int h, int w, int d, int s, float scale,
-                     int dtype) {
+                     int dtype, const long long* strides = nullptr) {
   int rc = check_grid(D, B, H, h, w, d, s, dtype);
   if (rc) return rc;
   rc = check_scale(scale);
   if (rc) return rc;
   if (D.BH == 0) return AGENT_ATTN_OK;  // empty batch: tensors may be NULL
+  if (strides) {
+    rc = set_strides(D, strides[0], strides[1], strides[2]);
+    if (rc) return rc;
+  }
   if (!q || !k || !v || !out)
     return fail(AGENT_ATTN_ERR_NULL, "q, k, v and out must be non-NULL");
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(out) || misaligned(agents))
     return fail(AGENT_ATTN_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
-  const size_t tb = (size_t)D.BH * D.N * D.d * elem_size(dtype);
+  const size_t tb = (size_t)D.span() * elem_size(dtype);
   const size_t ab = (size_t)D.BH * D.nag * D.d * elem_size(dtype);
   if (ranges_overlap(out, tb, q, tb) || ranges_overlap(out, tb, k, tb) ||
       ranges_overlap(out, tb, v, tb) || ranges_overlap(out, tb, agents, ab))
@@ -597,6 +652,28 @@ size_t aggregate_ws_bytes(const Dims& D) {
   return align_up(mfma_ml_bytes(D, P, DC), 256) + align_up(mfma_acc_bytes(D, P, DC), 256);
 }
 
+int forward_ws(const void* q, const void* k, const void* v, void* out, const void* agents, int B,
+               int H, int h, int w, int d, int s, float scale, int dtype, void* workspace,
+               size_t workspace_bytes, void* stream, const long long* strides) {
+  Dims D;
+  int rc = validate_forward(D, q, k, v, out, agents, B, H, h, w, d, s, scale, dtype, strides);
+  if (rc) return rc;
+  if (D.BH == 0) return AGENT_ATTN_OK;
+  const Plan P = make_plan(D, device_cus());
+  if (!workspace || workspace_bytes < P.bytes)
+    return fail(AGENT_ATTN_ERR_WORKSPACE, "workspace of %zu bytes at %p; %zu bytes needed",
+                workspace_bytes, workspace, P.bytes);
+  if (((uintptr_t)workspace & 255u) != 0)
+    return fail(AGENT_ATTN_ERR_ALIGN, "workspace must be 256-byte aligned");
+  const size_t tb = (size_t)D.span() * elem_size(dtype);
+  const size_t ab = (size_t)D.BH * D.nag * D.d * elem_size(dtype);
+  if (ranges_overlap(workspace, P.bytes, q, tb) || ranges_overlap(workspace, P.bytes, k, tb) ||
+      ranges_overlap(workspace, P.bytes, v, tb) || ranges_overlap(workspace, P.bytes, out, tb) ||
+      ranges_overlap(workspace, P.bytes, agents, ab))
+    return fail(AGENT_ATTN_ERR_ALIAS, "workspace overlaps a tensor argument");
+  return dispatch_forward(D, P, q, k, v, out, agents, scale, workspace, (hipStream_t)stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -608,27 +685,23 @@ size_t agent_attn_workspace_bytes(int B, int H, int h, int w, int d, int s, int 
   return make_plan(D, device_cus()).bytes;
 }
 
+
 int agent_attn_forward_ws(const void* q, const void* k, const void* v, void* out,
                           const void* agents, int B, int H, int h, int w, int d, int s,
                           float scale, int dtype, void* workspace, size_t workspace_bytes,
                           void* stream) {
-  Dims D;
-  int rc = validate_forward(D, q, k, v, out, agents, B, H, h, w, d, s, scale, dtype);
-  if (rc) return rc;
-  if (D.BH == 0) return AGENT_ATTN_OK;
-  const Plan P = make_plan(D, device_cus());
-  if (!workspace || workspace_bytes < P.bytes)
-    return fail(AGENT_ATTN_ERR_WORKSPACE, "workspace of %zu bytes at %p; %zu bytes needed",
-                workspace_bytes, workspace, P.bytes);
-  if (((uintptr_t)workspace & 255u) != 0)
-    return fail(AGENT_ATTN_ERR_ALIGN, "workspace must be 256-byte aligned");
-  const size_t tb = (size_t)D.BH * D.N * D.d * elem_size(dtype);
-  const size_t ab = (size_t)D.BH * D.nag * D.d * elem_size(dtype);
-  if (ranges_overlap(workspace, P.bytes, q, tb) || ranges_overlap(workspace, P.bytes, k, tb) ||
-      ranges_overlap(workspace, P.bytes, v, tb) || ranges_overlap(workspace, P.bytes, out, tb) ||
-      ranges_overlap(workspace, P.bytes, agents, ab))
-    return fail(AGENT_ATTN_ERR_ALIAS, "workspace overlaps a tensor argument");
-  return dispatch_forward(D, P, q, k, v, out, agents, scale, workspace, (hipStream_t)stream);
+  return forward_ws(q, k, v, out, agents, B, H, h, w, d, s, scale, dtype, workspace,
+                    workspace_bytes, stream, nullptr);
+}
+
+int agent_attn_forward_strided(const void* q, const void* k, const void* v, void* out,
+                               const void* agents, int B, int H, int h, int w, int d, int s,
+                               long long stride_b, long long stride_h, long long stride_n,
+                               float scale, int dtype, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  const long long st[3] = {stride_b, stride_h, stride_n};
+  return forward_ws(q, k, v, out, agents, B, H, h, w, d, s, scale, dtype, workspace,
+                    workspace_bytes, stream, st);
 }
 
 int agent_attn_forward(const void* q, const void* k, const void* v, void* out,

@@ -37,6 +37,16 @@ __device__ __forceinline__ int xcc_id() {
   return __builtin_amdgcn_s_getreg((20) | (0 << 6) | ((4 - 1) << 11));
 }
 
+// Element strides of q, k, v and out: batch b, head h and token n of the
+// [B, H, N, d] view (channels contiguous).  Head index bh = b*H + h.
+struct Strides {
+  long b, h, n;
+  int H;
+};
+__host__ __device__ __forceinline__ long head_offset(const Strides& st, long bh) {
+  return (bh / st.H) * st.b + (bh % st.H) * st.h;
+}
+
 // Bits of the fault word that the fused kernel leaves in its workspace.
 constexpr unsigned kFaultBarrier = 1u;   // a group barrier gave up waiting
 constexpr unsigned kFaultXcd = 2u;       // a workgroup ran off its planned XCD

@@ -91,6 +91,9 @@ struct MfmaParams {
   int xcd_heads;                // >0: heads per XCD for the XCD-aware mapping
   long spin_limit;              // polls before a group wait gives up (kSpinLimit)
   long long* trace;             // phase timestamps (trace builds only)
+  long sb, sh;                  // q/k/v/out element strides of batch and head
+  int H;                        // heads per batch entry (head index = b*H + h)
+  int sn;                       // element stride between tokens (channels contiguous)
 };
 
 // Phase timestamps for profiling builds (-DAGENT_ATTN_PHASE_TRACE): 32
@@ -427,7 +430,7 @@ __device__ __forceinline__ PoolGeo pool_geo(const MfmaParams& p, int a) {
 }
 
 __device__ __forceinline__ void pool_issue(const MfmaParams& p, rsrc_t rq, int slot, int item,
-                                           int items, int tbase, uint4 (&x)[kPoolTok]) {
+                                           int items, int tbase, uint4 (&x)[kPoolTok], int sn) {
   const int DCH = p.d >> 3, TGP = p.pool_tgp;
   const int pr = item >> p.pool_tgp_log2, tg = item - pr * TGP;
   const int m = idiv(pr, DCH, rcp_approx(DCH)), c = pr - m * DCH;
@@ -439,7 +442,7 @@ __device__ __forceinline__ void pool_issue(const MfmaParams& p, rsrc_t rq, int s
     const int tq = idiv(t, G.wc, rwc);
     const int rr = G.r0 + tq, cc = G.c0 + (t - tq * G.wc);
     const unsigned off = (item < items && t < G.cnt)
-                             ? (unsigned)(((rr * p.w + cc) * p.d + 8 * c) * 2)
+                             ? (unsigned)(((rr * p.w + cc) * sn + 8 * c) * 2)
                              : kOOB;
     x[u] = bld16<kPlain>(rq, off);
   }
@@ -460,13 +463,13 @@ __device__ __forceinline__ void pool_accum(const uint4 (&x)[kPoolTok], float (&a
 // tok0 + 8*(it / DCH) .. +8 and channels 8*(it % DCH) .. +8.  Tokens at or
 // past tok_end load as zeros.
 __device__ __forceinline__ void load_tile8(uint4 (&x)[8], rsrc_t r, int it, int tok0, int tok_end,
-                                           int d) {
+                                           int d, int sn) {
   const int DCH = d >> 3;
   const int t8 = idiv(it, DCH, rcp_approx(DCH)), ch = it - t8 * DCH;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int tok = tok0 + 8 * t8 + j;
-    x[j] = bld16<kPlain>(r, tok < tok_end ? (unsigned)((tok * d + 8 * ch) * 2) : kOOB);
+    x[j] = bld16<kPlain>(r, tok < tok_end ? (unsigned)((tok * sn + 8 * ch) * 2) : kOOB);
   }
 }
 // V tile -> transposed rows Vt[channel][token] of the round
@@ -581,13 +584,13 @@ __device__ __forceinline__ void agg_block(AggState<DC, ATW>& st, const bf16_t* K
 // ------------------------------------------------------------ broadcast
 template <int DC>
 __device__ __forceinline__ void load_q_tile(bf16x8 (&qf)[DC], rsrc_t rq, int tok0, int tok_end,
-                                            int d) {
+                                            int d, int sn) {
   const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
   const int tok = tok0 + r;
 #pragma unroll
   for (int c = 0; c < DC; ++c) {
     const int ch0 = 8 * (DC * g + c);
-    const unsigned off = (tok < tok_end && ch0 < d) ? (unsigned)((tok * d + ch0) * 2) : kOOB;
+    const unsigned off = (tok < tok_end && ch0 < d) ? (unsigned)((tok * sn + ch0) * 2) : kOOB;
     qf[c] = __builtin_bit_cast(bf16x8, bld16<kPlain>(rq, off));
   }
 }
@@ -656,7 +659,7 @@ __device__ __forceinline__ void bcast_probs(const bf16x8 (&qf)[DC], const bf16x8
 // VSPLIT = 2), normalised, rounded to bf16 and stored.
 template <class C, int DC, int KTC>
 __device__ __forceinline__ void bcast_out(const bf16x8 (&pf)[C::KC], float inv, const bf16x8* VAf,
-                                          rsrc_t ro, int tok0, int tok_end, int d) {
+                                          rsrc_t ro, int tok0, int tok_end, int d, int sn) {
   constexpr int DT = 2 * DC;
   constexpr int VA_PART = C::KC * DT * 64;
   const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
@@ -702,7 +705,7 @@ __device__ __forceinline__ void bcast_out(const bf16x8 (&pf)[C::KC], float inv, 
         pk[d1][w] = y[1];
       }
       const int c0 = 64 * q + 32 * s2 + 8 * g;
-      const unsigned off2 = (tok < tok_end && c0 < d) ? (unsigned)((tok * d + c0) * 2) : kOOB;
+      const unsigned off2 = (tok < tok_end && c0 < d) ? (unsigned)((tok * sn + c0) * 2) : kOOB;
       bst16<kStream>(ro, off2, uint4{pk[d0][0], pk[d0][1], pk[d1][0], pk[d1][1]});
     }
 }
@@ -710,15 +713,15 @@ __device__ __forceinline__ void bcast_out(const bf16x8 (&pf)[C::KC], float inv, 
 template <class C, int DC, int KTC>
 __device__ __forceinline__ void bcast_tile(const bf16x8 (&qf)[DC], const bf16x8* Af,
                                            const bf16x8* VAf, rsrc_t ro, int tok0, int tok_end,
-                                           int d, int nag, float sl2) {
+                                           int d, int sn, int nag, float sl2) {
   bf16x8 pf[C::KC];
   float inv;
   bcast_probs<C, DC, KTC>(qf, Af, nag, sl2, pf, inv);
-  bcast_out<C, DC, KTC>(pf, inv, VAf, ro, tok0, tok_end, d);
+  bcast_out<C, DC, KTC>(pf, inv, VAf, ro, tok0, tok_end, d, sn);
 }
 
 // ------------------------------------------------------------- the kernel
-template <int DC, int KTC>
+template <int DC, int KTC, bool STRIDED>
 __global__ void __launch_bounds__(kThreads)
 agent_mfma_kernel(MfmaParams p) {
   using C = Cfg<DC, KTC>;
@@ -753,8 +756,14 @@ agent_mfma_kernel(MfmaParams p) {
   const int d = p.d, DCH = d >> 3;
   const int n0 = slot * p.T;
   const int n1 = min(p.N, n0 + p.T);
-  const long hoff = (long)head * p.N * d;
-  const unsigned head_bytes = (unsigned)(p.N * d * 2);
+  // token stride and head offset: dense [B, H, N, d], or the caller's strides
+  const int sn = STRIDED ? p.sn : d;
+  long hoff = (long)head * p.N * d;
+  if (STRIDED) {
+    const int hb = idiv(head, p.H, rcp_approx(p.H));   // batch entry of the head
+    hoff = (long)hb * p.sb + (long)(head - hb * p.H) * p.sh;
+  }
+  const unsigned head_bytes = (unsigned)(((long)(p.N - 1) * sn + d) * 2);
   GroupSync gs{p.sync + (long)head * kSyncDwords, slot, p.P, false, p.status, p.spin_limit};
   const bool sync_group = p.fused && p.P > 1;
   const bool single = p.fused && p.P == 1;   // whole head in this workgroup
@@ -778,7 +787,7 @@ agent_mfma_kernel(MfmaParams p) {
   const int pool_chunk = p.pool_tgp * kPoolTok;       // window tokens per item pass
   const int pool_npass = (p.pool_maxcnt + pool_chunk - 1) / pool_chunk;
   uint4 px[kPoolTok];
-  if (p.phases & PH_POOL) pool_issue(p, rq, slot, tid, pool_items, 0, px);
+  if (p.phases & PH_POOL) pool_issue(p, rq, slot, tid, pool_items, 0, px, sn);
 
   // ---- then K and V of the first round (one 8x8 tile per thread)
   const int ag = wave % C::AG, tg = wave / C::AG;
@@ -790,8 +799,8 @@ agent_mfma_kernel(MfmaParams p) {
   // arrive during the pooling, barrier 0 and the agent fragments.
   auto load_kv0 = [&]() {
     const int tend = tid < r0tiles ? n0 + r0cnt : -1;
-    load_tile8(kx, rk, tid, n0, tend, d);
-    load_tile8(vx, rv, tid, n0, tend, d);
+    load_tile8(kx, rk, tid, n0, tend, d, sn);
+    load_tile8(vx, rv, tid, n0, tend, d, sn);
   };
   if ((p.phases & PH_AGG) && !(p.phases & PH_POOL)) load_kv0();
   // first query tile of this wave, loaded ahead of the broadcast
@@ -806,7 +815,7 @@ agent_mfma_kernel(MfmaParams p) {
   bf16x8 qe[kEarly][DC];
   float einv[kEarly];
   bool early = false;
-  if ((p.phases & PH_BCAST) && !(p.phases & PH_AGG)) load_q_tile<DC>(qcur, rq, n0 + 16 * wave, n1, d);
+  if ((p.phases & PH_BCAST) && !(p.phases & PH_AGG)) load_q_tile<DC>(qcur, rq, n0 + 16 * wave, n1, d, sn);
   AA_STAMP(1);
 
   // ---- POOL
@@ -820,7 +829,7 @@ agent_mfma_kernel(MfmaParams p) {
     for (int b0 = 0; b0 < pool_items; b0 += kThreads) {
       float acc8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
       for (int ps = 0; ps < pool_npass; ++ps) {
-        if (b0 > 0 || ps > 0) pool_issue(p, rq, slot, b0 + tid, pool_items, ps * pool_chunk, px);
+        if (b0 > 0 || ps > 0) pool_issue(p, rq, slot, b0 + tid, pool_items, ps * pool_chunk, px, sn);
         pool_accum(px, acc8);
         if (b0 == 0 && ps == 0 && (p.phases & PH_AGG)) load_kv0();
       }
@@ -954,8 +963,8 @@ agent_mfma_kernel(MfmaParams p) {
       __syncthreads();   // previous round (or the pooling sums) fully read
       if (rt0 != n0) {
         const int tend = tid < ntile ? rt0 + rcnt : -1;
-        load_tile8(kx, rk, tid, rt0, tend, d);
-        load_tile8(vx, rv, tid, rt0, tend, d);
+        load_tile8(kx, rk, tid, rt0, tend, d, sn);
+        load_tile8(vx, rv, tid, rt0, tend, d, sn);
       }
       if (tid < ntile && !(staged0 && rt0 == n0)) {
         store_tile_rows(Ks, C::KS_STRIDE, kx, tid, d);
@@ -967,7 +976,7 @@ agent_mfma_kernel(MfmaParams p) {
         agg_block<C, DC, ATW>(st, Ks, Af, Vt, 32 * b, ag, min(32, n1 - (rt0 + 32 * b)), d, p.sl2);
     }
     AA_STAMP(5);
-    if (single && (p.phases & PH_BCAST)) load_q_tile<DC>(qcur, rq, n0 + 16 * wave, n1, d);
+    if (single && (p.phases & PH_BCAST)) load_q_tile<DC>(qcur, rq, n0 + 16 * wave, n1, d, sn);
 #pragma unroll
     for (int a = 0; a < ATW; ++a) st.l[a] = st.lacc[a][0];
 
@@ -1086,14 +1095,14 @@ agent_mfma_kernel(MfmaParams p) {
         // query tiles of the early probabilities (computed during the merge)
 #pragma unroll
         for (int i = 0; i < kEarly; ++i)
-          load_q_tile<DC>(qe[i], rq, n0 + 16 * (wave + kWaves * i), n1, d);
+          load_q_tile<DC>(qe[i], rq, n0 + 16 * (wave + kWaves * i), n1, d, sn);
       } else if (p.phases & PH_BCAST) {
         // the query tile loads travel while the group gathers
-        load_q_tile<DC>(qcur, rq, n0 + 16 * wave, n1, d);
+        load_q_tile<DC>(qcur, rq, n0 + 16 * wave, n1, d, sn);
       }
       ok = group_wait(gs, 1);
     } else if (sync_group && (p.phases & PH_BCAST)) {
-      load_q_tile<DC>(qcur, rq, n0 + 16 * wave, n1, d);
+      load_q_tile<DC>(qcur, rq, n0 + 16 * wave, n1, d, sn);
     }
     AA_STAMP(7);
   }
@@ -1312,13 +1321,13 @@ agent_mfma_kernel(MfmaParams p) {
 #pragma unroll
       for (int i = 0; i < kEarly; ++i) {
         const int qt = wave + kWaves * i;
-        if (qt < nqt) bcast_out<C, DC, KTC>(epf[i], einv[i], VAf, ro, n0 + 16 * qt, n1, d);
+        if (qt < nqt) bcast_out<C, DC, KTC>(epf[i], einv[i], VAf, ro, n0 + 16 * qt, n1, d, sn);
       }
     } else
     for (int qt = wave; qt < nqt; qt += kWaves) {
       bf16x8 qnext[DC];
-      load_q_tile<DC>(qnext, rq, n0 + 16 * (qt + kWaves), n1, d);   // zeros past the end
-      bcast_tile<C, DC, KTC>(qcur, Af, VAf, ro, n0 + 16 * qt, n1, d, p.nag, p.sl2);
+      load_q_tile<DC>(qnext, rq, n0 + 16 * (qt + kWaves), n1, d, sn);   // zeros past the end
+      bcast_tile<C, DC, KTC>(qcur, Af, VAf, ro, n0 + 16 * qt, n1, d, sn, p.nag, p.sl2);
 #pragma unroll
       for (int c = 0; c < DC; ++c) qcur[c] = qnext[c];
     }
@@ -1335,7 +1344,7 @@ agent_mfma_kernel(MfmaParams p) {
 
 // Launch helper instantiated per DC in its own translation unit.
 template <int DC>
-int launch_mfma_dc(const MfmaParams& mp, int ktc, long grid, hipStream_t st);
+int launch_mfma_dc(const MfmaParams& mp, int ktc, bool strided, long grid, hipStream_t st);
 
 template <int DC, int KTC>
 int mfma_lds_bytes_t() { return Cfg<DC, KTC>::TOTAL; }

@@ -22,7 +22,8 @@ namespace aa {
 // (bh, agent): 64 lanes over channels x 4 groups over window rows.
 template <typename T>
 __global__ void __launch_bounds__(256)
-pool_kernel(const T* __restrict__ q, float* __restrict__ A, int h, int w, int d, int s) {
+pool_kernel(const T* __restrict__ q, float* __restrict__ A, int h, int w, int d, int s,
+            Strides sq) {
   const int k = s * s;
   const int agent = blockIdx.x % k;
   const long bh = blockIdx.x / k;
@@ -30,12 +31,12 @@ pool_kernel(const T* __restrict__ q, float* __restrict__ A, int h, int w, int d,
   const int r0 = (i * h) / s, r1 = ((i + 1) * h + s - 1) / s;
   const int c0 = (j * w) / s, c1 = ((j + 1) * w + s - 1) / s;
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  const T* qh = q + bh * (long)h * w * d;
+  const T* qh = q + head_offset(sq, bh);
   __shared__ float red[4][kMaxD];
   for (int c = tx; c < d; c += 64) {
     float acc = 0.f;
     for (int r = r0 + ty; r < r1; r += 4)
-      for (int cc = c0; cc < c1; ++cc) acc += to_f32(qh[((long)r * w + cc) * d + c]);
+      for (int cc = c0; cc < c1; ++cc) acc += to_f32(qh[((long)r * w + cc) * sq.n + c]);
     red[ty][c] = acc;
   }
   __syncthreads();
@@ -63,7 +64,7 @@ template <typename T, int MAXD>
 __global__ void __launch_bounds__(256)
 aggregate_partial_scalar(const float* __restrict__ A, const T* __restrict__ K,
                          const T* __restrict__ V, float* __restrict__ part, int N, int d,
-                         int nag, float sl2, int chunk, int nchunks) {
+                         int nag, float sl2, int chunk, int nchunks, Strides sk) {
   constexpr int TS = MAXD > 64 ? 16 : 32;
   const int ch = blockIdx.x % nchunks;
   const long bh = blockIdx.x / nchunks;
@@ -79,15 +80,15 @@ aggregate_partial_scalar(const float* __restrict__ A, const T* __restrict__ K,
   }
   float m = -INFINITY, l = 0.f;
   const int n0 = ch * chunk, n1 = min(N, n0 + chunk);
-  const T* Kh = K + bh * (long)N * d;
-  const T* Vh = V + bh * (long)N * d;
+  const T* Kh = K + head_offset(sk, bh);
+  const T* Vh = V + head_offset(sk, bh);
   for (int nb = n0; nb < n1; nb += TS) {
     const int cnt = min(TS, n1 - nb);
     __syncthreads();
     for (int idx = t; idx < cnt * d; idx += 256) {
       const int tok = idx / d, c = idx - tok * d;
-      Ks[tok][c] = to_f32(Kh[(long)(nb + tok) * d + c]);
-      Vs[tok][c] = to_f32(Vh[(long)(nb + tok) * d + c]);
+      Ks[tok][c] = to_f32(Kh[(long)(nb + tok) * sk.n + c]);
+      Vs[tok][c] = to_f32(Vh[(long)(nb + tok) * sk.n + c]);
     }
     __syncthreads();
     if (active) {
@@ -158,7 +159,7 @@ template <typename T, int MAXD>
 __global__ void __launch_bounds__(256)
 broadcast_scalar(const T* __restrict__ Q, const float* __restrict__ A,
                  const float* __restrict__ VA, T* __restrict__ O, int N, int d, int nag,
-                 float sl2, int nqblk) {
+                 float sl2, int nqblk, Strides sq) {
   constexpr int AC = MAXD > 64 ? 16 : 32;
   const int qb = blockIdx.x % nqblk;
   const long bh = blockIdx.x / nqblk;
@@ -166,7 +167,7 @@ broadcast_scalar(const T* __restrict__ Q, const float* __restrict__ A,
   const bool active = n < N;
   __shared__ float As[AC][MAXD];
   __shared__ float Vs[AC][MAXD];
-  const T* qrow = Q + (bh * N + (active ? n : 0)) * (long)d;
+  const T* qrow = Q + head_offset(sq, bh) + (long)(active ? n : 0) * sq.n;
   float qv[MAXD], o[MAXD];
 #pragma unroll
   for (int c = 0; c < MAXD; ++c) {
@@ -213,7 +214,7 @@ broadcast_scalar(const T* __restrict__ Q, const float* __restrict__ A,
     m = mx;
   }
   if (active) {
-    T* orow = O + (bh * N + n) * (long)d;
+    T* orow = O + head_offset(sq, bh) + (long)n * sq.n;
     const float inv = 1.0f / l;
 #pragma unroll
     for (int c = 0; c < MAXD; ++c)

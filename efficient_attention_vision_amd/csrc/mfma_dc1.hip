@@ -3,19 +3,20 @@
 
 namespace aa {
 
-template <int KTC>
+template <int KTC, bool STRIDED>
 static int launch_one(const MfmaParams& mp, long grid, hipStream_t st) {
-  agent_mfma_kernel<1, KTC>
+  agent_mfma_kernel<1, KTC, STRIDED>
       <<<dim3((unsigned)grid), dim3(kThreads), (unsigned)Cfg<1, KTC>::TOTAL, st>>>(mp);
   return (int)hipGetLastError();
 }
 
 template <>
-int launch_mfma_dc<1>(const MfmaParams& mp, int ktc, long grid, hipStream_t st) {
+int launch_mfma_dc<1>(const MfmaParams& mp, int ktc, bool strided, long grid, hipStream_t st) {
   switch (ktc) {
-    case 4: return launch_one<4>(mp, grid, st);
-    case 8: return launch_one<8>(mp, grid, st);
-    default: return launch_one<16>(mp, grid, st);
+    case 4: return strided ? launch_one<4, true>(mp, grid, st) : launch_one<4, false>(mp, grid, st);
+    case 8: return strided ? launch_one<8, true>(mp, grid, st) : launch_one<8, false>(mp, grid, st);
+    default:
+      return strided ? launch_one<16, true>(mp, grid, st) : launch_one<16, false>(mp, grid, st);
   }
 }
 

@@ -107,6 +107,24 @@ int agent_attn_forward_ws(const void* q, const void* k, const void* v,
                           void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/* Same as agent_attn_forward_ws with q, k, v and out given by element
+ * strides instead of the dense [B, H, N, d] layout: element (b, h, n, c) is
+ * at b*stride_b + h*stride_h + n*stride_n + c (channels contiguous), the same
+ * strides for all four.  [B, N, H, d] storage, as a projection to H heads
+ * produces, has stride_b = N*H*d, stride_h = d, stride_n = H*d.  Strides must
+ * be positive multiples of 8 elements, stride_n >= d, and no two positions
+ * may share an element (AGENT_ATTN_ERR_SHAPE / AGENT_ATTN_ERR_ALIGN
+ * otherwise); one head may span at most 2^31 bytes.  Caller-supplied agents
+ * stay dense [B, H, s*s, d].  The range from a tensor's first to its last
+ * element must not overlap the workspace, and out's must not overlap those
+ * of the inputs. */
+int agent_attn_forward_strided(const void* q, const void* k, const void* v,
+                               void* out, const void* agents, int B, int H,
+                               int h, int w, int d, int s, long long stride_b,
+                               long long stride_h, long long stride_n,
+                               float scale, int dtype, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
 /* Step 1 alone: agents_f32 [B, H, s*s, d] (float32) = 2-D average pool of q. */
 int agent_attn_pool(const void* q, float* agents_f32, int B, int H, int h,
                     int w, int d, int s, int dtype, void* stream);

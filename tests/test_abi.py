@@ -129,3 +129,26 @@ def test_wait_limit_query_and_set(L):
     assert L.agent_attn_set_wait_limit(123) == prev
     assert L.agent_attn_set_wait_limit(prev) == 123
     assert L.agent_attn_set_wait_limit(-1) == prev
+
+
+def strided(L, sb, sh, sn, *, B=2, H=3, h=8, w=8, d=64, s=4, dtype=1):
+    return L.agent_attn_forward_strided(P[0], P[1], P[2], P[3], None, B, H, h, w, d, s, sb, sh,
+                                        sn, 0.125, dtype, WS, 1 << 40, None)
+
+
+@pytest.mark.parametrize("sb,sh,sn,code", [
+    (64 * 3 * 64, 64, 3 * 64 + 4, ERR_ALIGN),     # token stride not a multiple of 8
+    (64 * 3 * 64, 12, 3 * 64, ERR_ALIGN),          # head stride not a multiple of 8
+    (64 * 3 * 64, 64, 32, ERR_SHAPE),               # token stride below d
+    (64 * 3 * 64, 64, 64, ERR_SHAPE),               # heads and tokens share elements
+    (64 * 64, 64 * 64, 64, ERR_SHAPE),              # batches and heads share elements
+    (0, 64, 3 * 64, ERR_SHAPE),                     # zero stride
+    (-8, 64, 3 * 64, ERR_SHAPE),                    # negative stride
+])
+def test_strided_validation(L, sb, sh, sn, code):
+    assert strided(L, sb, sh, sn) == code
+
+
+def test_strided_huge_head_span_rejected(L):
+    # one head spanning more than 2^31 bytes of bf16
+    assert strided(L, 1 << 34, 1 << 33, 1 << 26, B=1, H=1, h=64, w=64) == ERR_SHAPE

@@ -227,3 +227,49 @@ def test_barrier_timeout_is_reported_and_recovers():
     assert eav.agent_attn_read_faults() == 0
     O, _, _ = oracle.forward(inp.Q.exact, inp.K.exact, inp.V.exact, wl.h, wl.w, wl.s, wl.scale)
     parity.assert_close(to_host_f64(out), O, wl.dtype, "after timeout", kind="discriminating")
+
+
+# ------------------------------------------------------ strided layouts
+
+def _bnhd(t):
+    """The same [B, H, N, d] values stored as [B, N, H, d] (a head-split
+    projection output), returned as the [B, H, N, d] view of that storage."""
+    return t.transpose(1, 2).contiguous().transpose(1, 2)
+
+
+def _packed_qkv(q, k, v):
+    """q, k, v stored interleaved in one [B, N, 3, H, d] tensor."""
+    x = torch.stack([t.transpose(1, 2) for t in (q, k, v)], dim=2).contiguous()
+    return tuple(x[:, :, i].transpose(1, 2) for i in range(3))
+
+
+STRIDED = [
+    (inputs.WORKLOADS["sd_unet"], "bnhd"),
+    (inputs.WORKLOADS["deit_s"], "bnhd"),
+    (inputs.custom("packed_d64", B=2, H=4, h=20, w=20, d=64, s=5), "packed"),
+    (inputs.custom("bnhd_f32", B=2, H=3, h=12, w=12, d=32, s=4, dtype="f32"), "bnhd"),
+    (inputs.custom("packed_f32", B=1, H=2, h=10, w=10, d=64, s=2, dtype="f32"), "packed"),
+    (inputs.custom("bnhd_ragged", B=2, H=3, h=13, w=11, d=48, s=3), "bnhd"),
+]
+
+
+@pytest.mark.parametrize("wl,layout", STRIDED, ids=lambda x: x if isinstance(x, str) else x.name)
+def test_strided_layouts(wl, layout):
+    """q, k, v (and out) as strided views: head-split [B, N, H, d] storage and
+    a packed [B, N, 3, H, d] projection output.  The strided entry point must
+    give the oracle's result, in out's own strides."""
+    say(f"[strided] {wl.name} {layout}")
+    inp = inputs.make_inputs(wl, 8, "discriminating")
+    q, k, v = (to_device(x) for x in (inp.Q, inp.K, inp.V))
+    if layout == "bnhd":
+        qs, ks, vs = _bnhd(q), _bnhd(k), _bnhd(v)
+    else:
+        qs, ks, vs = _packed_qkv(q, k, v)
+    assert not qs.is_contiguous() or wl.H == 1
+    out = eav.agent_attn_forward(qs, ks, vs, (wl.h, wl.w), wl.s, wl.scale)
+    assert out.stride() == qs.stride()
+    torch.cuda.synchronize()
+    assert eav.agent_attn_read_faults() == 0
+    O, _, _ = oracle.forward(inp.Q.exact, inp.K.exact, inp.V.exact, wl.h, wl.w, wl.s, wl.scale)
+    parity.assert_close(to_host_f64(out.contiguous()), O, wl.dtype, wl.name + " " + layout,
+                        kind="discriminating")
