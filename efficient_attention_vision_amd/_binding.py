@@ -17,7 +17,7 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libagent_attn.so")
 
-F32, BF16 = 0, 1
+F32, BF16, F16 = 0, 1, 2   # agent_attn_dtype_t
 OK = 0
 _VALIDATION = {-1, -2, -3, -4, -5, -6, -7, -8}
 
@@ -84,7 +84,9 @@ def _dtype_code(t: torch.Tensor) -> int:
         return F32
     if t.dtype == torch.bfloat16:
         return BF16
-    raise ValueError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+    if t.dtype == torch.float16:
+        return F16
+    raise ValueError(f"unsupported dtype {t.dtype}; use float32, bfloat16 or float16")
 
 
 def _dev_tensor(t, name, ndim=4):
@@ -154,7 +156,8 @@ def agent_attn_forward(q, k, v, grid_hw, s, scale=None, agents=None, out=None, w
     """O = softmax(scale Q A^T) softmax(scale A K^T) V with A = 2-D average
     pool of Q to s x s agents (or `agents` [B, H, s*s, d]).
 
-    q, k, v: [B, H, h*w, d] float32 or bfloat16 GPU tensors; grid_hw = (h, w).
+    q, k, v: [B, H, h*w, d] float32, bfloat16 or float16 GPU tensors;
+    grid_hw = (h, w).
     Dense tensors use agent_attn_forward_ws; views with contiguous channels
     and the same strides for q, k, v (for example x.view(B, N, H, d)
     .transpose(1, 2)) use agent_attn_forward_strided, with `out` given those

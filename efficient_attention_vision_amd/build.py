@@ -12,7 +12,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libagent_attn.so")
-SOURCES = ["agent_attn.hip", "mfma_dc1.hip", "mfma_dc2.hip", "mfma_dc4.hip"]
+SOURCES = ["agent_attn.hip"] + [f"mfma_dc{dc}_{t}.hip" for dc in (1, 2, 4)
+                               for t in ("bf16", "f16")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 COMPILE_FLAGS = [

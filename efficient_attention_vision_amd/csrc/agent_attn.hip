@@ -60,9 +60,9 @@ struct Dims {
 };
 
 int check_dtype(int dtype) {
-  if (dtype != AGENT_ATTN_F32 && dtype != AGENT_ATTN_BF16)
-    return fail(AGENT_ATTN_ERR_DTYPE, "dtype %d is neither AGENT_ATTN_F32 nor AGENT_ATTN_BF16",
-                dtype);
+  if (dtype != AGENT_ATTN_F32 && dtype != AGENT_ATTN_BF16 && dtype != AGENT_ATTN_F16)
+    return fail(AGENT_ATTN_ERR_DTYPE,
+                "dtype %d is not AGENT_ATTN_F32, AGENT_ATTN_BF16 or AGENT_ATTN_F16", dtype);
   return AGENT_ATTN_OK;
 }
 
@@ -435,16 +435,25 @@ long long* g_trace = nullptr;  // profiling builds: per-workgroup phase stamps
 #endif
 std::atomic<long> g_spin_limit{aa::kSpinLimit};   // polls before a group wait gives up
 
-int launch_mfma(int DC, const aa::MfmaParams& mp, long grid, int nag, hipStream_t st) {
+int launch_mfma(int DC, bool f16, const aa::MfmaParams& mp, long grid, int nag,
+                hipStream_t st) {
   // the dense [B, H, N, d] layout has its own kernel instance
   const bool strided = !(mp.sn == mp.d && mp.sh == (long)mp.N * mp.d &&
                          mp.sb == (long)mp.H * mp.N * mp.d);
   const int ktc = mfma_ktc(nag);
   int e;
-  switch (DC) {
-    case 1: e = aa::launch_mfma_dc<1>(mp, ktc, strided, grid, st); break;
-    case 2: e = aa::launch_mfma_dc<2>(mp, ktc, strided, grid, st); break;
-    default: e = aa::launch_mfma_dc<4>(mp, ktc, strided, grid, st); break;
+  if (f16) {
+    switch (DC) {
+      case 1: e = aa::launch_mfma_dc<1, aa::ElemF16>(mp, ktc, strided, grid, st); break;
+      case 2: e = aa::launch_mfma_dc<2, aa::ElemF16>(mp, ktc, strided, grid, st); break;
+      default: e = aa::launch_mfma_dc<4, aa::ElemF16>(mp, ktc, strided, grid, st); break;
+    }
+  } else {
+    switch (DC) {
+      case 1: e = aa::launch_mfma_dc<1, aa::ElemBF16>(mp, ktc, strided, grid, st); break;
+      case 2: e = aa::launch_mfma_dc<2, aa::ElemBF16>(mp, ktc, strided, grid, st); break;
+      default: e = aa::launch_mfma_dc<4, aa::ElemBF16>(mp, ktc, strided, grid, st); break;
+    }
   }
   if (e != hipSuccess) return hip_fail((hipError_t)e, "agent attention matrix-core kernel launch");
   return AGENT_ATTN_OK;
@@ -488,7 +497,7 @@ int run_mfma_phases(const Dims& D, aa::MfmaParams mp, int DC, int phases, bool f
   if (fused) {
     mp.phases = phases;
     mp.fused = 1;
-    return launch_mfma(DC, mp, grid, D.nag, st);
+    return launch_mfma(DC, D.dtype == AGENT_ATTN_F16, mp, grid, D.nag, st);
   }
   mp.fused = 0;
   mp.xcd_heads = 0;
@@ -496,7 +505,7 @@ int run_mfma_phases(const Dims& D, aa::MfmaParams mp, int DC, int phases, bool f
     if (!(phases & ph)) continue;
     if (ph == aa::PH_MERGE && mp.P == 1) continue;
     mp.phases = ph;
-    const int rc = launch_mfma(DC, mp, grid, D.nag, st);
+    const int rc = launch_mfma(DC, D.dtype == AGENT_ATTN_F16, mp, grid, D.nag, st);
     if (rc) return rc;
   }
   return AGENT_ATTN_OK;

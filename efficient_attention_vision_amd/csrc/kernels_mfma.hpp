@@ -119,11 +119,6 @@ struct MfmaParams {
 #endif
 
 // ------------------------------------------------------------ small helpers
-// Eight bf16 ones: the A operand that turns a matrix-core product into
-// column sums of the B operand.
-__device__ __forceinline__ bf16x8 ones_bf16x8() {
-  return __builtin_bit_cast(bf16x8, uint4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
-}
 __device__ __forceinline__ bf16x8 zero_bf16x8() {
   return __builtin_bit_cast(bf16x8, uint4{0u, 0u, 0u, 0u});
 }
@@ -166,6 +161,40 @@ __device__ __forceinline__ float bf16_value(bf16_t b) {
 }
 __device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {
   return (unsigned)bf16_bits(lo) | ((unsigned)bf16_bits(hi) << 16);
+}
+
+// 16-bit element formats of the I/O tensors and of the matrix-core operands.
+// Fragments are kept as 16-byte vectors (bf16x8) for both; only the
+// conversions and the matrix-core instruction depend on the format.
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
+struct ElemBF16 {
+  static constexpr unsigned kOnes2 = 0x3f803f80u;   // two ones
+  static __device__ __forceinline__ uint16_t bits(float x) { return bf16_bits(x); }
+  static __device__ __forceinline__ float value(uint16_t b) { return bf16_value(b); }
+  static __device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+struct ElemF16 {
+  static constexpr unsigned kOnes2 = 0x3c003c00u;
+  static __device__ __forceinline__ uint16_t bits(float x) {
+    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));   // round to nearest even
+  }
+  static __device__ __forceinline__ float value(uint16_t b) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, b));
+  }
+  static __device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+};
+template <class E>
+__device__ __forceinline__ unsigned pack2(float lo, float hi) {
+  return (unsigned)E::bits(lo) | ((unsigned)E::bits(hi) << 16);
+}
+template <class E>
+__device__ __forceinline__ bf16x8 ones8() {
+  return __builtin_bit_cast(bf16x8, uint4{E::kOnes2, E::kOnes2, E::kOnes2, E::kOnes2});
 }
 
 // Buffer accesses.  CPol: kPlain = default caching; kL2 = sc0, which skips
@@ -448,13 +477,14 @@ __device__ __forceinline__ void pool_issue(const MfmaParams& p, rsrc_t rq, int s
   }
 }
 
+template <class E>
 __device__ __forceinline__ void pool_accum(const uint4 (&x)[kPoolTok], float (&acc)[8]) {
 #pragma unroll
   for (int u = 0; u < kPoolTok; ++u) {
     const unsigned w[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-      acc[e] += __uint_as_float((e & 1) ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16));
+      acc[e] += E::value((uint16_t)((e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xffffu)));
   }
 }
 
@@ -502,7 +532,7 @@ struct AggState {
   f32x4 lacc[ATW];   // row sums of the probabilities, on the matrix cores
 };
 
-template <class C, int DC, int ATW>
+template <class E, class C, int DC, int ATW>
 __device__ __forceinline__ void agg_block(AggState<DC, ATW>& st, const bf16_t* Ks,
                                           const bf16x8* Af, const bf16_t* Vt, int blk_col, int ag,
                                           int valid, int d, float sl2) {
@@ -535,8 +565,8 @@ __device__ __forceinline__ void agg_block(AggState<DC, ATW>& st, const bf16_t* K
 #pragma unroll
     for (int c = 0; c < DC; ++c) {
       const bf16x8 af = Af[(t * DC + c) * 64 + lane];
-      S0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0][c], af, S0, 0, 0, 0);
-      S1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][c], af, S1, 0, 0, 0);
+      S0 = E::mma(kf[0][c], af, S0);
+      S1 = E::mma(kf[1][c], af, S1);
     }
     if (valid < 32) {   // rows 16tt + 4g + i past the slice end
 #pragma unroll
@@ -571,13 +601,13 @@ __device__ __forceinline__ void agg_block(AggState<DC, ATW>& st, const bf16_t* K
     }
     union { bf16x8 v; unsigned w[4]; } pf;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) pf.w[e] = pack_bf16(pv[2 * e], pv[2 * e + 1]);
+    for (int e = 0; e < 4; ++e) pf.w[e] = pack2<E>(pv[2 * e], pv[2 * e + 1]);
     // the sum over the block's tokens of the same bf16 probabilities that
     // enter P V (every row of the result holds it)
-    st.lacc[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_bf16x8(), pf.v, st.lacc[a], 0, 0, 0);
+    st.lacc[a] = E::mma(ones8<E>(), pf.v, st.lacc[a]);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
-      st.acc[a][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], pf.v, st.acc[a][dt], 0, 0, 0);
+      st.acc[a][dt] = E::mma(vf[dt], pf.v, st.acc[a][dt]);
   }
 }
 
@@ -600,7 +630,7 @@ __device__ __forceinline__ void load_q_tile(bf16x8 (&qf)[DC], rsrc_t rq, int tok
 // Broadcast logits and softmax of one 16-token query tile: P2 = softmax over
 // the agents of scale * Q A^T, as bf16 B-operand fragments pf[j] (agent pairs
 // of chunk j, see pair_index) and the reciprocal of the row sum.
-template <class C, int DC, int KTC>
+template <class E, class C, int DC, int KTC>
 __device__ __forceinline__ void bcast_probs(const bf16x8 (&qf)[DC], const bf16x8* Af, int nag,
                                             float sl2, bf16x8 (&pf)[C::KC], float& inv) {
   const int lane = threadIdx.x & 63, g = lane >> 4;
@@ -621,8 +651,7 @@ __device__ __forceinline__ void bcast_probs(const bf16x8 (&qf)[DC], const bf16x8
     S[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < DC; ++c)
-      S[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Af[(t * DC + c) * 64 + fl], qf[c], S[t],
-                                                     0, 0, 0);
+      S[t] = E::mma(Af[(t * DC + c) * 64 + fl], qf[c], S[t]);
   }
 #pragma unroll
   for (int t = 0; t < KTC; ++t)
@@ -648,16 +677,16 @@ __device__ __forceinline__ void bcast_probs(const bf16x8 (&qf)[DC], const bf16x8
         pv[4 * h2 + i] = fast_exp2(fmaf(S[2 * j + h2][i], sl2, -off));
     union { bf16x8 v; unsigned w[4]; } u;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) u.w[e] = pack_bf16(pv[2 * e], pv[2 * e + 1]);
+    for (int e = 0; e < 4; ++e) u.w[e] = pack2<E>(pv[2 * e], pv[2 * e + 1]);
     pf[j] = u.v;
-    Lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_bf16x8(), u.v, Lacc, 0, 0, 0);
+    Lacc = E::mma(ones8<E>(), u.v, Lacc);
   }
   inv = 1.0f / Lacc[0];
 }
 
 // Broadcast output of one query tile: O = P2 V_A (V_A as bf16 hi + lo when
 // VSPLIT = 2), normalised, rounded to bf16 and stored.
-template <class C, int DC, int KTC>
+template <class E, class C, int DC, int KTC>
 __device__ __forceinline__ void bcast_out(const bf16x8 (&pf)[C::KC], float inv, const bf16x8* VAf,
                                           rsrc_t ro, int tok0, int tok_end, int d, int sn) {
   constexpr int DT = 2 * DC;
@@ -674,9 +703,9 @@ __device__ __forceinline__ void bcast_out(const bf16x8 (&pf)[C::KC], float inv, 
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       const int f = (j * DT + dt) * 64 + fl;
-      O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(VAf[f], pf[j], O[dt], 0, 0, 0);
+      O[dt] = E::mma(VAf[f], pf[j], O[dt]);
       if (C::VSPLIT > 1)
-        O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(VAf[VA_PART + f], pf[j], O[dt], 0, 0, 0);
+        O[dt] = E::mma(VAf[VA_PART + f], pf[j], O[dt]);
     }
   const int tok = tok0 + r;
   // Lane (r, g) holds channels 16 dt + 4 g .. +3 of token r for every dt.
@@ -688,8 +717,8 @@ __device__ __forceinline__ void bcast_out(const bf16x8 (&pf)[C::KC], float inv, 
   unsigned pk[DT][2];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
-    pk[dt][0] = pack_bf16(O[dt][0] * inv, O[dt][1] * inv);
-    pk[dt][1] = pack_bf16(O[dt][2] * inv, O[dt][3] * inv);
+    pk[dt][0] = pack2<E>(O[dt][0] * inv, O[dt][1] * inv);
+    pk[dt][1] = pack2<E>(O[dt][2] * inv, O[dt][3] * inv);
   }
   constexpr int NS = DT >= 4 ? 2 : 1;
 #pragma unroll
@@ -710,18 +739,18 @@ __device__ __forceinline__ void bcast_out(const bf16x8 (&pf)[C::KC], float inv, 
     }
 }
 
-template <class C, int DC, int KTC>
+template <class E, class C, int DC, int KTC>
 __device__ __forceinline__ void bcast_tile(const bf16x8 (&qf)[DC], const bf16x8* Af,
                                            const bf16x8* VAf, rsrc_t ro, int tok0, int tok_end,
                                            int d, int sn, int nag, float sl2) {
   bf16x8 pf[C::KC];
   float inv;
-  bcast_probs<C, DC, KTC>(qf, Af, nag, sl2, pf, inv);
-  bcast_out<C, DC, KTC>(pf, inv, VAf, ro, tok0, tok_end, d, sn);
+  bcast_probs<E, C, DC, KTC>(qf, Af, nag, sl2, pf, inv);
+  bcast_out<E, C, DC, KTC>(pf, inv, VAf, ro, tok0, tok_end, d, sn);
 }
 
 // ------------------------------------------------------------- the kernel
-template <int DC, int KTC, bool STRIDED>
+template <int DC, int KTC, bool STRIDED, class E>
 __global__ void __launch_bounds__(kThreads)
 agent_mfma_kernel(MfmaParams p) {
   using C = Cfg<DC, KTC>;
@@ -830,7 +859,7 @@ agent_mfma_kernel(MfmaParams p) {
       float acc8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
       for (int ps = 0; ps < pool_npass; ++ps) {
         if (b0 > 0 || ps > 0) pool_issue(p, rq, slot, b0 + tid, pool_items, ps * pool_chunk, px, sn);
-        pool_accum(px, acc8);
+        pool_accum<E>(px, acc8);
         if (b0 == 0 && ps == 0 && (p.phases & PH_AGG)) load_kv0();
       }
       __syncthreads();   // red free
@@ -858,7 +887,7 @@ agent_mfma_kernel(MfmaParams p) {
           const int t16 = a >> 4, r = a & 15, g = c / DC, cc = c - g * DC;
           union { bf16x8 v; unsigned u[4]; } fr;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) fr.u[e] = pack_bf16(s8[2 * e], s8[2 * e + 1]);
+          for (int e = 0; e < 4; ++e) fr.u[e] = pack2<E>(s8[2 * e], s8[2 * e + 1]);
           Af[(t16 * DC + cc) * 64 + 16 * g + r] = fr.v;
         } else if (sync_group) {
           // the group exchanges A as bf16 MFMA fragments: one 16-byte
@@ -866,7 +895,7 @@ agent_mfma_kernel(MfmaParams p) {
           const int t16 = a >> 4, r = a & 15, g = c / DC, cc = c - g * DC;
           union { uint4 v; unsigned u[4]; } fr;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) fr.u[e] = pack_bf16(s8[2 * e], s8[2 * e + 1]);
+          for (int e = 0; e < 4; ++e) fr.u[e] = pack2<E>(s8[2 * e], s8[2 * e + 1]);
           const rsrc_t rf = rsrc_of(reinterpret_cast<char*>(p.agents_f32) + head * C::A_BYTES,
                                     C::A_BYTES);
           const unsigned off = (unsigned)(((t16 * DC + cc) * 64 + 16 * g + r) * 16);
@@ -930,10 +959,10 @@ agent_mfma_kernel(MfmaParams p) {
         x1 = bld16<POL>(ra, off + 16);
         const float4 a0 = bits_f4(x0), a1 = bits_f4(x1);
         union { bf16x8 v; unsigned w[4]; } fr;
-        fr.w[0] = pack_bf16(a0.x, a0.y);
-        fr.w[1] = pack_bf16(a0.z, a0.w);
-        fr.w[2] = pack_bf16(a1.x, a1.y);
-        fr.w[3] = pack_bf16(a1.z, a1.w);
+        fr.w[0] = pack2<E>(a0.x, a0.y);
+        fr.w[1] = pack2<E>(a0.z, a0.w);
+        fr.w[2] = pack2<E>(a1.x, a1.y);
+        fr.w[3] = pack2<E>(a1.z, a1.w);
         if (f < A_FRAGS) Af[f] = fr.v;
       } else {
         const uint4 x = bld16<kPlain>(ra, in ? (unsigned)((agent * d + ch0) * 2) : kOOB);
@@ -973,7 +1002,7 @@ agent_mfma_kernel(MfmaParams p) {
       __syncthreads();
       AA_STAMP(12);
       for (int b = tg; b < rblk; b += C::TG)
-        agg_block<C, DC, ATW>(st, Ks, Af, Vt, 32 * b, ag, min(32, n1 - (rt0 + 32 * b)), d, p.sl2);
+        agg_block<E, C, DC, ATW>(st, Ks, Af, Vt, 32 * b, ag, min(32, n1 - (rt0 + 32 * b)), d, p.sl2);
     }
     AA_STAMP(5);
     if (single && (p.phases & PH_BCAST)) load_q_tile<DC>(qcur, rq, n0 + 16 * wave, n1, d, sn);
@@ -1129,7 +1158,7 @@ agent_mfma_kernel(MfmaParams p) {
 #pragma unroll
       for (int i = 0; i < kEarly; ++i)
         if (wave + kWaves * i < nqt)
-          bcast_probs<C, DC, KTC>(qe[i], Af, p.nag, p.sl2, epf[i], einv[i]);
+          bcast_probs<E, C, DC, KTC>(qe[i], Af, p.nag, p.sl2, epf[i], einv[i]);
     };
     if (early && !merge_wave) early_probs();
     AA_STAMP_BY(15, 0);
@@ -1217,14 +1246,14 @@ agent_mfma_kernel(MfmaParams p) {
         for (int i = 0; i < 4; ++i) {
           const int c = ch + i;
           const int f = (j * DT + (c >> 4)) * 64 + 16 * gg + (c & 15);
-          const bf16_t hi = bf16_bits(v4[i]);
+          const bf16_t hi = E::bits(v4[i]);
           const unsigned off = keep ? (unsigned)((f * 8 + e) * 2) : kOOB;
           if (xp == kXL2 && !C::ROW_PARTIALS)   // streamed like the partials
             __builtin_amdgcn_raw_buffer_store_b16(hi, rvf, (int)off, 0, kL2 | kStream);
           else if (xp == kXL2) __builtin_amdgcn_raw_buffer_store_b16(hi, rvf, (int)off, 0, kL2);
           else __builtin_amdgcn_raw_buffer_store_b16(hi, rvf, (int)off, 0, kCoherent);
           if (C::VSPLIT > 1) {
-            const bf16_t lo = bf16_bits(v4[i] - bf16_value(hi));
+            const bf16_t lo = E::bits(v4[i] - E::value(hi));
             const unsigned offl = keep ? (unsigned)(((VA_FRAGS + f) * 8 + e) * 2) : kOOB;
             if (xp == kXL2 && !C::ROW_PARTIALS)
               __builtin_amdgcn_raw_buffer_store_b16(lo, rvf, (int)offl, 0, kL2 | kStream);
@@ -1304,8 +1333,8 @@ agent_mfma_kernel(MfmaParams p) {
       union { bf16x8 v; bf16_t e[8]; } hi, lo;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        hi.e[e] = bf16_bits(x[e]);
-        lo.e[e] = bf16_bits(x[e] - bf16_value(hi.e[e]));
+        hi.e[e] = E::bits(x[e]);
+        lo.e[e] = E::bits(x[e] - E::value(hi.e[e]));
       }
       if (f < VA_FRAGS) {
         VAf[f] = hi.v;
@@ -1321,13 +1350,13 @@ agent_mfma_kernel(MfmaParams p) {
 #pragma unroll
       for (int i = 0; i < kEarly; ++i) {
         const int qt = wave + kWaves * i;
-        if (qt < nqt) bcast_out<C, DC, KTC>(epf[i], einv[i], VAf, ro, n0 + 16 * qt, n1, d, sn);
+        if (qt < nqt) bcast_out<E, C, DC, KTC>(epf[i], einv[i], VAf, ro, n0 + 16 * qt, n1, d, sn);
       }
     } else
     for (int qt = wave; qt < nqt; qt += kWaves) {
       bf16x8 qnext[DC];
       load_q_tile<DC>(qnext, rq, n0 + 16 * (qt + kWaves), n1, d, sn);   // zeros past the end
-      bcast_tile<C, DC, KTC>(qcur, Af, VAf, ro, n0 + 16 * qt, n1, d, sn, p.nag, p.sl2);
+      bcast_tile<E, C, DC, KTC>(qcur, Af, VAf, ro, n0 + 16 * qt, n1, d, sn, p.nag, p.sl2);
 #pragma unroll
       for (int c = 0; c < DC; ++c) qcur[c] = qnext[c];
     }
@@ -1342,9 +1371,33 @@ agent_mfma_kernel(MfmaParams p) {
 #endif
 }
 
-// Launch helper instantiated per DC in its own translation unit.
-template <int DC>
+// Launch helper, instantiated per (DC, element type) in its own translation
+// unit (mfma_dc<DC>_<type>.hip) so that the instances compile in parallel.
+template <int DC, class E>
 int launch_mfma_dc(const MfmaParams& mp, int ktc, bool strided, long grid, hipStream_t st);
+
+template <int DC, int KTC, bool STRIDED, class E>
+int launch_mfma_one(const MfmaParams& mp, long grid, hipStream_t st) {
+  agent_mfma_kernel<DC, KTC, STRIDED, E>
+      <<<dim3((unsigned)grid), dim3(kThreads), (unsigned)Cfg<DC, KTC>::TOTAL, st>>>(mp);
+  return (int)hipGetLastError();
+}
+
+// Agent tiles of 16: KTC = 4 (<= 64 agents), 8 (<= 128), 16 (<= 256).
+template <int DC, class E>
+int launch_mfma_switch(const MfmaParams& mp, int ktc, bool strided, long grid, hipStream_t st) {
+  switch (ktc) {
+    case 4:
+      return strided ? launch_mfma_one<DC, 4, true, E>(mp, grid, st)
+                     : launch_mfma_one<DC, 4, false, E>(mp, grid, st);
+    case 8:
+      return strided ? launch_mfma_one<DC, 8, true, E>(mp, grid, st)
+                     : launch_mfma_one<DC, 8, false, E>(mp, grid, st);
+    default:
+      return strided ? launch_mfma_one<DC, 16, true, E>(mp, grid, st)
+                     : launch_mfma_one<DC, 16, false, E>(mp, grid, st);
+  }
+}
 
 template <int DC, int KTC>
 int mfma_lds_bytes_t() { return Cfg<DC, KTC>::TOTAL; }

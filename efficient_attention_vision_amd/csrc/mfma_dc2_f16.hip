@@ -1,0 +1,13 @@
+// Instances of the matrix-core kernel for head dims up to 64 (DC = 2),
+// float16 tensors.
+#include "kernels_mfma.hpp"
+
+namespace aa {
+
+template <>
+int launch_mfma_dc<2, ElemF16>(const MfmaParams& mp, int ktc, bool strided, long grid,
+                              hipStream_t st) {
+  return launch_mfma_switch<2, ElemF16>(mp, ktc, strided, grid, st);
+}
+
+}  // namespace aa

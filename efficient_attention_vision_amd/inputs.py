@@ -30,7 +30,7 @@ class Workload:
     w: int          # token-grid columns
     d: int          # head dimension
     s: int          # agent grid side: k = s*s agents
-    dtype: str      # "f32" or "bf16"
+    dtype: str      # "f32", "bf16" or "f16"
     sigma: float    # std of the i.i.d. normal Q, K, V draws
     supplied_agents: bool = False   # caller passes A instead of pooling Q
     agent_sigma: float = 1.0
@@ -90,10 +90,20 @@ def f32_from_bf16_bits(b: np.ndarray) -> np.ndarray:
             << np.uint32(16)).view(np.float32)
 
 
+def f16_bits_from_f32(x: np.ndarray) -> np.ndarray:
+    """float32 -> IEEE binary16 bit patterns (uint16), round to nearest even
+    (numpy's float16 conversion)."""
+    return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def f32_from_f16_bits(b: np.ndarray) -> np.ndarray:
+    return np.asarray(b, dtype=np.uint16).view(np.float16).astype(np.float32)
+
+
 @dataclasses.dataclass
 class Operand:
     """One tensor in its storage format plus its exact value in float64."""
-    storage: np.ndarray   # float32 array, or uint16 bfloat16 bit patterns
+    storage: np.ndarray   # float32 array, or uint16 bfloat16 / float16 bit patterns
     exact: np.ndarray     # the same values, widened exactly to float64
     dtype: str
 
@@ -102,6 +112,9 @@ def _pack(x32: np.ndarray, dtype: str) -> Operand:
     if dtype == "f32":
         x32 = np.ascontiguousarray(x32, dtype=np.float32)
         return Operand(x32, x32.astype(np.float64), dtype)
+    if dtype == "f16":
+        bits = f16_bits_from_f32(x32)
+        return Operand(bits, f32_from_f16_bits(bits).astype(np.float64), dtype)
     bits = bf16_bits_from_f32(x32)
     return Operand(bits, f32_from_bf16_bits(bits).astype(np.float64), dtype)
 

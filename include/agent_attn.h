@@ -23,9 +23,13 @@
  *   q, k, v, out : [B, H, N, d]      (N = h*w)
  *   agents       : [B, H, k, d]      (k = s*s, or n_agents in the step calls)
  *   agents_f32 / agent_values_f32 in the step calls: float32 [B, H, k, d].
- * Element type of q, k, v, out and caller agents: `dtype` (float32 or
- * bfloat16).  Arithmetic is float32 (bf16 inputs feed the matrix cores,
- * accumulation is float32, O is rounded to bf16 with round-to-nearest-even).
+ * Element type of q, k, v, out and caller agents: `dtype` (float32,
+ * bfloat16 or float16).  Arithmetic is float32: 16-bit inputs feed the
+ * matrix cores in their own format, accumulation is float32, and O is
+ * rounded to the I/O format with round-to-nearest-even.  With float16 the
+ * pooled agents, the probabilities and V_A are float16 matrix-core operands;
+ * the partial aggregation sums exchanged between workgroups stay float32 or
+ * bfloat16 (float16 has too little range for unnormalised sums).
  *
  * Pointers: device pointers (hipMalloc/torch CUDA tensors) of the current
  * device, 16-byte aligned.  The library never frees or retains them.
@@ -57,7 +61,8 @@ extern "C" {
 
 typedef enum {
   AGENT_ATTN_F32 = 0,
-  AGENT_ATTN_BF16 = 1
+  AGENT_ATTN_BF16 = 1,
+  AGENT_ATTN_F16 = 2
 } agent_attn_dtype_t;
 
 typedef enum {

@@ -13,7 +13,7 @@ def to_device(op: inputs.Operand | None, device="cuda"):
     if op.dtype == "f32":
         return torch.from_numpy(np.ascontiguousarray(op.storage)).to(device)
     return torch.from_numpy(np.ascontiguousarray(op.storage).view(np.int16)).view(
-        torch.bfloat16).to(device)
+        torch.float16 if op.dtype == "f16" else torch.bfloat16).to(device)
 
 
 def f64_to_device(x: np.ndarray, device="cuda"):
@@ -26,6 +26,9 @@ def to_host_f64(t: torch.Tensor) -> np.ndarray:
     if t.dtype == torch.bfloat16:
         bits = t.view(torch.int16).cpu().numpy().view(np.uint16)
         return inputs.f32_from_bf16_bits(bits).astype(np.float64)
+    if t.dtype == torch.float16:
+        bits = t.view(torch.int16).cpu().numpy().view(np.uint16)
+        return inputs.f32_from_f16_bits(bits).astype(np.float64)
     return t.cpu().numpy().astype(np.float64)
 
 

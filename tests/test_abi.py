@@ -56,6 +56,8 @@ def fwd(L, *, q=P[0], k=P[1], v=P[2], out=P[3], agents=None, B=2, H=3, h=8, w=8,
     (dict(d=136), ERR_UNSUP),
     (dict(d=0), ERR_SHAPE),
     (dict(dtype=7), ERR_DTYPE),
+    (dict(dtype=3), ERR_DTYPE),
+    (dict(dtype=-1), ERR_DTYPE),
     (dict(scale=0.0), ERR_SCALE),
     (dict(scale=float("nan")), ERR_SCALE),
     (dict(scale=float("inf")), ERR_SCALE),
@@ -84,6 +86,15 @@ def test_workspace_bytes(L):
     assert L.agent_attn_workspace_bytes(16, 1, 56, 56, 64, 7, 1) > 0
     assert L.agent_attn_workspace_bytes(16, 1, 56, 56, 12, 7, 1) == 0     # invalid d
     assert L.agent_attn_workspace_bytes(16, 1, 56, 56, 64, 7, 9) == 0     # invalid dtype
+
+
+def test_float16_is_a_16_bit_dtype(L):
+    """float16 plans like bfloat16: the same matrix-core workspace, and the
+    same validation (the dtype itself is accepted)."""
+    assert L.agent_attn_workspace_bytes(16, 1, 56, 56, 64, 7, 2) == \
+        L.agent_attn_workspace_bytes(16, 1, 56, 56, 64, 7, 1)
+    assert fwd(L, dtype=2, d=12) == ERR_UNSUP
+    assert fwd(L, dtype=2, out=P[0]) == ERR_ALIAS
 
 
 def test_step_entry_points_validate(L):

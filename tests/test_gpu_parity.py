@@ -7,6 +7,8 @@ benchmark times.  Edge cases cover ragged grids (windows that overlap by one
 row or column), head dims 8..128, 1..256 agents, a single token, empty
 batches and caller-supplied agents.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -273,3 +275,68 @@ def test_strided_layouts(wl, layout):
     O, _, _ = oracle.forward(inp.Q.exact, inp.K.exact, inp.V.exact, wl.h, wl.w, wl.s, wl.scale)
     parity.assert_close(to_host_f64(out.contiguous()), O, wl.dtype, wl.name + " " + layout,
                         kind="discriminating")
+
+
+# ------------------------------------------------------ float16 tensors
+
+def _as_f16(wl, name=None):
+    return dataclasses.replace(wl, name=name or wl.name + "_f16", dtype="f16")
+
+
+F16_CASES = [_as_f16(inputs.WORKLOADS[n]) for n in
+             ("deit_s", "pvt_stage1", "sd_unet", "sd_unet_agents", "latent_hr")] + [
+    # every head-dim class (d <= 32, 64, 128) and agent-tile count (<= 64,
+    # 128, 256 agents), ragged windows and a single token
+    inputs.custom("f16_d8_s4", B=2, H=2, h=16, w=16, d=8, s=4, dtype="f16"),
+    inputs.custom("f16_ragged_57x55_s7", B=1, H=2, h=57, w=55, d=64, s=7, dtype="f16"),
+    inputs.custom("f16_d96_s10", B=1, H=2, h=40, w=30, d=96, s=10, dtype="f16"),
+    inputs.custom("f16_max_agents_d128", B=1, H=2, h=64, w=48, d=128, s=16, dtype="f16"),
+    inputs.custom("f16_bh100_p2", B=25, H=4, h=20, w=20, d=32, s=5, dtype="f16"),
+    inputs.custom("f16_single_token", B=3, H=1, h=1, w=1, d=64, s=1, dtype="f16"),
+    inputs.custom("f16_supplied_s3", B=2, H=2, h=10, w=10, d=64, s=3, dtype="f16",
+                  supplied_agents=True),
+]
+
+
+@pytest.mark.parametrize("wl", F16_CASES, ids=lambda w: w.name)
+def test_f16_forward(wl):
+    run_case(wl, 30, "iid")
+    run_case(wl, 31, "discriminating")
+
+
+@pytest.mark.parametrize("wl", [F16_CASES[1], F16_CASES[4]], ids=lambda w: w.name)
+def test_f16_steps(wl):
+    """Pool, aggregation and broadcast steps called one by one on float16
+    tensors."""
+    say(f"[f16 steps] {wl.name}")
+    inp = inputs.make_inputs(wl, 32, "discriminating")
+    A = eav.agent_attn_pool(to_device(inp.Q), (wl.h, wl.w), wl.s)
+    refA = oracle.pool_agents(inp.Q.exact, wl.h, wl.w, wl.s)
+    assert np.abs(to_host_f64(A) - refA).max() <= 1e-5 * max(1.0, np.abs(refA).max())
+    A32 = refA.astype(np.float32)
+    VA = eav.agent_attn_aggregate(f64_to_device(A32), to_device(inp.K), to_device(inp.V),
+                                  wl.scale)
+    refVA = oracle.aggregate(A32.astype(np.float64), inp.K.exact, inp.V.exact, wl.scale)
+    parity.assert_close(to_host_f64(VA), refVA, "f16", "aggregate " + wl.name,
+                        kind="discriminating")
+    VA32 = refVA.astype(np.float32)
+    out = eav.agent_attn_broadcast(to_device(inp.Q), f64_to_device(A32), f64_to_device(VA32),
+                                   wl.scale)
+    ref = oracle.broadcast(inp.Q.exact, A32.astype(np.float64), VA32.astype(np.float64),
+                           wl.scale)
+    parity.assert_close(to_host_f64(out), ref, "f16", "broadcast " + wl.name,
+                        kind="discriminating")
+
+
+def test_f16_strided():
+    wl = inputs.custom("f16_bnhd", B=2, H=8, h=32, w=32, d=40, s=8, dtype="f16")
+    say(f"[f16 strided] {wl.name}")
+    inp = inputs.make_inputs(wl, 33, "discriminating")
+    q, k, v = (_bnhd(to_device(x)) for x in (inp.Q, inp.K, inp.V))
+    out = eav.agent_attn_forward(q, k, v, (wl.h, wl.w), wl.s, wl.scale)
+    assert out.dtype == torch.float16 and out.stride() == q.stride()
+    torch.cuda.synchronize()
+    assert eav.agent_attn_read_faults() == 0
+    O, _, _ = oracle.forward(inp.Q.exact, inp.K.exact, inp.V.exact, wl.h, wl.w, wl.s, wl.scale)
+    parity.assert_close(to_host_f64(out.contiguous()), O, "f16", wl.name, kind="discriminating")
+
