@@ -288,8 +288,10 @@ struct GroupSync {
   int* status;
   long spin_limit; // polls before a wait gives up
 };
-__device__ __forceinline__ void group_arrive(const GroupSync& g, int k) {
-  __builtin_amdgcn_s_waitcnt(0);
+// Every wave that stored data the group reads after the barrier must pass
+// `wait` (its stores complete before the flag or counter is published).
+__device__ __forceinline__ void group_arrive(const GroupSync& g, int k, bool wait = true) {
+  if (wait) __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
     if (g.flags) {
@@ -301,11 +303,13 @@ __device__ __forceinline__ void group_arrive(const GroupSync& g, int k) {
     }
   }
 }
-__device__ __forceinline__ bool group_wait(const GroupSync& g, int k) {
+// One wave (`poll_wave`) polls; a wave with no vector loads in flight sees
+// the flags soonest (its poll results do not queue behind those loads).
+__device__ __forceinline__ bool group_wait(const GroupSync& g, int k, int poll_wave = 0) {
   __shared__ int ok;
   if (g.flags) {
-    if (threadIdx.x < 64) {
-      const int lane = threadIdx.x;
+    if ((int)(threadIdx.x >> 6) == poll_wave) {
+      const int lane = threadIdx.x & 63;
       const rsrc_t r = rsrc_of(g.blk, kMaxGroup);
       const int nw = (g.P + 3) >> 2;
       // bytes past P count as arrived
@@ -768,6 +772,24 @@ agent_mfma_kernel(MfmaParams p) {
   float* stage = reinterpret_cast<float*>(big);   // V_A rows [KTC*16][DPAD] (single mode)
   bf16x8* VAf = reinterpret_cast<bf16x8*>(big + (C::STAGE_LDS ? C::STAGE_BYTES : 0));
 
+  // The parameters span four 64-byte lines of the kernel-argument segment.
+  // Fetch them into the scalar cache together, so that the parameter reads
+  // below hit it instead of each paying a dependent miss.
+  {
+    static_assert(sizeof(MfmaParams) <= 256, "parameters beyond four lines");
+    const auto* ka = __builtin_amdgcn_kernarg_segment_ptr();
+    unsigned x0, x1, x2, x3;
+    asm volatile(
+        "s_load_dword %0, %4, 0x0\n\t"
+        "s_load_dword %1, %4, 0x40\n\t"
+        "s_load_dword %2, %4, 0x80\n\t"
+        "s_load_dword %3, %4, 0xc0\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=s"(x0), "=s"(x1), "=s"(x2), "=s"(x3)
+        : "s"(ka));
+    asm volatile("" ::"s"(x0 ^ x1 ^ x2 ^ x3));
+  }
+
   // workgroup -> (head, slot)
   int head, slot;
   if (p.xcd_heads > 0) {
@@ -815,13 +837,21 @@ agent_mfma_kernel(MfmaParams p) {
   const int pool_items = pool_na * DCH * p.pool_tgp;
   const int pool_chunk = p.pool_tgp * kPoolTok;       // window tokens per item pass
   const int pool_npass = (p.pool_maxcnt + pool_chunk - 1) / pool_chunk;
+  const int r0cnt = n1 > n0 ? min(RT, n1 - n0) : 0;
+  const int r0tiles = ((r0cnt + 31) / 32 * 4) * DCH;   // 8x8 K/V tiles of round 0
+  // In a group, when both fit in half the workgroup, the pooling runs on
+  // waves 4..7 while waves 0..3 load the first round's keys and values:
+  // arrival at barrier 0 then waits only for the pooling waves' agent
+  // stores, not for those loads.
+  const bool split_kv = sync_group && (p.phases & PH_POOL) && (p.phases & PH_AGG) &&
+                        pool_items <= kThreads / 2 && r0tiles <= kThreads / 2;
+  const int pool_threads = split_kv ? kThreads / 2 : kThreads;
+  const int pt = split_kv ? tid - kThreads / 2 : tid;   // pooling thread (< 0: none)
   uint4 px[kPoolTok];
-  if (p.phases & PH_POOL) pool_issue(p, rq, slot, tid, pool_items, 0, px, sn);
+  if ((p.phases & PH_POOL) && pt >= 0) pool_issue(p, rq, slot, pt, pool_items, 0, px, sn);
 
   // ---- then K and V of the first round (one 8x8 tile per thread)
   const int ag = wave % C::AG, tg = wave / C::AG;
-  const int r0cnt = n1 > n0 ? min(RT, n1 - n0) : 0;
-  const int r0tiles = ((r0cnt + 31) / 32 * 4) * DCH;
   uint4 kx[8], vx[8];
   // Without pooling they are issued now; with pooling, once the pooling's
   // query loads have landed, so that they do not delay the pooling and
@@ -855,20 +885,30 @@ agent_mfma_kernel(MfmaParams p) {
     }
     const int TGP = p.pool_tgp;
     const float rdch = rcp_approx(DCH);
-    for (int b0 = 0; b0 < pool_items; b0 += kThreads) {
+    for (int b0 = 0; b0 < pool_items; b0 += pool_threads) {
       float acc8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      for (int ps = 0; ps < pool_npass; ++ps) {
-        if (b0 > 0 || ps > 0) pool_issue(p, rq, slot, b0 + tid, pool_items, ps * pool_chunk, px, sn);
-        pool_accum<E>(px, acc8);
-        if (b0 == 0 && ps == 0 && (p.phases & PH_AGG)) load_kv0();
+      if (pt >= 0) {
+        for (int ps = 0; ps < pool_npass; ++ps) {
+          if (b0 > 0 || ps > 0)
+            pool_issue(p, rq, slot, b0 + pt, pool_items, ps * pool_chunk, px, sn);
+          pool_accum<E>(px, acc8);
+          if (b0 == 0 && ps == 0 && (p.phases & PH_AGG) && !sync_group) load_kv0();
+        }
       }
-      __syncthreads();   // red free
-      *reinterpret_cast<float4*>(red + tid * 8) = float4{acc8[0], acc8[1], acc8[2], acc8[3]};
-      *reinterpret_cast<float4*>(red + tid * 8 + 4) = float4{acc8[4], acc8[5], acc8[6], acc8[7]};
+      __syncthreads();   // red free; the pooling loads of Q have landed
+      // the key/value waves of a split load now, behind Q (which starts the
+      // dependency chain) and while the pooling waves sum and publish
+      if (split_kv && b0 == 0 && pt < 0) load_kv0();
+      if (pt >= 0) {
+        *reinterpret_cast<float4*>(red + pt * 8) = float4{acc8[0], acc8[1], acc8[2], acc8[3]};
+        *reinterpret_cast<float4*>(red + pt * 8 + 4) = float4{acc8[4], acc8[5], acc8[6], acc8[7]};
+      }
       __syncthreads();
-      // pairs (m, c) of this batch (TGP divides kThreads)
-      const int pr0 = b0 >> p.pool_tgp_log2, npr = min(kThreads, pool_items - b0) >> p.pool_tgp_log2;
-      for (int o = tid; o < npr; o += kThreads) {
+      // pairs (m, c) of this batch (TGP divides the pooling thread count),
+      // summed and stored by pooling threads
+      const int pr0 = b0 >> p.pool_tgp_log2;
+      const int npr = min(pool_threads, pool_items - b0) >> p.pool_tgp_log2;
+      for (int o = pt; o >= 0 && o < npr; o += pool_threads) {
         const int pr = pr0 + o;
         const int m = idiv(pr, DCH, rdch), c = pr - m * DCH;
         const int a = slot + p.P * m;
@@ -911,17 +951,20 @@ agent_mfma_kernel(MfmaParams p) {
         }
       }
     }
-    if (pool_items == 0 && (p.phases & PH_AGG)) load_kv0();
+    if (pool_items == 0 && (p.phases & PH_AGG) && (!sync_group || (split_kv && pt < 0)))
+      load_kv0();   // no agents to pool here: the loop above did not load them
     AA_STAMP(2);
     if (sync_group) {
-      group_arrive(gs, 0);
-      // the first round's key and value tiles go to LDS while the group gathers
-      if ((p.phases & PH_AGG) && tid < r0tiles) {
-        store_tile_rows(Ks, C::KS_STRIDE, kx, tid, d);
-        store_tile_t(Vt, C::VT_STRIDE, vx, tid, d);
-      }
-      staged0 = (p.phases & PH_AGG) != 0;
-      ok = group_wait(gs, 0);
+      // the key/value waves of a split have nothing to publish: they skip
+      // arrival's wait for their memory operations
+      group_arrive(gs, 0, !(split_kv && pt < 0));
+      // Without the split, the first round's keys and values are loaded
+      // only now (arrival waits for every load in flight of its wave, so
+      // loads issued during the pooling would hold it back until they
+      // land); they travel while the group gathers.  The last wave, which
+      // has none of them, polls.
+      if (!split_kv && (p.phases & PH_AGG) && wave * 64 < r0tiles) load_kv0();
+      ok = group_wait(gs, 0, kWaves - 1);
     }
     AA_STAMP(3);
   }
@@ -1001,8 +1044,16 @@ agent_mfma_kernel(MfmaParams p) {
       }
       __syncthreads();
       AA_STAMP(12);
-      for (int b = tg; b < rblk; b += C::TG)
+      for (int b = tg; b < rblk; b += C::TG) {
         agg_block<E, C, DC, ATW>(st, Ks, Af, Vt, 32 * b, ag, min(32, n1 - (rt0 + 32 * b)), d, p.sl2);
+#ifdef AGENT_ATTN_PHASE_TRACE
+        if (b / C::TG < 4) {
+          __builtin_amdgcn_s_waitcnt(0);
+          AA_STAMP_BY(18 + b / C::TG, 0);
+          AA_STAMP_BY(22 + b / C::TG, 64 * (kWaves - 1));
+        }
+#endif
+      }
     }
     AA_STAMP(5);
     if (single && (p.phases & PH_BCAST)) load_q_tile<DC>(qcur, rq, n0 + 16 * wave, n1, d, sn);
@@ -1050,6 +1101,7 @@ agent_mfma_kernel(MfmaParams p) {
         }
       }
     }
+    AA_STAMP(26);
     // wave (ag, 0) now holds the workgroup's partial for its agent tiles
     const int g = lane >> 4;
     if (p.P == 1) {
