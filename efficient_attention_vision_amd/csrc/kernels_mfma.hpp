@@ -159,8 +159,13 @@ __device__ __forceinline__ bf16_t bf16_bits(float x) {
 __device__ __forceinline__ float bf16_value(bf16_t b) {
   return __uint_as_float(static_cast<unsigned>(b) << 16);
 }
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+// two floats -> one dword of two bfloat16 (lo in bits 0..15), one
+// v_cvt_pk_bf16_f32 (round to nearest even)
 __device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {
-  return (unsigned)bf16_bits(lo) | ((unsigned)bf16_bits(hi) << 16);
+  return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
 // 16-bit element formats of the I/O tensors and of the matrix-core operands.
@@ -171,6 +176,7 @@ struct ElemBF16 {
   static constexpr unsigned kOnes2 = 0x3f803f80u;   // two ones
   static __device__ __forceinline__ uint16_t bits(float x) { return bf16_bits(x); }
   static __device__ __forceinline__ float value(uint16_t b) { return bf16_value(b); }
+  static __device__ __forceinline__ unsigned pack2(float lo, float hi) { return pack_bf16(lo, hi); }
   static __device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
@@ -183,6 +189,9 @@ struct ElemF16 {
   static __device__ __forceinline__ float value(uint16_t b) {
     return static_cast<float>(__builtin_bit_cast(_Float16, b));
   }
+  static __device__ __forceinline__ unsigned pack2(float lo, float hi) {   // v_cvt_pk_f16_f32
+    return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2_t){lo, hi}, f16x2_t));
+  }
   static __device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
@@ -190,7 +199,7 @@ struct ElemF16 {
 };
 template <class E>
 __device__ __forceinline__ unsigned pack2(float lo, float hi) {
-  return (unsigned)E::bits(lo) | ((unsigned)E::bits(hi) << 16);
+  return E::pack2(lo, hi);
 }
 template <class E>
 __device__ __forceinline__ bf16x8 ones8() {
@@ -531,7 +540,7 @@ __device__ __forceinline__ void store_tile_rows(bf16_t* Ks, int ks_stride, const
 // One wave: agent tiles [ATW*ag, ATW*ag + ATW) over its 32-token blocks.
 template <int DC, int ATW>
 struct AggState {
-  float m[ATW], l[ATW];
+  float m[ATW], l[ATW], thr[ATW];
   f32x4 acc[ATW][2 * DC];
   f32x4 lacc[ATW];   // row sums of the probabilities, on the matrix cores
 };
@@ -539,20 +548,18 @@ struct AggState {
 template <class E, class C, int DC, int ATW>
 __device__ __forceinline__ void agg_block(AggState<DC, ATW>& st, const bf16_t* Ks,
                                           const bf16x8* Af, const bf16_t* Vt, int blk_col, int ag,
-                                          int valid, int d, float sl2) {
+                                          int valid, float sl2) {
   constexpr int DT = 2 * DC;
   const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
   // K fragments: token row blk_col + 16tt + r, channel chunk DC*g + c
-  // (chunks at or past d are never staged: zero them)
+  // (chunks at or past d hold zeros)
   bf16x8 kf[2][DC];
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-    for (int c = 0; c < DC; ++c) {
-      const int ch0 = 8 * (DC * g + c);
-      const bf16x8 x = *reinterpret_cast<const bf16x8*>(Ks + (blk_col + 16 * tt + r) * C::KS_STRIDE + ch0);
-      kf[tt][c] = ch0 < d ? x : zero_bf16x8();
-    }
+    for (int c = 0; c < DC; ++c)
+      kf[tt][c] = *reinterpret_cast<const bf16x8*>(Ks + (blk_col + 16 * tt + r) * C::KS_STRIDE +
+                                                   8 * (DC * g + c));
   // V^T fragments: channel row 16dt + r, tokens {4g..4g+3, 16+4g..16+4g+3}
   bf16x8 vf[DT];
 #pragma unroll
@@ -579,22 +586,29 @@ __device__ __forceinline__ void agg_block(AggState<DC, ATW>& st, const bf16_t* K
         if (16 + 4 * g + i >= valid) S1[i] = -INFINITY;
       }
     }
-    float bm = fmaxf(fmaxf(fmaxf(S0[0], S0[1]), fmaxf(S0[2], S0[3])),
-                     fmaxf(fmaxf(S1[0], S1[1]), fmaxf(S1[2], S1[3])));
-    bm = group4_max(bm);
     // Lazy rescaling: the reference max m of a row moves (and the running
     // sum and accumulators are rescaled) only when a block's max exceeds it
-    // by more than 8 in the log2 domain, so probabilities stay below 2^8:
-    // exact in the fp32 sums, and no loss in bf16, whose precision is
-    // relative.  The first block always sets m (m starts at -inf).
-    const bool grow = (bm - st.m[a]) * sl2 > 8.f;
-    if (__any(grow)) {
+    // by more than 8 in the log2 domain (a score above thr = m + 8 / sl2),
+    // so probabilities stay below 2^8: exact in the fp32 sums, and no loss
+    // in bf16, whose precision is relative.  The first block always sets m
+    // (m and thr start at -inf).  Each lane compares its own 8 scores; only
+    // when one exceeds does the row max over the lane groups get formed.
+    const float thr = st.thr[a];
+    bool over = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) over = over || S0[i] > thr || S1[i] > thr;
+    if (__any(over)) {
+      const float lm = fmaxf(fmaxf(fmaxf(S0[0], S0[1]), fmaxf(S0[2], S0[3])),
+                             fmaxf(fmaxf(S1[0], S1[1]), fmaxf(S1[2], S1[3])));
+      const float bm = group4_max(lm);
+      const bool grow = (bm - st.m[a]) * sl2 > 8.f;
       const float mn = grow ? bm : st.m[a];
       const float corr = grow ? fast_exp2((st.m[a] - mn) * sl2) : 1.f;
       st.lacc[a] *= corr;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) st.acc[a][dt] *= corr;
       st.m[a] = mn;
+      st.thr[a] = mn + 8.f / sl2;
     }
     const float off = st.m[a] * sl2;
     float pv[8];
@@ -865,7 +879,6 @@ agent_mfma_kernel(MfmaParams p) {
   // first query tile of this wave, loaded ahead of the broadcast
   const int nqt = n1 > n0 ? (n1 - n0 + 15) / 16 : 0;
   bf16x8 qcur[DC];
-  bool staged0 = false;   // first round already in LDS
   // With up to 64 agents, the broadcast probabilities of up to kEarly tiles
   // per wave are computed while the group gathers at barrier 1 (they need
   // only A and Q); only P2 V_A is left after V_A arrives.
@@ -1023,6 +1036,7 @@ agent_mfma_kernel(MfmaParams p) {
 #pragma unroll
     for (int a = 0; a < ATW; ++a) {
       st.m[a] = -INFINITY;
+      st.thr[a] = -INFINITY;
       st.l[a] = 0.f;
       st.lacc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1038,19 +1052,29 @@ agent_mfma_kernel(MfmaParams p) {
         load_tile8(kx, rk, tid, rt0, tend, d, sn);
         load_tile8(vx, rv, tid, rt0, tend, d, sn);
       }
-      if (tid < ntile && !(staged0 && rt0 == n0)) {
+      if (tid < ntile) {
         store_tile_rows(Ks, C::KS_STRIDE, kx, tid, d);
         store_tile_t(Vt, C::VT_STRIDE, vx, tid, d);
+      }
+      // below the padded head dim, the key columns [d, DPAD) that the score
+      // products read are cleared (the LDS holds other phases' data)
+      const int npad = DPAD / 8 - DCH;
+      for (int i = tid; i < rblk * 32 * npad; i += kThreads) {
+        const int row = idiv(i, npad, rcp_approx(npad));
+        *reinterpret_cast<uint4*>(Ks + row * C::KS_STRIDE + 8 * (DCH + i - row * npad)) =
+            uint4{0u, 0u, 0u, 0u};
       }
       __syncthreads();
       AA_STAMP(12);
       for (int b = tg; b < rblk; b += C::TG) {
-        agg_block<E, C, DC, ATW>(st, Ks, Af, Vt, 32 * b, ag, min(32, n1 - (rt0 + 32 * b)), d, p.sl2);
+        agg_block<E, C, DC, ATW>(st, Ks, Af, Vt, 32 * b, ag, min(32, n1 - (rt0 + 32 * b)), p.sl2);
 #ifdef AGENT_ATTN_PHASE_TRACE
         if (b / C::TG < 4) {
           __builtin_amdgcn_s_waitcnt(0);
           AA_STAMP_BY(18 + b / C::TG, 0);
           AA_STAMP_BY(22 + b / C::TG, 64 * (kWaves - 1));
+          if (p.trace && threadIdx.x == 0 && (b == 0 || b / C::TG == 3))
+            p.trace[(long)blockIdx.x * 32 + (b == 0 ? 28 : 29)] = (long long)clock64();
         }
 #endif
       }
