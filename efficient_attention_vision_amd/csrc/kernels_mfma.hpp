@@ -1154,8 +1154,8 @@ agent_mfma_kernel(MfmaParams p) {
         }
       }
     } else if (tg == 0) {
-      // partials: agent rows of DPAD channels (the merge reads whole rows)
-      // or, with up to 64 agents, register order (1 KiB per tile and dt)
+      // partials: agent rows of DPAD channels (the merge reads whole rows),
+      // bf16 from 128 agents, fp32 below
       const long pbase = ((long)head * p.P + slot) * KTC;
       const rsrc_t racc = rsrc_of(p.part_acc + pbase * DT * 256, (unsigned)(KTC * DT * 1024));
       const rsrc_t rml = rsrc_of(p.part_ml + pbase * 32, (unsigned)(KTC * 128));
@@ -1175,7 +1175,9 @@ agent_mfma_kernel(MfmaParams p) {
             xst8(xp, racc, off, uint2{pack_bf16(st.acc[a][dt][0], st.acc[a][dt][1]),
                                       pack_bf16(st.acc[a][dt][2], st.acc[a][dt][3])});
           } else {
-            const unsigned off = real ? (unsigned)(((t * DT + dt) * 64 + lane) * 16) : kOOB;
+            // fp32 agent rows: quad 4 dt + g of agent 16 t + r
+            const unsigned off =
+                real ? (unsigned)(((16 * t + (lane & 15)) * 4 * DT + 4 * dt + g) * 16) : kOOB;
             const uint4 x = f4_bits(float4{st.acc[a][dt][0], st.acc[a][dt][1], st.acc[a][dt][2],
                                            st.acc[a][dt][3]});
             // small partial sets (up to 64 agents) are streamed (nt), so the
@@ -1246,7 +1248,7 @@ agent_mfma_kernel(MfmaParams p) {
       const int a = slot + p.P * m;
       const int t = a >> 4, r = a & 15, dt = q >> 2, g = q & 3;
       const unsigned aoff = C::ROW_PARTIALS ? (unsigned)((a * DPAD + 4 * q) * 2)
-                                            : (unsigned)(((t * DT + dt) * 64 + 16 * g + r) * 16);
+                                            : (unsigned)((a * nq + q) * 16);
       const unsigned moff = (unsigned)((t * 16 + r) * 8);
       constexpr unsigned sstride_acc = KTC * DT * 1024, sstride_ml = KTC * 128;
       float M = -INFINITY, Ls = 0.f;
