@@ -799,7 +799,7 @@ agent_mfma_kernel(MfmaParams p) {
         "s_load_dword %2, %4, 0x80\n\t"
         "s_load_dword %3, %4, 0xc0\n\t"
         "s_waitcnt lgkmcnt(0)"
-        : "=s"(x0), "=s"(x1), "=s"(x2), "=s"(x3)
+        : "=&s"(x0), "=&s"(x1), "=&s"(x2), "=&s"(x3)   // results must not overwrite the address
         : "s"(ka));
     asm volatile("" ::"s"(x0 ^ x1 ^ x2 ^ x3));
   }
