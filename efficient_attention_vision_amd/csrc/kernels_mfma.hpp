@@ -1047,14 +1047,19 @@ agent_mfma_kernel(MfmaParams p) {
       const int rblk = (rcnt + 31) / 32;
       const int ntile = rblk * 4 * DCH;
       __syncthreads();   // previous round (or the pooling sums) fully read
-      if (rt0 != n0) {
-        const int tend = tid < ntile ? rt0 + rcnt : -1;
-        load_tile8(kx, rk, tid, rt0, tend, d, sn);
-        load_tile8(vx, rv, tid, rt0, tend, d, sn);
-      }
       if (tid < ntile) {
         store_tile_rows(Ks, C::KS_STRIDE, kx, tid, d);
         store_tile_t(Vt, C::VT_STRIDE, vx, tid, d);
+      }
+      // the next round's tiles travel while this round is aggregated
+      if (rt0 + RT < n1) {
+        const int ncnt = min(RT, n1 - rt0 - RT);
+        const int ntn = (ncnt + 31) / 32 * 4 * DCH;
+        if (wave * 64 < ntn) {
+          const int tend = tid < ntn ? rt0 + RT + ncnt : -1;
+          load_tile8(kx, rk, tid, rt0 + RT, tend, d, sn);
+          load_tile8(vx, rv, tid, rt0 + RT, tend, d, sn);
+        }
       }
       // below the padded head dim, the key columns [d, DPAD) that the score
       // products read are cleared (the LDS holds other phases' data)
