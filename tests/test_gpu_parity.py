@@ -79,6 +79,10 @@ EDGE = [
     inputs.custom("bh260_p1", B=26, H=10, h=8, w=8, d=64, s=4),
     # a long sequence: 256 x 256 grid, 256 agents
     inputs.custom("long_256x256", B=1, H=2, h=256, w=256, d=64, s=16),
+    # one workgroup per head with 100 agents (grouped broadcast, partial
+    # groups of query tiles, padding agents in the last chunk)
+    inputs.custom("p1_100_agents", B=40, H=8, h=20, w=20, d=64, s=10),
+    inputs.custom("p1_100_agents_d32", B=33, H=8, h=20, w=20, d=32, s=10),
     # caller-supplied agents with ragged counts
     inputs.custom("supplied_s3", B=2, H=2, h=10, w=10, d=64, s=3, supplied_agents=True),
     inputs.custom("supplied_f32", B=1, H=2, h=10, w=12, d=48, s=2, dtype="f32",
