@@ -3,5 +3,5 @@
 Imported by tests/, the smoke check and the benchmark's CPU-baseline leg;
 never by the product path.
 """
-from .agent_oracle import (aggregate, broadcast, forward, pool_agents,  # noqa: F401
+from .agent_oracle import (aggregate, broadcast, dwc, forward, pool_agents,  # noqa: F401
                            softmax_last, window_bounds)

@@ -32,8 +32,20 @@ Readings where the pages leave a step open:
     are the plain non-overlapping block means.
   * one scale factor (1/sqrt(d) in every workload) is applied in both
     softmaxes, as in the [JSQMD] §1 pseudocode.
-  * the broadcast keys are the agents A (not V_A); agent bias, the
-    depth-wise convolution and projections are not part of this operator.
+  * the broadcast keys are the agents A (not V_A); projections are not part
+    of this operator.
+  * module enhancements ([Paper] §4 Module Enhancements and Implementation
+    Details), optional: agent biases B1 and B2 enter the two attentions as
+    additive terms of the scaled logits, softmax(scale A K^T + B1) and
+    softmax(scale Q A^T + B2).  The pages name their construction from
+    column, row and block components but do not give it, so the full bias
+    tensors are inputs here: B1 [H, k, N] and B2 [H, N, k], shared by the
+    batch (they are per-head parameters).  The depth-wise convolution term
+    has kernel size 3 ([Paper] §4 Efficiency: k^2 N C with k = 3): DWC(V) is
+    a per-channel 3 x 3 convolution (cross-correlation, as deep-learning
+    convolutions are) of V over the h x w grid with zero padding of one,
+    weights W [H*d, 3, 3] and bias b [H*d] (channel c of head h is model
+    channel h*d + c), added to the output: O = broadcast + DWC(V).
   * softmax runs over the last axis: over the N keys in aggregation, over
     the k agents in broadcast.
 Every function is pinned by tests (library cross-checks, closed forms,
@@ -77,30 +89,73 @@ def softmax_last(S: np.ndarray) -> np.ndarray:
     return P
 
 
-def aggregate(A: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndarray:
-    """Agent aggregation: V_A = softmax(scale * A K^T) V, per (b, h).
+def aggregate(A: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float,
+              bias=None) -> np.ndarray:
+    """Agent aggregation: V_A = softmax(scale * A K^T [+ B1]) V, per (b, h).
 
     A: [B, H, k, d], K, V: [B, H, N, d] -> V_A: [B, H, k, d].
+    bias: None or B1 [H, k, N], added to the scaled logits of every batch
+    entry ([Paper] §4 Module Enhancements: agent bias in both attentions).
     ([JSQMD] §1, stage one; [Paper] §4, first Softmax attention.)
     """
     S1 = scale * (A @ np.swapaxes(K, -1, -2))          # [B, H, k, N]
+    if bias is not None:
+        S1 = S1 + np.asarray(bias, dtype=np.float64)[None]
     return softmax_last(S1) @ V
 
 
-def broadcast(Q: np.ndarray, A: np.ndarray, V_A: np.ndarray, scale: float) -> np.ndarray:
-    """Agent broadcast: O = softmax(scale * Q A^T) V_A, per (b, h).
+def broadcast(Q: np.ndarray, A: np.ndarray, V_A: np.ndarray, scale: float,
+              bias=None) -> np.ndarray:
+    """Agent broadcast: O = softmax(scale * Q A^T [+ B2]) V_A, per (b, h).
 
     Q: [B, H, N, d], A, V_A: [B, H, k, d] -> O: [B, H, N, d].
+    bias: None or B2 [H, N, k], added to the scaled logits of every batch
+    entry ([Paper] §4 Module Enhancements).
     ([JSQMD] §1, stage two; [Paper] §4, second Softmax attention.)
     """
     S2 = scale * (Q @ np.swapaxes(A, -1, -2))          # [B, H, N, k]
+    if bias is not None:
+        S2 = S2 + np.asarray(bias, dtype=np.float64)[None]
     return softmax_last(S2) @ V_A
 
 
-def forward(Q, K, V, h: int, w: int, s: int, scale: float, A=None):
+def dwc(V: np.ndarray, h: int, w: int, weight: np.ndarray, bias=None) -> np.ndarray:
+    """Depth-wise 3 x 3 convolution of V over the h x w token grid.
+
+    out[b, hd, r*w + c, ch] = bias[hd*d + ch]
+        + sum over dy, dx in {-1, 0, 1} of
+          weight[hd*d + ch, dy + 1, dx + 1] * V[b, hd, (r+dy)*w + (c+dx), ch],
+    where taps outside the grid contribute zero (padding one).
+    V: [B, H, h*w, d]; weight: [H*d, 3, 3]; bias: None (zero) or [H*d].
+    ([Paper] §4 Module Enhancements and Efficiency: the depth-wise
+    convolution term, kernel size 3.)
+    """
+    V = np.asarray(V, dtype=np.float64)
+    B, H, N, d = V.shape
+    assert N == h * w
+    W = np.asarray(weight, dtype=np.float64).reshape(H, d, 3, 3)
+    bb = np.zeros((H, d)) if bias is None else np.asarray(bias, dtype=np.float64).reshape(H, d)
+    grid = V.reshape(B, H, h, w, d)
+    out = np.empty_like(grid)
+    out[...] = bb[None, :, None, None, :]
+    for dy in (-1, 0, 1):
+        for dx in (-1, 0, 1):
+            # rows r with 0 <= r + dy < h, columns c with 0 <= c + dx < w
+            r0, r1 = max(0, -dy), min(h, h - dy)
+            c0, c1 = max(0, -dx), min(w, w - dx)
+            tap = W[:, :, dy + 1, dx + 1]                      # [H, d]
+            out[:, :, r0:r1, c0:c1, :] += (tap[None, :, None, None, :] *
+                                           grid[:, :, r0 + dy:r1 + dy, c0 + dx:c1 + dx, :])
+    return out.reshape(B, H, N, d)
+
+
+def forward(Q, K, V, h: int, w: int, s: int, scale: float, A=None, bias_agg=None,
+            bias_bcast=None, dwc_weight=None, dwc_bias=None):
     """Full forward.  Returns (O, A, V_A), all float64.
 
     Q, K, V: [B, H, h*w, d]; A: None (pool Q to s x s) or [B, H, s*s, d].
+    Optional module terms: bias_agg B1 [H, k, N], bias_bcast B2 [H, N, k],
+    dwc_weight [H*d, 3, 3] with dwc_bias [H*d] (O += DWC(V)).
     """
     Q = np.asarray(Q, dtype=np.float64)
     K = np.asarray(K, dtype=np.float64)
@@ -110,6 +165,8 @@ def forward(Q, K, V, h: int, w: int, s: int, scale: float, A=None):
     else:
         A = np.asarray(A, dtype=np.float64)
         assert A.shape == Q.shape[:2] + (s * s, Q.shape[3])
-    V_A = aggregate(A, K, V, scale)
-    O = broadcast(Q, A, V_A, scale)
+    V_A = aggregate(A, K, V, scale, bias_agg)
+    O = broadcast(Q, A, V_A, scale, bias_bcast)
+    if dwc_weight is not None:
+        O = O + dwc(V, h, w, dwc_weight, dwc_bias)
     return O, A, V_A

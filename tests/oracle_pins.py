@@ -293,4 +293,129 @@ def pin_brute_force_generalised_linear_attention(orc):
         assert np.allclose(O[0, 0], ref, rtol=0, atol=1e-12)
 
 
+# ------------------------------------------- module terms: agent biases, DWC
+
+def _sdpa_mask(q, k, v, mask, scale):
+    """torch's float64 attention with an additive float mask on the scaled
+    logits (broadcast over the batch)."""
+    return F.scaled_dot_product_attention(_t(q), _t(k), _t(v), attn_mask=_t(mask),
+                                          scale=scale).numpy()
+
+
+def pin_aggregate_bias_is_masked_attention(orc):
+    """With B1, the aggregation is torch's attention with B1 as its additive
+    float mask ([Paper] §4: the bias enters the attention logits)."""
+    rng = _rng(61)
+    B, H, N, k, d, scale = 2, 3, 11, 5, 4, 0.7
+    A, K, V = (rng.standard_normal(sh) for sh in ((B, H, k, d), (B, H, N, d), (B, H, N, d)))
+    B1 = 2.0 * rng.standard_normal((H, k, N))
+    got = orc.aggregate(A, K, V, scale, B1)
+    assert np.allclose(got, _sdpa_mask(A, K, V, B1[None], scale), rtol=0, atol=1e-12)
+
+
+def pin_broadcast_bias_is_masked_attention(orc):
+    rng = _rng(62)
+    B, H, N, k, d, scale = 2, 2, 9, 6, 5, 0.6
+    Q, A, VA = (rng.standard_normal(sh) for sh in ((B, H, N, d), (B, H, k, d), (B, H, k, d)))
+    B2 = 2.0 * rng.standard_normal((H, N, k))
+    got = orc.broadcast(Q, A, VA, scale, B2)
+    assert np.allclose(got, _sdpa_mask(Q, A, VA, B2[None], scale), rtol=0, atol=1e-12)
+
+
+def pin_row_constant_bias_changes_nothing(orc):
+    """A bias that is constant along the softmax axis cancels (softmax is
+    invariant to a per-row shift)."""
+    rng = _rng(63)
+    B, H, N, k, d, scale = 1, 2, 10, 4, 3, 0.8
+    Q, K, V = (rng.standard_normal((B, H, N, d)) for _ in range(3))
+    A = rng.standard_normal((B, H, k, d))
+    c1 = np.repeat(rng.standard_normal((H, k, 1)) * 5, N, axis=2)
+    c2 = np.repeat(rng.standard_normal((H, N, 1)) * 5, k, axis=2)
+    assert np.allclose(orc.aggregate(A, K, V, scale, c1), orc.aggregate(A, K, V, scale),
+                       rtol=0, atol=1e-12)
+    VA = orc.aggregate(A, K, V, scale)
+    assert np.allclose(orc.broadcast(Q, A, VA, scale, c2), orc.broadcast(Q, A, VA, scale),
+                       rtol=0, atol=1e-12)
+
+
+def pin_bias_selects_one_key(orc):
+    """A bias of 0 on one key and -1e4 elsewhere makes every agent's value
+    that key's value row (closed form)."""
+    rng = _rng(64)
+    B, H, N, k, d = 1, 1, 8, 3, 4
+    A, K, V = (rng.standard_normal(sh) for sh in ((B, H, k, d), (B, H, N, d), (B, H, N, d)))
+    B1 = np.full((H, k, N), -1e4)
+    pick = [5, 0, 7]
+    for i, m in enumerate(pick):
+        B1[0, i, m] = 0.0
+    VA = orc.aggregate(A, K, V, 0.5, B1)
+    assert np.allclose(VA[0, 0], V[0, 0, pick], rtol=0, atol=1e-12)
+
+
+def _dwc_torch(V, h, w, weight, bias):
+    B, H, N, d = V.shape
+    x = _t(V).reshape(B, H, h, w, d).permute(0, 1, 4, 2, 3).reshape(B, H * d, h, w)
+    y = F.conv2d(x, _t(weight).reshape(H * d, 1, 3, 3), _t(bias), padding=1, groups=H * d)
+    return y.reshape(B, H, d, h, w).permute(0, 1, 3, 4, 2).reshape(B, H, N, d).numpy()
+
+
+def pin_dwc_vs_conv2d(orc):
+    """DWC equals torch's grouped conv2d (one group per channel, padding 1),
+    on a non-square grid so that a row/column mix-up shows."""
+    rng = _rng(65)
+    B, H, h, w, d = 2, 2, 5, 7, 3
+    V = rng.standard_normal((B, H, h * w, d))
+    W = rng.standard_normal((H * d, 3, 3))
+    b = rng.standard_normal(H * d)
+    assert np.allclose(orc.dwc(V, h, w, W, b), _dwc_torch(V, h, w, W, b), rtol=0, atol=1e-12)
+
+
+def pin_dwc_center_tap_is_identity(orc):
+    rng = _rng(66)
+    V = rng.standard_normal((1, 2, 12, 4))
+    W = np.zeros((8, 3, 3))
+    W[:, 1, 1] = 1.0
+    assert np.array_equal(orc.dwc(V, 3, 4, W), V)
+
+
+def pin_dwc_explicit_loops(orc):
+    """Per-element loops with explicit bounds checks on a tiny grid."""
+    rng = _rng(67)
+    B, H, h, w, d = 1, 2, 3, 4, 2
+    V = rng.standard_normal((B, H, h * w, d))
+    W = rng.standard_normal((H * d, 3, 3))
+    b = rng.standard_normal(H * d)
+    got = orc.dwc(V, h, w, W, b)
+    for hd in range(H):
+        for r in range(h):
+            for c in range(w):
+                for ch in range(d):
+                    acc = b[hd * d + ch]
+                    for dy in (-1, 0, 1):
+                        for dx in (-1, 0, 1):
+                            rr, cc = r + dy, c + dx
+                            if 0 <= rr < h and 0 <= cc < w:
+                                acc += W[hd * d + ch, dy + 1, dx + 1] * V[0, hd, rr * w + cc, ch]
+                    assert abs(got[0, hd, r * w + c, ch] - acc) < 1e-12
+
+
+def pin_forward_module_is_library_composition(orc):
+    """Pooling, two masked attentions and conv2d, composed from library
+    routines, equal the oracle's forward with every module term."""
+    rng = _rng(68)
+    B, H, h, w, d, s, scale = 2, 2, 6, 5, 4, 2, 0.5
+    N, k = h * w, s * s
+    Q, K, V = (rng.standard_normal((B, H, N, d)) for _ in range(3))
+    B1 = rng.standard_normal((H, k, N))
+    B2 = rng.standard_normal((H, N, k))
+    W = rng.standard_normal((H * d, 3, 3))
+    b = rng.standard_normal(H * d)
+    O, A, _ = orc.forward(Q, K, V, h, w, s, scale, bias_agg=B1, bias_bcast=B2, dwc_weight=W,
+                          dwc_bias=b)
+    A_ref = _torch_pool(Q, h, w, s)
+    VA = _sdpa_mask(A_ref, K, V, B1[None], scale)
+    ref = _sdpa_mask(Q, A_ref, VA, B2[None], scale) + _dwc_torch(V, h, w, W, b)
+    assert np.allclose(O, ref, rtol=0, atol=1e-12)
+
+
 ALL_PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_")]

@@ -44,32 +44,32 @@ def _pool_sum(Q, h, w, s):
     return A
 
 
-def _agg_no_scale(A, K, V, scale):
+def _agg_no_scale(A, K, V, scale, bias=None):
     return orc.softmax_last(A @ np.swapaxes(K, -1, -2)) @ V
 
 
-def _agg_wrong_axis(A, K, V, scale):
+def _agg_wrong_axis(A, K, V, scale, bias=None):
     S = scale * (A @ np.swapaxes(K, -1, -2))
     E = np.exp(S - S.max(axis=-2, keepdims=True))
     return (E / E.sum(axis=-2, keepdims=True)) @ V
 
 
-def _agg_scale_twice(A, K, V, scale):
+def _agg_scale_twice(A, K, V, scale, bias=None):
     return orc.softmax_last(scale * scale * (A @ np.swapaxes(K, -1, -2))) @ V
 
 
-def _bc_values_as_keys(Q, A, VA, scale):
+def _bc_values_as_keys(Q, A, VA, scale, bias=None):
     """the garbled broadcast of one blog post: keys V_A, no scale."""
     return orc.softmax_last(Q @ np.swapaxes(VA, -1, -2)) @ VA
 
 
-def _bc_wrong_axis(Q, A, VA, scale):
+def _bc_wrong_axis(Q, A, VA, scale, bias=None):
     S = scale * (Q @ np.swapaxes(A, -1, -2))
     E = np.exp(S - S.max(axis=-2, keepdims=True))
     return (E / E.sum(axis=-2, keepdims=True)) @ VA
 
 
-def _bc_no_scale(Q, A, VA, scale):
+def _bc_no_scale(Q, A, VA, scale, bias=None):
     return orc.softmax_last(Q @ np.swapaxes(A, -1, -2)) @ VA
 
 
@@ -87,28 +87,28 @@ def _softmax_no_norm(S):
     return np.exp(S - S.max(axis=-1, keepdims=True))
 
 
-def _forward_swap_kv(Q, K, V, h, w, s, scale, A=None):
+def _forward_swap_kv(Q, K, V, h, w, s, scale, A=None, **module_terms):
     Q, K, V = (np.asarray(x, float) for x in (Q, K, V))
     A = orc.pool_agents(Q, h, w, s) if A is None else np.asarray(A, float)
     VA = orc.aggregate(A, V, K, scale)
     return orc.broadcast(Q, A, VA, scale), A, VA
 
 
-def _forward_agents_as_values(Q, K, V, h, w, s, scale, A=None):
+def _forward_agents_as_values(Q, K, V, h, w, s, scale, A=None, **module_terms):
     Q, K, V = (np.asarray(x, float) for x in (Q, K, V))
     A = orc.pool_agents(Q, h, w, s) if A is None else np.asarray(A, float)
     VA = orc.aggregate(A, K, V, scale)
     return orc.broadcast(Q, A, A, scale), A, VA
 
 
-def _forward_pool_keys(Q, K, V, h, w, s, scale, A=None):
+def _forward_pool_keys(Q, K, V, h, w, s, scale, A=None, **module_terms):
     Q, K, V = (np.asarray(x, float) for x in (Q, K, V))
     A = orc.pool_agents(K, h, w, s) if A is None else np.asarray(A, float)
     VA = orc.aggregate(A, K, V, scale)
     return orc.broadcast(Q, A, VA, scale), A, VA
 
 
-def _forward_skip_aggregation(Q, K, V, h, w, s, scale, A=None):
+def _forward_skip_aggregation(Q, K, V, h, w, s, scale, A=None, **module_terms):
     """a dropped step: broadcast straight from pooled values."""
     Q, K, V = (np.asarray(x, float) for x in (Q, K, V))
     A = orc.pool_agents(Q, h, w, s) if A is None else np.asarray(A, float)
@@ -116,7 +116,91 @@ def _forward_skip_aggregation(Q, K, V, h, w, s, scale, A=None):
     return orc.broadcast(Q, A, VA, scale), A, VA
 
 
+def _agg_bias_scaled(A, K, V, scale, bias=None):
+    """bias inside the scaled product: scale * (A K^T + B1)."""
+    S = A @ np.swapaxes(K, -1, -2)
+    if bias is not None:
+        S = S + np.asarray(bias)[None]
+    return orc.softmax_last(scale * S) @ V
+
+
+def _agg_bias_dropped(A, K, V, scale, bias=None):
+    return orc.softmax_last(scale * (A @ np.swapaxes(K, -1, -2))) @ V
+
+
+def _bc_bias_dropped(Q, A, VA, scale, bias=None):
+    return orc.softmax_last(scale * (Q @ np.swapaxes(A, -1, -2))) @ VA
+
+
+def _bc_bias_negated(Q, A, VA, scale, bias=None):
+    S = scale * (Q @ np.swapaxes(A, -1, -2))
+    if bias is not None:
+        S = S - np.asarray(bias)[None]
+    return orc.softmax_last(S) @ VA
+
+
+def _dwc_flipped(V, h, w, weight, bias=None):
+    """convolution with the kernel flipped (true convolution, not the
+    cross-correlation deep-learning layers compute)."""
+    return _orig_dwc(V, h, w, np.asarray(weight)[:, ::-1, ::-1], bias)
+
+
+def _dwc_wraparound(V, h, w, weight, bias=None):
+    """circular instead of zero padding."""
+    V = np.asarray(V, float)
+    B, H, N, d = V.shape
+    W = np.asarray(weight, float).reshape(H, d, 3, 3)
+    grid = V.reshape(B, H, h, w, d)
+    out = np.zeros_like(grid)
+    if bias is not None:
+        out += np.asarray(bias, float).reshape(H, d)[None, :, None, None, :]
+    for dy in (-1, 0, 1):
+        for dx in (-1, 0, 1):
+            shifted = np.roll(np.roll(grid, -dy, axis=2), -dx, axis=3)
+            out += W[None, :, None, None, :, dy + 1, dx + 1] * shifted
+    return out.reshape(B, H, N, d)
+
+
+def _dwc_transposed_taps(V, h, w, weight, bias=None):
+    """dy and dx exchanged in the kernel index."""
+    return _orig_dwc(V, h, w, np.swapaxes(np.asarray(weight), 1, 2), bias)
+
+
+def _dwc_no_bias(V, h, w, weight, bias=None):
+    return _orig_dwc(V, h, w, weight, None)
+
+
+def _forward_dwc_of_queries(Q, K, V, h, w, s, scale, A=None, bias_agg=None, bias_bcast=None,
+                            dwc_weight=None, dwc_bias=None):
+    O, A_, VA = _orig_forward(Q, K, V, h, w, s, scale, A=A, bias_agg=bias_agg,
+                              bias_bcast=bias_bcast)
+    if dwc_weight is not None:
+        O = O + orc.dwc(Q, h, w, dwc_weight, dwc_bias)
+    return O, A_, VA
+
+
+def _forward_biases_swapped(Q, K, V, h, w, s, scale, A=None, bias_agg=None, bias_bcast=None,
+                            dwc_weight=None, dwc_bias=None):
+    """B1 and B2 used in the other attention (transposed to fit)."""
+    sw = lambda b: None if b is None else np.swapaxes(np.asarray(b), -1, -2)  # noqa: E731
+    return _orig_forward(Q, K, V, h, w, s, scale, A=A, bias_agg=sw(bias_bcast),
+                         bias_bcast=sw(bias_agg), dwc_weight=dwc_weight, dwc_bias=dwc_bias)
+
+
+_orig_dwc = orc.dwc
+_orig_forward = orc.forward
+
 MUTANTS = {
+    "aggregate_bias_inside_scale": ("aggregate", _agg_bias_scaled),
+    "aggregate_bias_dropped": ("aggregate", _agg_bias_dropped),
+    "broadcast_bias_dropped": ("broadcast", _bc_bias_dropped),
+    "broadcast_bias_negated": ("broadcast", _bc_bias_negated),
+    "dwc_kernel_flipped": ("dwc", _dwc_flipped),
+    "dwc_circular_padding": ("dwc", _dwc_wraparound),
+    "dwc_taps_transposed": ("dwc", _dwc_transposed_taps),
+    "dwc_bias_dropped": ("dwc", _dwc_no_bias),
+    "forward_dwc_of_queries": ("forward", _forward_dwc_of_queries),
+    "forward_biases_swapped": ("forward", _forward_biases_swapped),
     "pool_column_major": ("pool_agents", _pool_column_major),
     "window_floor_stop": ("window_bounds", _window_floor),
     "pool_sum_not_mean": ("pool_agents", _pool_sum),
