@@ -30,6 +30,8 @@ _SIGNATURES = {
                                                                   _vp]),
     "agent_attn_forward_strided": (_c_int, [_vp] * 5 + [_c_int] * 6 + [ctypes.c_longlong] * 3 +
                                    [_c_float, _c_int, _vp, _c_size, _vp]),
+    "agent_attn_forward_module": (_c_int, [_vp] * 9 + [_c_int] * 6 + [_c_float, _c_int, _vp,
+                                                                       _c_size, _vp]),
     "agent_attn_pool": (_c_int, [_vp, _vp] + [_c_int] * 7 + [_vp]),
     "agent_attn_aggregate_workspace_bytes": (_c_size, [_c_int] * 6),
     "agent_attn_aggregate": (_c_int, [_vp] * 4 + [_c_int] * 5 + [_c_float, _c_int, _vp, _c_size,
@@ -205,6 +207,63 @@ def agent_attn_forward(q, k, v, grid_hw, s, scale=None, agents=None, out=None, w
             rc = L.agent_attn_forward_strided(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(agents),
                                               B, H, h, w, d, int(s), sb, sh, sn, float(scale),
                                               code, ws_ptr, ws_size, _stream(q.device))
+    _check(rc)
+    return out
+
+
+def agent_attn_forward_module(q, k, v, grid_hw, s, scale=None, agents=None, bias_agg=None,
+                              bias_bcast=None, dwc_weight=None, dwc_bias=None, out=None,
+                              workspace=None):
+    """The full module's forward: softmax(scale Q A^T + B2) softmax(scale A
+    K^T + B1) V + DWC(V) ("Agent Attention: On the Integration of Softmax
+    and Linear Attention", §4 Module Enhancements).
+
+    q, k, v: dense [B, H, h*w, d] GPU tensors (float32, bfloat16 or float16).
+    bias_agg B1 [H, s*s, N], bias_bcast B2 [H, N, s*s], dwc_weight
+    [H*d, 3, 3] and dwc_bias [H*d]: float32 GPU tensors or None.
+    Runs on torch's current stream; returns `out`.
+    """
+    L = lib()
+    _dev_tensor(q, "q")
+    B, H, N, d = q.shape
+    h, w = (int(x) for x in grid_hw)
+    if h * w != N:
+        raise ValueError(f"grid {h}x{w} does not match N={N}")
+    k_ag = int(s) * int(s)
+    for name, t in (("k", k), ("v", v)):
+        _dev_tensor(t, name)
+        _same(q, t, name, q.shape, q.dtype)
+    if agents is not None:
+        _dev_tensor(agents, "agents")
+        _same(q, agents, "agents", (B, H, k_ag, d), q.dtype)
+    shapes = {"bias_agg": (H, k_ag, N), "bias_bcast": (H, N, k_ag),
+              "dwc_weight": (H * d, 3, 3), "dwc_bias": (H * d,)}
+    params = {"bias_agg": bias_agg, "bias_bcast": bias_bcast, "dwc_weight": dwc_weight,
+              "dwc_bias": dwc_bias}
+    for name, t in params.items():
+        if t is None:
+            continue
+        _dev_tensor(t, name, ndim=len(shapes[name]))
+        _same(q, t, name, shapes[name], torch.float32)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _dev_tensor(out, "out")
+        _same(q, out, "out", q.shape, q.dtype)
+    code = _dtype_code(q)
+    with torch.cuda.device(q.device):
+        need = L.agent_attn_workspace_bytes(B, H, h, w, d, int(s), code)
+        ws_ptr, ws_size = None, 0
+        if need > 0:
+            if workspace is None:
+                workspace = cached_workspace(q.device, need)
+            ws_ptr, ws_size = _ptr(workspace), workspace.numel() * workspace.element_size()
+        rc = L.agent_attn_forward_module(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(agents),
+                                         _ptr(bias_agg), _ptr(bias_bcast), _ptr(dwc_weight),
+                                         _ptr(dwc_bias), B, H, h, w, d, int(s), float(scale),
+                                         code, ws_ptr, ws_size, _stream(q.device))
     _check(rc)
     return out
 

@@ -397,16 +397,17 @@ int launch_widen(const Dims& D, const void* src, float* dst, hipStream_t st) {
 
 template <typename T>
 int launch_aggregate(const Dims& D, const float* A, const void* k, const void* v, float* VA,
-                     float* part, int chunk, int nchunks, float sl2, hipStream_t st) {
+                     float* part, int chunk, int nchunks, float sl2, hipStream_t st,
+                     const float* bias1 = nullptr) {
   const long blocks = D.BH * nchunks;
   if (D.d <= 64)
     hipLaunchKernelGGL((aa::aggregate_partial_scalar<T, 64>), dim3((unsigned)blocks), dim3(256), 0,
                        st, A, (const T*)k, (const T*)v, part, (int)D.N, D.d, D.nag, sl2, chunk,
-                       nchunks, D.strides());
+                       nchunks, D.strides(), bias1);
   else
     hipLaunchKernelGGL((aa::aggregate_partial_scalar<T, 128>), dim3((unsigned)blocks), dim3(256),
                        0, st, A, (const T*)k, (const T*)v, part, (int)D.N, D.d, D.nag, sl2, chunk,
-                       nchunks, D.strides());
+                       nchunks, D.strides(), bias1);
   AA_LAUNCH_CHECK("agent_aggregate launch");
   hipLaunchKernelGGL(aa::merge_partials_kernel, dim3((unsigned)(D.BH * D.nag)), dim3(128), 0, st,
                      part, VA, D.d, D.nag, nchunks);
@@ -416,15 +417,17 @@ int launch_aggregate(const Dims& D, const float* A, const void* k, const void* v
 
 template <typename T>
 int launch_broadcast(const Dims& D, const void* q, const float* A, const float* VA, void* out,
-                     float sl2, hipStream_t st) {
+                     float sl2, hipStream_t st, aa::ScalarMod md = aa::ScalarMod{}) {
   const int nqblk = (int)((D.N + 255) / 256);
   const long blocks = D.BH * nqblk;
   if (D.d <= 64)
     hipLaunchKernelGGL((aa::broadcast_scalar<T, 64>), dim3((unsigned)blocks), dim3(256), 0, st,
-                       (const T*)q, A, VA, (T*)out, (int)D.N, D.d, D.nag, sl2, nqblk, D.strides());
+                       (const T*)q, A, VA, (T*)out, (int)D.N, D.d, D.nag, sl2, nqblk, D.strides(),
+                       md);
   else
     hipLaunchKernelGGL((aa::broadcast_scalar<T, 128>), dim3((unsigned)blocks), dim3(256), 0, st,
-                       (const T*)q, A, VA, (T*)out, (int)D.N, D.d, D.nag, sl2, nqblk, D.strides());
+                       (const T*)q, A, VA, (T*)out, (int)D.N, D.d, D.nag, sl2, nqblk, D.strides(),
+                       md);
   AA_LAUNCH_CHECK("agent_broadcast launch");
   return AGENT_ATTN_OK;
 }
@@ -437,22 +440,25 @@ std::atomic<long> g_spin_limit{aa::kSpinLimit};   // polls before a group wait g
 
 int launch_mfma(int DC, bool f16, const aa::MfmaParams& mp, long grid, int nag,
                 hipStream_t st) {
-  // the dense [B, H, N, d] layout has its own kernel instance
+  // the dense [B, H, N, d] layout has its own kernel instance, and so has
+  // the dense layout with the module terms
   const bool strided = !(mp.sn == mp.d && mp.sh == (long)mp.N * mp.d &&
                          mp.sb == (long)mp.H * mp.N * mp.d);
+  const bool module = mp.bias_agg || mp.bias_bcast || mp.dwc_w;
+  const int variant = module ? aa::kModule : (strided ? aa::kStrided : aa::kDense);
   const int ktc = mfma_ktc(nag);
   int e;
   if (f16) {
     switch (DC) {
-      case 1: e = aa::launch_mfma_dc<1, aa::ElemF16>(mp, ktc, strided, grid, st); break;
-      case 2: e = aa::launch_mfma_dc<2, aa::ElemF16>(mp, ktc, strided, grid, st); break;
-      default: e = aa::launch_mfma_dc<4, aa::ElemF16>(mp, ktc, strided, grid, st); break;
+      case 1: e = aa::launch_mfma_dc<1, aa::ElemF16>(mp, ktc, variant, grid, st); break;
+      case 2: e = aa::launch_mfma_dc<2, aa::ElemF16>(mp, ktc, variant, grid, st); break;
+      default: e = aa::launch_mfma_dc<4, aa::ElemF16>(mp, ktc, variant, grid, st); break;
     }
   } else {
     switch (DC) {
-      case 1: e = aa::launch_mfma_dc<1, aa::ElemBF16>(mp, ktc, strided, grid, st); break;
-      case 2: e = aa::launch_mfma_dc<2, aa::ElemBF16>(mp, ktc, strided, grid, st); break;
-      default: e = aa::launch_mfma_dc<4, aa::ElemBF16>(mp, ktc, strided, grid, st); break;
+      case 1: e = aa::launch_mfma_dc<1, aa::ElemBF16>(mp, ktc, variant, grid, st); break;
+      case 2: e = aa::launch_mfma_dc<2, aa::ElemBF16>(mp, ktc, variant, grid, st); break;
+      default: e = aa::launch_mfma_dc<4, aa::ElemBF16>(mp, ktc, variant, grid, st); break;
     }
   }
   if (e != hipSuccess) return hip_fail((hipError_t)e, "agent attention matrix-core kernel launch");
@@ -486,7 +492,8 @@ aa::MfmaParams mfma_params(const Dims& D, int P, int T, float scale) {
 // Runs `phases` either in one fused launch or as one launch per phase.
 int run_mfma_phases(const Dims& D, aa::MfmaParams mp, int DC, int phases, bool fused,
                     hipStream_t st) {
-  const int lds = mfma_lds_bytes(DC, D.nag);
+  const bool module = mp.bias_agg || mp.bias_bcast || mp.dwc_w;
+  const int lds = mfma_lds_bytes(DC, D.nag) + (module ? 10 * 32 * DC * 4 : 0);
   if (lds > 160 * 1024 - 64)
     return fail(AGENT_ATTN_ERR_UNSUPPORTED, "d=%d with %d agents needs %d bytes of LDS", D.d,
                 D.nag, lds);
@@ -511,9 +518,24 @@ int run_mfma_phases(const Dims& D, aa::MfmaParams mp, int DC, int phases, bool f
   return AGENT_ATTN_OK;
 }
 
+// Module terms of a forward (agent biases, depth-wise convolution); all
+// null for the plain operator.
+struct ModTerms {
+  const float* bias_agg = nullptr;     // B1 [H, k, N]
+  const float* bias_bcast = nullptr;   // B2 [H, N, k]
+  const float* dwc_w = nullptr;        // [H*d, 3, 3]
+  const float* dwc_b = nullptr;        // [H*d]
+};
+
 int run_forward_mfma(const Dims& D, const Plan& P, const void* q, const void* k, const void* v,
-                     void* out, const void* agents, float scale, char* ws, hipStream_t st) {
+                     void* out, const void* agents, float scale, char* ws, hipStream_t st,
+                     const ModTerms& mt) {
   aa::MfmaParams mp = mfma_params(D, P.P, P.T, scale);
+  mp.bias_agg = mt.bias_agg;
+  mp.bias_bcast = mt.bias_bcast;
+  mp.dwc_w = mt.dwc_w;
+  mp.dwc_b = mt.dwc_w ? mt.dwc_b : nullptr;
+  mp.inv_scale = 1.0f / scale;
   mp.q = (const aa::bf16_t*)q;
   mp.k = (const aa::bf16_t*)k;
   mp.v = (const aa::bf16_t*)v;
@@ -536,16 +558,23 @@ int run_forward_mfma(const Dims& D, const Plan& P, const void* q, const void* k,
 
 template <typename T>
 int run_forward(const Dims& D, const Plan& P, const void* q, const void* k, const void* v,
-                void* out, const void* agents, float scale, char* ws, hipStream_t st) {
+                void* out, const void* agents, float scale, char* ws, hipStream_t st,
+                const ModTerms& mt) {
   float* A = (float*)(ws + P.off_A);
   float* VA = (float*)(ws + P.off_VA);
   float* part = (float*)(ws + P.off_part);
   const float sl2 = scale * aa::kLog2e;
   int rc = agents ? launch_widen<T>(D, agents, A, st) : launch_pool<T>(D, q, A, st);
   if (rc) return rc;
-  rc = launch_aggregate<T>(D, A, k, v, VA, part, P.chunk, P.nchunks, sl2, st);
+  rc = launch_aggregate<T>(D, A, k, v, VA, part, P.chunk, P.nchunks, sl2, st, mt.bias_agg);
   if (rc) return rc;
-  return launch_broadcast<T>(D, q, A, VA, out, sl2, st);
+  aa::ScalarMod md{};
+  md.bias2 = mt.bias_bcast;
+  md.v = v;
+  md.dwc_w = mt.dwc_w;
+  md.dwc_b = mt.dwc_w ? mt.dwc_b : nullptr;
+  md.w = D.w;
+  return launch_broadcast<T>(D, q, A, VA, out, sl2, st, md);
 }
 
 // Element strides (batch, head, token) of q/k/v/out: positive multiples of
@@ -610,10 +639,11 @@ int validate_forward(Dims& D, const void* q, const void* k, const void* v, void*
 }
 
 int dispatch_forward(const Dims& D, const Plan& P, const void* q, const void* k, const void* v,
-                     void* out, const void* agents, float scale, void* ws, hipStream_t st) {
+                     void* out, const void* agents, float scale, void* ws, hipStream_t st,
+                     const ModTerms& mt = ModTerms{}) {
   if (D.dtype == AGENT_ATTN_F32)
-    return run_forward<float>(D, P, q, k, v, out, agents, scale, (char*)ws, st);
-  return run_forward_mfma(D, P, q, k, v, out, agents, scale, (char*)ws, st);
+    return run_forward<float>(D, P, q, k, v, out, agents, scale, (char*)ws, st, mt);
+  return run_forward_mfma(D, P, q, k, v, out, agents, scale, (char*)ws, st, mt);
 }
 
 // Per-device grow-only scratch for agent_attn_forward.
@@ -661,13 +691,42 @@ size_t aggregate_ws_bytes(const Dims& D) {
   return align_up(mfma_ml_bytes(D, P, DC), 256) + align_up(mfma_acc_bytes(D, P, DC), 256);
 }
 
+// Checks the module-term buffers of a forward: 4-byte aligned, within the
+// kernels' 32-bit offsets, and disjoint from out and the workspace.
+int check_module(const Dims& D, const ModTerms& mt, const void* out, const void* ws,
+                 size_t ws_bytes) {
+  const size_t bias_bytes = (size_t)D.H * D.nag * D.N * 4;
+  const size_t w_bytes = (size_t)D.H * D.d * 9 * 4, b_bytes = (size_t)D.H * D.d * 4;
+  const void* ptrs[4] = {mt.bias_agg, mt.bias_bcast, mt.dwc_w, mt.dwc_w ? mt.dwc_b : nullptr};
+  const size_t sizes[4] = {bias_bytes, bias_bytes, w_bytes, b_bytes};
+  for (int i = 0; i < 4; ++i)
+    if (ptrs[i] && ((uintptr_t)ptrs[i] & 3u))
+      return fail(AGENT_ATTN_ERR_ALIGN, "bias and convolution parameters must be 4-byte aligned");
+  if ((mt.bias_agg || mt.bias_bcast) && (size_t)D.nag * D.N * 4 >= (size_t)aa::kOOB)
+    return fail(AGENT_ATTN_ERR_SHAPE, "an agent bias of one head spans more than 2^31 bytes");
+  if (mt.dwc_w && D.N >= (1L << 22))   // grid positions come from a float-reciprocal division
+    return fail(AGENT_ATTN_ERR_SHAPE, "the convolution term supports up to 2^22 tokens");
+  const size_t tb = (size_t)D.span() * elem_size(D.dtype);
+  for (int i = 0; i < 4; ++i) {
+    if (!ptrs[i]) continue;
+    if (ranges_overlap(out, tb, ptrs[i], sizes[i]))
+      return fail(AGENT_ATTN_ERR_ALIAS, "out overlaps a bias or convolution parameter");
+    if (ws && ranges_overlap(ws, ws_bytes, ptrs[i], sizes[i]))
+      return fail(AGENT_ATTN_ERR_ALIAS, "the workspace overlaps a bias or convolution parameter");
+  }
+  return AGENT_ATTN_OK;
+}
+
 int forward_ws(const void* q, const void* k, const void* v, void* out, const void* agents, int B,
                int H, int h, int w, int d, int s, float scale, int dtype, void* workspace,
-               size_t workspace_bytes, void* stream, const long long* strides) {
+               size_t workspace_bytes, void* stream, const long long* strides,
+               const ModTerms& mt = ModTerms{}) {
   Dims D;
   int rc = validate_forward(D, q, k, v, out, agents, B, H, h, w, d, s, scale, dtype, strides);
   if (rc) return rc;
   if (D.BH == 0) return AGENT_ATTN_OK;
+  rc = check_module(D, mt, out, workspace, workspace_bytes);
+  if (rc) return rc;
   const Plan P = make_plan(D, device_cus());
   if (!workspace || workspace_bytes < P.bytes)
     return fail(AGENT_ATTN_ERR_WORKSPACE, "workspace of %zu bytes at %p; %zu bytes needed",
@@ -680,7 +739,7 @@ int forward_ws(const void* q, const void* k, const void* v, void* out, const voi
       ranges_overlap(workspace, P.bytes, v, tb) || ranges_overlap(workspace, P.bytes, out, tb) ||
       ranges_overlap(workspace, P.bytes, agents, ab))
     return fail(AGENT_ATTN_ERR_ALIAS, "workspace overlaps a tensor argument");
-  return dispatch_forward(D, P, q, k, v, out, agents, scale, workspace, (hipStream_t)stream);
+  return dispatch_forward(D, P, q, k, v, out, agents, scale, workspace, (hipStream_t)stream, mt);
 }
 
 }  // namespace
@@ -711,6 +770,20 @@ int agent_attn_forward_strided(const void* q, const void* k, const void* v, void
   const long long st[3] = {stride_b, stride_h, stride_n};
   return forward_ws(q, k, v, out, agents, B, H, h, w, d, s, scale, dtype, workspace,
                     workspace_bytes, stream, st);
+}
+
+int agent_attn_forward_module(const void* q, const void* k, const void* v, void* out,
+                              const void* agents, const float* bias_agg, const float* bias_bcast,
+                              const float* dwc_weight, const float* dwc_bias, int B, int H, int h,
+                              int w, int d, int s, float scale, int dtype, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  ModTerms mt;
+  mt.bias_agg = bias_agg;
+  mt.bias_bcast = bias_bcast;
+  mt.dwc_w = dwc_weight;
+  mt.dwc_b = dwc_bias;
+  return forward_ws(q, k, v, out, agents, B, H, h, w, d, s, scale, dtype, workspace,
+                    workspace_bytes, stream, nullptr, mt);
 }
 
 int agent_attn_forward(const void* q, const void* k, const void* v, void* out,

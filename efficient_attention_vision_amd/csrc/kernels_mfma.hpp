@@ -94,6 +94,21 @@ struct MfmaParams {
   long sb, sh;                  // q/k/v/out element strides of batch and head
   int H;                        // heads per batch entry (head index = b*H + h)
   int sn;                       // element stride between tokens (channels contiguous)
+  // module terms (instances with MOD only; each pointer may be null)
+  const float* bias_agg;        // B1 [H, nag, N], added to the scaled aggregation logits
+  const float* bias_bcast;      // B2 [H, N, nag], added to the scaled broadcast logits
+  const float* dwc_w;           // depth-wise 3x3 weights [H*d, 3, 3]
+  const float* dwc_b;           // their bias [H*d] (null: zero)
+  float inv_scale;              // 1 / scale: biases in units of the unscaled scores
+};
+
+// Module terms as a kernel sees them for its head (see MfmaParams).
+struct ModCtx {
+  rsrc_t b1, b2, rv;            // B1 and B2 of the head's parameters; V of the head
+  const float* wl;              // DWC weights in LDS: [9][DPAD] taps, then [DPAD] bias
+  bool has_b1, has_b2, has_dwc;
+  float inv_scale;
+  int N, nag, w;
 };
 
 // Phase timestamps for profiling builds (-DAGENT_ATTN_PHASE_TRACE): 32
@@ -545,10 +560,10 @@ struct AggState {
   f32x4 lacc[ATW];   // row sums of the probabilities, on the matrix cores
 };
 
-template <class E, class C, int DC, int ATW>
+template <class E, class C, int DC, int ATW, bool MOD>
 __device__ __forceinline__ void agg_block(AggState<DC, ATW>& st, const bf16_t* Ks,
                                           const bf16x8* Af, const bf16_t* Vt, int blk_col, int ag,
-                                          int valid, float sl2) {
+                                          int valid, float sl2, const ModCtx& mc, int tok0) {
   constexpr int DT = 2 * DC;
   const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
   // K fragments: token row blk_col + 16tt + r, channel chunk DC*g + c
@@ -578,6 +593,19 @@ __device__ __forceinline__ void agg_block(AggState<DC, ATW>& st, const bf16_t* K
       const bf16x8 af = Af[(t * DC + c) * 64 + lane];
       S0 = E::mma(kf[0][c], af, S0);
       S1 = E::mma(kf[1][c], af, S1);
+    }
+    if constexpr (MOD) {
+      if (mc.has_b1) {   // B1[agent 16t + r][tokens tok0 + 16tt + 4g + i], in score units
+        const int a = 16 * t + r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int n0i = tok0 + 4 * g + i, n1i = n0i + 16;
+          const unsigned o0 = (a < mc.nag && n0i < mc.N) ? (unsigned)((a * mc.N + n0i) * 4) : kOOB;
+          const unsigned o1 = (a < mc.nag && n1i < mc.N) ? (unsigned)((a * mc.N + n1i) * 4) : kOOB;
+          S0[i] = fmaf(bld4<kPlain>(mc.b1, o0), mc.inv_scale, S0[i]);
+          S1[i] = fmaf(bld4<kPlain>(mc.b1, o1), mc.inv_scale, S1[i]);
+        }
+      }
     }
     if (valid < 32) {   // rows 16tt + 4g + i past the slice end
 #pragma unroll
@@ -648,9 +676,10 @@ __device__ __forceinline__ void load_q_tile(bf16x8 (&qf)[DC], rsrc_t rq, int tok
 // Broadcast logits and softmax of one 16-token query tile: P2 = softmax over
 // the agents of scale * Q A^T, as bf16 B-operand fragments pf[j] (agent pairs
 // of chunk j, see pair_index) and the reciprocal of the row sum.
-template <class E, class C, int DC, int KTC>
+template <class E, class C, int DC, int KTC, bool MOD>
 __device__ __forceinline__ void bcast_probs(const bf16x8 (&qf)[DC], const bf16x8* Af, int nag,
-                                            float sl2, bf16x8 (&pf)[C::KC], float& inv) {
+                                            float sl2, bf16x8 (&pf)[C::KC], float& inv,
+                                            const ModCtx& mc, int tok0) {
   const int lane = threadIdx.x & 63, g = lane >> 4;
   // When the agent and V_A fragments need more than 128 registers they
   // cannot all stay in registers across the caller's tile loop: the LDS
@@ -670,6 +699,21 @@ __device__ __forceinline__ void bcast_probs(const bf16x8 (&qf)[DC], const bf16x8
 #pragma unroll
     for (int c = 0; c < DC; ++c)
       S[t] = E::mma(Af[(t * DC + c) * 64 + fl], qf[c], S[t]);
+  }
+  if constexpr (MOD) {
+    if (mc.has_b2) {   // B2[token tok0 + r][agents 16t + 4g + i], in score units
+      const int tok = tok0 + (lane & 15);
+#pragma unroll
+      for (int t = 0; t < KTC; ++t) {
+        if (t % 4 == 0) asm volatile("" ::: "memory");   // 16 loads in flight at most
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int a = 16 * t + 4 * g + i;
+          const unsigned o = (tok < mc.N && a < nag_t) ? (unsigned)((tok * mc.nag + a) * 4) : kOOB;
+          S[t][i] = fmaf(bld4<kPlain>(mc.b2, o), mc.inv_scale, S[t][i]);
+        }
+      }
+    }
   }
 #pragma unroll
   for (int t = 0; t < KTC; ++t)
@@ -702,30 +746,66 @@ __device__ __forceinline__ void bcast_probs(const bf16x8 (&qf)[DC], const bf16x8
   inv = 1.0f / Lacc[0];
 }
 
-// Broadcast output of one query tile: O = P2 V_A (V_A as bf16 hi + lo when
-// VSPLIT = 2), normalised, rounded to bf16 and stored.
-template <class E, class C, int DC, int KTC>
-__device__ __forceinline__ void bcast_out(const bf16x8 (&pf)[C::KC], float inv, const bf16x8* VAf,
-                                          rsrc_t ro, int tok0, int tok_end, int d, int sn) {
+// Depth-wise 3 x 3 convolution of V at grid position (row, col) for
+// channels ch .. ch+3: bias + sum over the taps inside the grid of weight *
+// V (weights and bias from LDS, [9][32 DC] then [32 DC]).  Not inlined, so
+// that its loads stay within one call instead of being hoisted across the
+// caller's tiles.
+template <class E, int DC>
+__device__ __attribute__((noinline)) float4 dwc4(rsrc_t rv, const float* wl, int rows, int w,
+                                                 int row, int col, int ch, int d, int sn) {
+  const float4 b = *reinterpret_cast<const float4*>(wl + 9 * 32 * DC + ch);
+  float acc[4] = {b.x, b.y, b.z, b.w};
+  u32x2 v[9];
+#pragma unroll
+  for (int tap = 0; tap < 9; ++tap) {
+    const int rr = row + tap / 3 - 1, cc = col + tap % 3 - 1;
+    const bool in = rr >= 0 && rr < rows && cc >= 0 && cc < w && ch < d;
+    v[tap] = __builtin_amdgcn_raw_buffer_load_b64(
+        rv, in ? (int)(((rr * w + cc) * sn + ch) * 2) : (int)kOOB, 0, kPlain);
+  }
+#pragma unroll
+  for (int tap = 0; tap < 9; ++tap) {
+    const float4 wt = *reinterpret_cast<const float4*>(wl + tap * 32 * DC + ch);
+    acc[0] = fmaf(wt.x, E::value((uint16_t)(v[tap][0] & 0xffffu)), acc[0]);
+    acc[1] = fmaf(wt.y, E::value((uint16_t)(v[tap][0] >> 16)), acc[1]);
+    acc[2] = fmaf(wt.z, E::value((uint16_t)(v[tap][1] & 0xffffu)), acc[2]);
+    acc[3] = fmaf(wt.w, E::value((uint16_t)(v[tap][1] >> 16)), acc[3]);
+  }
+  return float4{acc[0], acc[1], acc[2], acc[3]};
+}
+
+// Stores one normalised 16-token output tile held in the matrix-core result
+// layout (O[dt]: channels 16 dt + 4 g .. +3 of token tok0 + r in lane (r, g)),
+// with the depth-wise convolution term added in the MOD instances.
+template <class E, int DC, bool MOD>
+__device__ __forceinline__ void store_o_tile(const f32x4 (&O)[2 * DC], float inv, rsrc_t ro,
+                                             int tok0, int tok_end, int d, int sn,
+                                             const ModCtx& mc) {
   constexpr int DT = 2 * DC;
-  constexpr int VA_PART = C::KC * DT * 64;
   const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
-  constexpr int kFragRegs = 4 * (KTC * DC + C::KC * DT * C::VSPLIT);
-  int fl = lane;
-  if (kFragRegs > 128 || KTC >= 16) asm volatile("" : "+v"(fl));
-  f32x4 O[DT];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) O[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int j = 0; j < C::KC; ++j)
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const int f = (j * DT + dt) * 64 + fl;
-      O[dt] = E::mma(VAf[f], pf[j], O[dt]);
-      if (C::VSPLIT > 1)
-        O[dt] = E::mma(VAf[VA_PART + f], pf[j], O[dt]);
-    }
   const int tok = tok0 + r;
+  float val[DT][4];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) val[dt][i] = O[dt][i] * inv;
+  if constexpr (MOD) {
+    if (mc.has_dwc) {
+      // + DWC(V) for token tok = row * w + col (see dwc4)
+      const int row = tok < tok_end ? idiv(tok, mc.w, rcp_approx(mc.w)) : -4;
+      const int col = tok - row * mc.w;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const float4 x =
+            dwc4<E, DC>(mc.rv, mc.wl, mc.N / mc.w, mc.w, row, col, 16 * dt + 4 * g, d, sn);
+        val[dt][0] += x.x;
+        val[dt][1] += x.y;
+        val[dt][2] += x.z;
+        val[dt][3] += x.w;
+      }
+    }
+  }
   // Lane (r, g) holds channels 16 dt + 4 g .. +3 of token r for every dt.
   // Two 2 x 2 transposes between lane groups (permlane32_swap exchanges
   // lane-group bit 1 with the dt bit 0, permlane16_swap then exchanges
@@ -735,8 +815,8 @@ __device__ __forceinline__ void bcast_out(const bf16x8 (&pf)[C::KC], float inv, 
   unsigned pk[DT][2];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
-    pk[dt][0] = pack2<E>(O[dt][0] * inv, O[dt][1] * inv);
-    pk[dt][1] = pack2<E>(O[dt][2] * inv, O[dt][3] * inv);
+    pk[dt][0] = pack2<E>(val[dt][0], val[dt][1]);
+    pk[dt][1] = pack2<E>(val[dt][2], val[dt][3]);
   }
   constexpr int NS = DT >= 4 ? 2 : 1;
 #pragma unroll
@@ -757,18 +837,45 @@ __device__ __forceinline__ void bcast_out(const bf16x8 (&pf)[C::KC], float inv, 
     }
 }
 
-template <class E, class C, int DC, int KTC>
+// Broadcast output of one query tile: O = P2 V_A (V_A as bf16 hi + lo when
+// VSPLIT = 2), normalised, rounded to bf16 and stored.
+template <class E, class C, int DC, int KTC, bool MOD>
+__device__ __forceinline__ void bcast_out(const bf16x8 (&pf)[C::KC], float inv, const bf16x8* VAf,
+                                          rsrc_t ro, int tok0, int tok_end, int d, int sn,
+                                          const ModCtx& mc) {
+  constexpr int DT = 2 * DC;
+  constexpr int VA_PART = C::KC * DT * 64;
+  const int lane = threadIdx.x & 63;
+  constexpr int kFragRegs = 4 * (KTC * DC + C::KC * DT * C::VSPLIT);
+  int fl = lane;
+  if (kFragRegs > 128 || KTC >= 16) asm volatile("" : "+v"(fl));
+  f32x4 O[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) O[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < C::KC; ++j)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int f = (j * DT + dt) * 64 + fl;
+      O[dt] = E::mma(VAf[f], pf[j], O[dt]);
+      if (C::VSPLIT > 1)
+        O[dt] = E::mma(VAf[VA_PART + f], pf[j], O[dt]);
+    }
+  store_o_tile<E, DC, MOD>(O, inv, ro, tok0, tok_end, d, sn, mc);
+}
+
+template <class E, class C, int DC, int KTC, bool MOD>
 __device__ __forceinline__ void bcast_tile(const bf16x8 (&qf)[DC], const bf16x8* Af,
                                            const bf16x8* VAf, rsrc_t ro, int tok0, int tok_end,
-                                           int d, int sn, int nag, float sl2) {
+                                           int d, int sn, int nag, float sl2, const ModCtx& mc) {
   bf16x8 pf[C::KC];
   float inv;
-  bcast_probs<E, C, DC, KTC>(qf, Af, nag, sl2, pf, inv);
-  bcast_out<E, C, DC, KTC>(pf, inv, VAf, ro, tok0, tok_end, d, sn);
+  bcast_probs<E, C, DC, KTC, MOD>(qf, Af, nag, sl2, pf, inv, mc, tok0);
+  bcast_out<E, C, DC, KTC, MOD>(pf, inv, VAf, ro, tok0, tok_end, d, sn, mc);
 }
 
 // ------------------------------------------------------------- the kernel
-template <int DC, int KTC, bool STRIDED, class E>
+template <int DC, int KTC, bool STRIDED, class E, bool MOD>
 __global__ void __launch_bounds__(kThreads)
 agent_mfma_kernel(MfmaParams p) {
   using C = Cfg<DC, KTC>;
@@ -843,6 +950,25 @@ agent_mfma_kernel(MfmaParams p) {
   const rsrc_t rq = rsrc_of(p.q + hoff, head_bytes);
   const rsrc_t rk = rsrc_of(p.k + hoff, head_bytes);
   const rsrc_t rv = rsrc_of(p.v + hoff, head_bytes);
+  // module terms: the parameters of head hh of the batch entry
+  ModCtx mc{};
+  int hh = 0;
+  if constexpr (MOD) {
+    static_assert(C::TOTAL % 16 == 0, "DWC weights follow the LDS plan, 16-byte aligned");
+    hh = head - idiv(head, p.H, rcp_approx(p.H)) * p.H;
+    mc.has_b1 = p.bias_agg != nullptr;
+    mc.has_b2 = p.bias_bcast != nullptr;
+    mc.has_dwc = p.dwc_w != nullptr;
+    const unsigned pb = (unsigned)(p.nag * p.N * 4);
+    mc.b1 = rsrc_of(p.bias_agg + (mc.has_b1 ? (long)hh * p.nag * p.N : 0), mc.has_b1 ? pb : 0u);
+    mc.b2 = rsrc_of(p.bias_bcast + (mc.has_b2 ? (long)hh * p.nag * p.N : 0), mc.has_b2 ? pb : 0u);
+    mc.rv = rv;
+    mc.wl = reinterpret_cast<const float*>(smem + C::TOTAL);
+    mc.inv_scale = p.inv_scale;
+    mc.N = p.N;
+    mc.nag = p.nag;
+    mc.w = p.w;
+  }
   const long ahb = (long)head * p.nag * d;    // offset of this head's agent rows
   const unsigned arow_bytes = (unsigned)(p.nag * d * 4);
 
@@ -1072,7 +1198,8 @@ agent_mfma_kernel(MfmaParams p) {
       __syncthreads();
       AA_STAMP(12);
       for (int b = tg; b < rblk; b += C::TG) {
-        agg_block<E, C, DC, ATW>(st, Ks, Af, Vt, 32 * b, ag, min(32, n1 - (rt0 + 32 * b)), p.sl2);
+        agg_block<E, C, DC, ATW, MOD>(st, Ks, Af, Vt, 32 * b, ag, min(32, n1 - (rt0 + 32 * b)),
+                                      p.sl2, mc, rt0 + 32 * b);
 #ifdef AGENT_ATTN_PHASE_TRACE
         if (b / C::TG < 4) {
           __builtin_amdgcn_s_waitcnt(0);
@@ -1241,7 +1368,8 @@ agent_mfma_kernel(MfmaParams p) {
 #pragma unroll
       for (int i = 0; i < kEarly; ++i)
         if (wave + kWaves * i < nqt)
-          bcast_probs<E, C, DC, KTC>(qe[i], Af, p.nag, p.sl2, epf[i], einv[i]);
+          bcast_probs<E, C, DC, KTC, MOD>(qe[i], Af, p.nag, p.sl2, epf[i], einv[i], mc,
+                                          n0 + 16 * (wave + kWaves * i));
     };
     if (early && !merge_wave) early_probs();
     AA_STAMP_BY(15, 0);
@@ -1426,6 +1554,20 @@ agent_mfma_kernel(MfmaParams p) {
     }
     });
     }
+    if constexpr (MOD) {
+      if (mc.has_dwc) {
+        // DWC weights of the head's channels as [9 taps][DPAD], then the
+        // bias [DPAD]; channels at or past d hold zeros
+        float* wl = reinterpret_cast<float*>(smem + C::TOTAL);
+        for (int i = tid; i < 10 * DPAD; i += kThreads) {
+          const int tap = i / DPAD, c = i - tap * DPAD;
+          const long ch = (long)hh * d + c;
+          float x = 0.f;
+          if (c < d) x = tap < 9 ? p.dwc_w[ch * 9 + tap] : (p.dwc_b ? p.dwc_b[ch] : 0.f);
+          wl[i] = x;
+        }
+      }
+    }
     __syncthreads();
     AA_STAMP(10);
     const rsrc_t ro = rsrc_of(p.out + hoff, head_bytes);
@@ -1433,13 +1575,14 @@ agent_mfma_kernel(MfmaParams p) {
 #pragma unroll
       for (int i = 0; i < kEarly; ++i) {
         const int qt = wave + kWaves * i;
-        if (qt < nqt) bcast_out<E, C, DC, KTC>(epf[i], einv[i], VAf, ro, n0 + 16 * qt, n1, d, sn);
+        if (qt < nqt)
+          bcast_out<E, C, DC, KTC, MOD>(epf[i], einv[i], VAf, ro, n0 + 16 * qt, n1, d, sn, mc);
       }
     } else
     for (int qt = wave; qt < nqt; qt += kWaves) {
       bf16x8 qnext[DC];
       load_q_tile<DC>(qnext, rq, n0 + 16 * (qt + kWaves), n1, d, sn);   // zeros past the end
-      bcast_tile<E, C, DC, KTC>(qcur, Af, VAf, ro, n0 + 16 * qt, n1, d, sn, p.nag, p.sl2);
+      bcast_tile<E, C, DC, KTC, MOD>(qcur, Af, VAf, ro, n0 + 16 * qt, n1, d, sn, p.nag, p.sl2, mc);
 #pragma unroll
       for (int c = 0; c < DC; ++c) qcur[c] = qnext[c];
     }
@@ -1457,28 +1600,39 @@ agent_mfma_kernel(MfmaParams p) {
 // Launch helper, instantiated per (DC, element type) in its own translation
 // unit (mfma_dc<DC>_<type>.hip) so that the instances compile in parallel.
 template <int DC, class E>
-int launch_mfma_dc(const MfmaParams& mp, int ktc, bool strided, long grid, hipStream_t st);
+int launch_mfma_dc(const MfmaParams& mp, int ktc, int variant, long grid, hipStream_t st);
 
-template <int DC, int KTC, bool STRIDED, class E>
+// LDS of the DWC weights and bias in the MOD instances.
+template <int DC>
+constexpr int dwc_lds_bytes() { return 10 * 32 * DC * 4; }
+
+template <int DC, int KTC, bool STRIDED, class E, bool MOD>
 int launch_mfma_one(const MfmaParams& mp, long grid, hipStream_t st) {
-  agent_mfma_kernel<DC, KTC, STRIDED, E>
-      <<<dim3((unsigned)grid), dim3(kThreads), (unsigned)Cfg<DC, KTC>::TOTAL, st>>>(mp);
+  const unsigned lds = (unsigned)(Cfg<DC, KTC>::TOTAL + (MOD ? dwc_lds_bytes<DC>() : 0));
+  agent_mfma_kernel<DC, KTC, STRIDED, E, MOD><<<dim3((unsigned)grid), dim3(kThreads), lds, st>>>(mp);
   return (int)hipGetLastError();
+}
+
+// Kernel variants: the dense layout, caller strides, and the dense layout
+// with the module terms (agent biases, depth-wise convolution).
+enum Variant { kDense = 0, kStrided = 1, kModule = 2 };
+
+template <int DC, int KTC, class E>
+int launch_mfma_variant(const MfmaParams& mp, int variant, long grid, hipStream_t st) {
+  switch (variant) {
+    case kStrided: return launch_mfma_one<DC, KTC, true, E, false>(mp, grid, st);
+    case kModule: return launch_mfma_one<DC, KTC, false, E, true>(mp, grid, st);
+    default: return launch_mfma_one<DC, KTC, false, E, false>(mp, grid, st);
+  }
 }
 
 // Agent tiles of 16: KTC = 4 (<= 64 agents), 8 (<= 128), 16 (<= 256).
 template <int DC, class E>
-int launch_mfma_switch(const MfmaParams& mp, int ktc, bool strided, long grid, hipStream_t st) {
+int launch_mfma_switch(const MfmaParams& mp, int ktc, int variant, long grid, hipStream_t st) {
   switch (ktc) {
-    case 4:
-      return strided ? launch_mfma_one<DC, 4, true, E>(mp, grid, st)
-                     : launch_mfma_one<DC, 4, false, E>(mp, grid, st);
-    case 8:
-      return strided ? launch_mfma_one<DC, 8, true, E>(mp, grid, st)
-                     : launch_mfma_one<DC, 8, false, E>(mp, grid, st);
-    default:
-      return strided ? launch_mfma_one<DC, 16, true, E>(mp, grid, st)
-                     : launch_mfma_one<DC, 16, false, E>(mp, grid, st);
+    case 4: return launch_mfma_variant<DC, 4, E>(mp, variant, grid, st);
+    case 8: return launch_mfma_variant<DC, 8, E>(mp, variant, grid, st);
+    default: return launch_mfma_variant<DC, 16, E>(mp, variant, grid, st);
   }
 }
 

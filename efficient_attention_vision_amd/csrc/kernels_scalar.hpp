@@ -20,6 +20,17 @@ namespace aa {
 // A[bh, i*s+j, :] = mean of q over grid rows [floor(i h/s), ceil((i+1) h/s))
 // and columns [floor(j w/s), ceil((j+1) w/s)).  One block (256 threads) per
 // (bh, agent): 64 lanes over channels x 4 groups over window rows.
+// Module terms of the scalar broadcast (each pointer may be null): agent
+// bias B2 [H, N, nag], and the depth-wise convolution of V (same layout as
+// Q) with weights [H*d, 3, 3], bias [H*d], over a grid of width w.
+struct ScalarMod {
+  const float* bias2;
+  const void* v;
+  const float* dwc_w;
+  const float* dwc_b;
+  int w;
+};
+
 template <typename T>
 __global__ void __launch_bounds__(256)
 pool_kernel(const T* __restrict__ q, float* __restrict__ A, int h, int w, int d, int s,
@@ -64,7 +75,8 @@ template <typename T, int MAXD>
 __global__ void __launch_bounds__(256)
 aggregate_partial_scalar(const float* __restrict__ A, const T* __restrict__ K,
                          const T* __restrict__ V, float* __restrict__ part, int N, int d,
-                         int nag, float sl2, int chunk, int nchunks, Strides sk) {
+                         int nag, float sl2, int chunk, int nchunks, Strides sk,
+                         const float* __restrict__ bias1) {
   constexpr int TS = MAXD > 64 ? 16 : 32;
   const int ch = blockIdx.x % nchunks;
   const long bh = blockIdx.x / nchunks;
@@ -82,6 +94,8 @@ aggregate_partial_scalar(const float* __restrict__ A, const T* __restrict__ K,
   const int n0 = ch * chunk, n1 = min(N, n0 + chunk);
   const T* Kh = K + head_offset(sk, bh);
   const T* Vh = V + head_offset(sk, bh);
+  // agent bias B1[h][t][n] of the head's parameters (null: none)
+  const float* b1 = bias1 ? bias1 + ((bh % sk.H) * nag + (active ? t : 0)) * (long)N : nullptr;
   for (int nb = n0; nb < n1; nb += TS) {
     const int cnt = min(TS, n1 - nb);
     __syncthreads();
@@ -101,6 +115,7 @@ aggregate_partial_scalar(const float* __restrict__ A, const T* __restrict__ K,
         for (int c = 0; c < MAXD; ++c)
           if (c < d) dot = fmaf(a[c], Ks[tok][c], dot);
         sc[tok] = dot * sl2;
+        if (b1 && tok < cnt) sc[tok] = fmaf(b1[nb + tok], kLog2e, sc[tok]);
         if (tok < cnt) mx = fmaxf(mx, sc[tok]);
       }
       const float corr = fast_exp2(m - mx);
@@ -159,7 +174,7 @@ template <typename T, int MAXD>
 __global__ void __launch_bounds__(256)
 broadcast_scalar(const T* __restrict__ Q, const float* __restrict__ A,
                  const float* __restrict__ VA, T* __restrict__ O, int N, int d, int nag,
-                 float sl2, int nqblk, Strides sq) {
+                 float sl2, int nqblk, Strides sq, ScalarMod md) {
   constexpr int AC = MAXD > 64 ? 16 : 32;
   const int qb = blockIdx.x % nqblk;
   const long bh = blockIdx.x / nqblk;
@@ -177,6 +192,8 @@ broadcast_scalar(const T* __restrict__ Q, const float* __restrict__ A,
   float m = -INFINITY, l = 0.f;
   const float* Ah = A + bh * (long)nag * d;
   const float* Vh = VA + bh * (long)nag * d;
+  const long hh = bh % sq.H;   // head of the batch entry: index of the module parameters
+  const float* b2 = md.bias2 ? md.bias2 + (hh * N + (active ? n : 0)) * (long)nag : nullptr;
   for (int a0 = 0; a0 < nag; a0 += AC) {
     const int cnt = min(AC, nag - a0);
     __syncthreads();
@@ -195,6 +212,7 @@ broadcast_scalar(const T* __restrict__ Q, const float* __restrict__ A,
       for (int c = 0; c < MAXD; ++c)
         if (c < d) dot = fmaf(qv[c], As[ag][c], dot);
       sc[ag] = dot * sl2;
+      if (b2 && ag < cnt) sc[ag] = fmaf(b2[a0 + ag], kLog2e, sc[ag]);
       if (ag < cnt) mx = fmaxf(mx, sc[ag]);
     }
     const float corr = fast_exp2(m - mx);
@@ -217,8 +235,28 @@ broadcast_scalar(const T* __restrict__ Q, const float* __restrict__ A,
     T* orow = O + head_offset(sq, bh) + (long)n * sq.n;
     const float inv = 1.0f / l;
 #pragma unroll
+    for (int c = 0; c < MAXD; ++c) o[c] *= inv;
+    if (md.dwc_w) {
+      // + DWC(V): 3 x 3 neighbourhood of token n on the grid, zero outside
+      const T* Vsrc = static_cast<const T*>(md.v) + head_offset(sq, bh);
+      const int row = n / md.w, col = n - row * md.w, rows = N / md.w;
+#pragma unroll
+      for (int c = 0; c < MAXD; ++c) {
+        if (c >= d) continue;
+        const long ch = hh * d + c;
+        float acc = md.dwc_b ? md.dwc_b[ch] : 0.f;
+        for (int tap = 0; tap < 9; ++tap) {
+          const int rr = row + tap / 3 - 1, cc = col + tap % 3 - 1;
+          if (rr >= 0 && rr < rows && cc >= 0 && cc < md.w)
+            acc = fmaf(md.dwc_w[ch * 9 + tap], to_f32(Vsrc[(long)(rr * md.w + cc) * sq.n + c]),
+                       acc);
+        }
+        o[c] += acc;
+      }
+    }
+#pragma unroll
     for (int c = 0; c < MAXD; ++c)
-      if (c < d) orow[c] = from_f32<T>(o[c] * inv);
+      if (c < d) orow[c] = from_f32<T>(o[c]);
   }
 }
 

@@ -5,9 +5,9 @@
 namespace aa {
 
 template <>
-int launch_mfma_dc<4, ElemBF16>(const MfmaParams& mp, int ktc, bool strided, long grid,
+int launch_mfma_dc<4, ElemBF16>(const MfmaParams& mp, int ktc, int variant, long grid,
                               hipStream_t st) {
-  return launch_mfma_switch<4, ElemBF16>(mp, ktc, strided, grid, st);
+  return launch_mfma_switch<4, ElemBF16>(mp, ktc, variant, grid, st);
 }
 
 }  // namespace aa

@@ -172,3 +172,22 @@ def make_inputs(wl: Workload, seed: int, kind: str = "iid") -> Inputs:
         raise ValueError(f"unknown input kind {kind!r}")
     return Inputs(wl, _pack(q, wl.dtype), _pack(k, wl.dtype), _pack(v, wl.dtype),
                   _pack(a, wl.dtype) if a is not None else None)
+
+
+def make_module_terms(wl: Workload, seed: int, terms=("bias_agg", "bias_bcast", "dwc")) -> dict:
+    """Seeded float32 parameters of the module terms for workload `wl`:
+    agent biases B1 [H, k, N] and B2 [H, N, k] ~ N(0, 1) (the size of the
+    logits they are added to), depth-wise convolution weights [H*d, 3, 3] ~
+    N(0, 1/9) (so that the term is about as large as V) and its bias [H*d] ~
+    N(0, 0.25).  Keys: bias_agg, bias_bcast, dwc_weight, dwc_bias (None for
+    terms not asked for).  Drawn in that order from PCG64(seed + 7919)."""
+    rng = np.random.Generator(np.random.PCG64(seed + 7919))
+    H, k, N, d = wl.H, wl.k, wl.N, wl.d
+    b1 = rng.standard_normal((H, k, N)).astype(np.float32)
+    b2 = rng.standard_normal((H, N, k)).astype(np.float32)
+    w = (rng.standard_normal((H * d, 3, 3)) / 3.0).astype(np.float32)
+    b = (0.5 * rng.standard_normal(H * d)).astype(np.float32)
+    return {"bias_agg": b1 if "bias_agg" in terms else None,
+            "bias_bcast": b2 if "bias_bcast" in terms else None,
+            "dwc_weight": w if "dwc" in terms else None,
+            "dwc_bias": b if "dwc" in terms else None}

@@ -130,6 +130,36 @@ int agent_attn_forward_strided(const void* q, const void* k, const void* v,
                                float scale, int dtype, void* workspace,
                                size_t workspace_bytes, void* stream);
 
+/* The full module's forward (sources: "Agent Attention: On the Integration
+ * of Softmax and Linear Attention", §4 Module Enhancements, Implementation
+ * Details and the Efficiency paragraph): the operator above with the agent
+ * biases added to the scaled logits of both attentions and the depth-wise
+ * convolution of V added to the output,
+ *   V_A = softmax(scale A K^T + B1) V,   O = softmax(scale Q A^T + B2) V_A + DWC(V).
+ * The page names the biases' construction (column, row and block
+ * components) without giving it, so the caller passes the full tensors:
+ *   bias_agg   : NULL or B1, float32 [H, k, N] (k = s*s), shared by the batch;
+ *   bias_bcast : NULL or B2, float32 [H, N, k], shared by the batch;
+ *   dwc_weight : NULL (no convolution term) or float32 [H*d, 3, 3]: channel c
+ *                of head h uses row h*d + c; out[n] += sum over the 3 x 3
+ *                grid neighbourhood of token n of weight[dy+1][dx+1] *
+ *                v[neighbour] (cross-correlation), taps outside the h x w
+ *                grid reading zero;
+ *   dwc_bias   : NULL (zero) or float32 [H*d]; ignored without dwc_weight.
+ * All four are device pointers, 4-byte aligned, read only, and must not
+ * overlap out or the workspace (AGENT_ATTN_ERR_ALIGN / _ALIAS otherwise);
+ * one head's bias may span at most 2^31 bytes.  With all four NULL this is
+ * agent_attn_forward_ws.  Tensors are dense [B, H, N, d]; the other
+ * arguments, the workspace (agent_attn_workspace_bytes) and the errors are
+ * those of agent_attn_forward_ws.  The call allocates nothing. */
+int agent_attn_forward_module(const void* q, const void* k, const void* v,
+                              void* out, const void* agents,
+                              const float* bias_agg, const float* bias_bcast,
+                              const float* dwc_weight, const float* dwc_bias,
+                              int B, int H, int h, int w, int d, int s,
+                              float scale, int dtype, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
 /* Step 1 alone: agents_f32 [B, H, s*s, d] (float32) = 2-D average pool of q. */
 int agent_attn_pool(const void* q, float* agents_f32, int B, int H, int h,
                     int w, int d, int s, int dtype, void* stream);

@@ -163,3 +163,30 @@ def test_strided_validation(L, sb, sh, sn, code):
 def test_strided_huge_head_span_rejected(L):
     # one head spanning more than 2^31 bytes of bf16
     assert strided(L, 1 << 34, 1 << 33, 1 << 26, B=1, H=1, h=64, w=64) == ERR_SHAPE
+
+
+# ---------------------------------------------------------- module forward
+
+def modfwd(L, *, b1=None, b2=None, w=None, wb=None, out=P[3], ws=WS, ws_bytes=1 << 40, dtype=1,
+           d=64):
+    return L.agent_attn_forward_module(P[0], P[1], P[2], out, None, b1, b2, w, wb, 2, 3, 8, 8,
+                                       d, 4, 0.125, dtype, ws, ws_bytes, None)
+
+
+def test_module_forward_validates_its_parameters(L):
+    """Misaligned, overlapping or oversized bias / convolution buffers are
+    rejected on the host, after the checks of the plain forward."""
+    good = ctypes.c_void_p(P[5].value)
+    assert modfwd(L, b1=ctypes.c_void_p(good.value + 2)) == ERR_ALIGN
+    assert modfwd(L, w=ctypes.c_void_p(good.value + 1)) == ERR_ALIGN
+    # out covers [P3, P3 + 2*3*64*64*2): a bias starting inside it aliases
+    assert modfwd(L, b2=ctypes.c_void_p(P[3].value + 4096)) == ERR_ALIAS
+    assert modfwd(L, wb=ctypes.c_void_p(P[3].value + 64), w=good) == ERR_ALIAS
+    # the workspace may not overlap them either
+    assert modfwd(L, b1=ctypes.c_void_p(WS.value + 256)) == ERR_ALIAS
+    # plain-forward checks still apply
+    assert modfwd(L, b1=good, d=12) == ERR_UNSUP
+    assert modfwd(L, b1=good, dtype=5) == ERR_DTYPE
+    assert modfwd(L, b1=good, ws=None) == ERR_WS
+    # a DWC bias without weights is ignored (no alias check against it)
+    assert modfwd(L, wb=ctypes.c_void_p(P[3].value + 64), ws_bytes=10) == ERR_WS
