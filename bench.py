@@ -215,8 +215,9 @@ def algorithmic_flops(wl) -> int:
     return 8 * wl.B * wl.H * wl.N * wl.k * wl.d
 
 
-def cpu_baseline(wl, min_seconds=10.0):
-    """The float64 oracle timed on the host cores on the same workload shape."""
+def cpu_baseline(wl, min_seconds=10.0, module=False):
+    """The float64 oracle timed on the host cores on the same workload shape
+    (with the module terms when `module`)."""
     import numpy as np
     from threadpoolctl import threadpool_info
     import oracle
@@ -224,9 +225,11 @@ def cpu_baseline(wl, min_seconds=10.0):
 
     inp = inputs.make_inputs(wl, 0, "iid")
     A = None if inp.A is None else inp.A.exact
+    mt = inputs.make_module_terms(wl, 0) if module else {}
     reps, t0 = 0, time.perf_counter()
     while True:
-        oracle.forward(inp.Q.exact, inp.K.exact, inp.V.exact, wl.h, wl.w, wl.s, wl.scale, A=A)
+        oracle.forward(inp.Q.exact, inp.K.exact, inp.V.exact, wl.h, wl.w, wl.s, wl.scale, A=A,
+                       **mt)
         reps += 1
         el = time.perf_counter() - t0
         if el >= min_seconds and reps >= 2:
@@ -274,6 +277,11 @@ def main():
     ap.add_argument("--layout", choices=("bhnd", "bnhd"), default="bhnd",
                     help="q/k/v/out as dense [B,H,N,d] (default) or as [B,N,H,d] storage "
                          "(strided views, as a head-split projection leaves them)")
+    ap.add_argument("--module", action="store_true",
+                    help="time the full module forward: agent biases in both attentions and "
+                         "the depth-wise 3x3 convolution of V (agent_attn_forward_module)")
+    ap.add_argument("--dtype", choices=("bf16", "f16"), default=None,
+                    help="16-bit element type of the tensors (default: the workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -308,9 +316,15 @@ def main():
     from efficient_attention_vision_amd import _binding, inputs
 
     wl = inputs.WORKLOADS[args.workload]
+    if args.dtype and wl.dtype != "f32":
+        import dataclasses
+        wl = dataclasses.replace(wl, dtype=args.dtype)
+    if args.module and args.layout != "bhnd":
+        print("bench.py: --module takes the dense layout only", file=sys.stderr)
+        sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    dt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[wl.dtype]
     shape = (wl.B, wl.H, wl.N, wl.d)
     set_bytes = algorithmic_bytes(wl)
     R = max(2, min(args.steps, math.ceil((1 << 30) / set_bytes)))
@@ -330,11 +344,21 @@ def main():
     need = _binding.agent_attn_workspace_bytes(wl.B, wl.H, wl.h, wl.w, wl.d, wl.s,
                                                0 if wl.dtype == "f32" else 1)
     ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+    mod = {}
+    if args.module:   # module parameters, shared by the batch (same recipe as the tests)
+        mod = {"bias_agg": torch.randn((wl.H, wl.k, wl.N), generator=gen, device=dev),
+               "bias_bcast": torch.randn((wl.H, wl.N, wl.k), generator=gen, device=dev),
+               "dwc_weight": torch.randn((wl.H * wl.d, 3, 3), generator=gen, device=dev) / 3,
+               "dwc_bias": 0.5 * torch.randn((wl.H * wl.d,), generator=gen, device=dev)}
 
     def step(i):
         q, k, v, a, o = sets[i % R]
-        eav.agent_attn_forward(q, k, v, (wl.h, wl.w), wl.s, wl.scale, agents=a, out=o,
-                               workspace=ws)
+        if args.module:
+            eav.agent_attn_forward_module(q, k, v, (wl.h, wl.w), wl.s, wl.scale, agents=a, out=o,
+                                          workspace=ws, **mod)
+        else:
+            eav.agent_attn_forward(q, k, v, (wl.h, wl.w), wl.s, wl.scale, agents=a, out=o,
+                                   workspace=ws)
 
     stream = torch.cuda.current_stream(dev)
     for i in range(args.warmup):
@@ -381,9 +405,14 @@ def main():
     value = tokens / (ms_per_step * 1e-3)
     abytes = algorithmic_bytes(wl)
     aflops = algorithmic_flops(wl)
+    if args.module:   # + the two biases (read once, shared by the batch), + 9 MACs per output
+        abytes += 2 * wl.H * wl.k * wl.N * 4
+        aflops += 18 * wl.B * wl.H * wl.N * wl.d
     achieved_gbs = abytes / (kernel_us * 1e-6) / 1e9
     achieved_tflops = aflops / (kernel_us * 1e-6) / 1e12
-    traffic = measured_traffic(wl.name)
+    # counters were taken on the plain bf16 dense kernel: other variants report none
+    plain = not args.module and args.layout == "bhnd" and wl.dtype in ("bf16", "f32")
+    traffic = measured_traffic(wl.name) if plain else None
     if wl.k >= 256:
         roof = {"bound": "mfma", "achieved": achieved_tflops, "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": achieved_tflops / BF16_PEAK_TFLOPS, "traffic": traffic}
@@ -406,7 +435,9 @@ def main():
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "grid": [wl.h, wl.w], "N": wl.N,
                    "d": wl.d, "agents": wl.k, "agent_grid": [wl.s, wl.s],
                    "supplied_agents": wl.supplied_agents, "rotating_sets": R,
-                   "layout": "[B,N,H,d] storage" if args.layout == "bnhd" else "[B,H,N,d]"},
+                   "layout": "[B,N,H,d] storage" if args.layout == "bnhd" else "[B,H,N,d]",
+                   **({"module_terms": ["agent biases B1, B2", "depth-wise 3x3 conv of V"]}
+                      if args.module else {})},
         "roofline": roof,
         "kernel_us_per_launch": kernel_us,
         "eager_launch_us": {"median": pct(0.5), "p10": pct(0.1), "p90": pct(0.9)},
@@ -416,7 +447,7 @@ def main():
         "algorithmic_flops": aflops,
     }
     if not args.no_cpu_baseline:
-        cb = cpu_baseline(wl, args.cpu_seconds)
+        cb = cpu_baseline(wl, args.cpu_seconds, module=args.module)
         cb.pop("seconds", None)
         line["cpu_baseline"] = cb
     print(json.dumps(line), flush=True)

@@ -560,10 +560,36 @@ struct AggState {
   f32x4 lacc[ATW];   // row sums of the probabilities, on the matrix cores
 };
 
+// B1 of one block for agent tile t of this lane: tokens tok0 + 4 g .. +3
+// (b[0]) and tok0 + 16 + 4 g .. +3 (b[1]) of agent row 16 t + r, in score
+// units; 16-byte loads when the rows are 16-byte aligned.
+__device__ __forceinline__ void load_b1(const ModCtx& mc, int t, int tok0, float4 (&b)[2]) {
+  const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+  const int a = 16 * t + r;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int n = tok0 + 16 * h + 4 * g;
+    if ((mc.N & 3) == 0) {
+      const unsigned o = (a < mc.nag && n < mc.N) ? (unsigned)((a * mc.N + n) * 4) : kOOB;
+      b[h] = bits_f4(bld16<kPlain>(mc.b1, o));
+    } else {
+      float x[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const unsigned o =
+            (a < mc.nag && n + i < mc.N) ? (unsigned)((a * mc.N + n + i) * 4) : kOOB;
+        x[i] = bld4<kPlain>(mc.b1, o);
+      }
+      b[h] = float4{x[0], x[1], x[2], x[3]};
+    }
+  }
+}
+
 template <class E, class C, int DC, int ATW, bool MOD>
 __device__ __forceinline__ void agg_block(AggState<DC, ATW>& st, const bf16_t* Ks,
                                           const bf16x8* Af, const bf16_t* Vt, int blk_col, int ag,
-                                          int valid, float sl2, const ModCtx& mc, int tok0) {
+                                          int valid, float sl2, const ModCtx& mc,
+                                          const float4 (&b1)[ATW][2]) {
   constexpr int DT = 2 * DC;
   const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
   // K fragments: token row blk_col + 16tt + r, channel chunk DC*g + c
@@ -595,16 +621,15 @@ __device__ __forceinline__ void agg_block(AggState<DC, ATW>& st, const bf16_t* K
       S1 = E::mma(kf[1][c], af, S1);
     }
     if constexpr (MOD) {
-      if (mc.has_b1) {   // B1[agent 16t + r][tokens tok0 + 16tt + 4g + i], in score units
-        const int a = 16 * t + r;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int n0i = tok0 + 4 * g + i, n1i = n0i + 16;
-          const unsigned o0 = (a < mc.nag && n0i < mc.N) ? (unsigned)((a * mc.N + n0i) * 4) : kOOB;
-          const unsigned o1 = (a < mc.nag && n1i < mc.N) ? (unsigned)((a * mc.N + n1i) * 4) : kOOB;
-          S0[i] = fmaf(bld4<kPlain>(mc.b1, o0), mc.inv_scale, S0[i]);
-          S1[i] = fmaf(bld4<kPlain>(mc.b1, o1), mc.inv_scale, S1[i]);
-        }
+      if (mc.has_b1) {   // B1 of this block (loaded one block ahead), in score units
+        S0[0] = fmaf(b1[a][0].x, mc.inv_scale, S0[0]);
+        S0[1] = fmaf(b1[a][0].y, mc.inv_scale, S0[1]);
+        S0[2] = fmaf(b1[a][0].z, mc.inv_scale, S0[2]);
+        S0[3] = fmaf(b1[a][0].w, mc.inv_scale, S0[3]);
+        S1[0] = fmaf(b1[a][1].x, mc.inv_scale, S1[0]);
+        S1[1] = fmaf(b1[a][1].y, mc.inv_scale, S1[1]);
+        S1[2] = fmaf(b1[a][1].z, mc.inv_scale, S1[2]);
+        S1[3] = fmaf(b1[a][1].w, mc.inv_scale, S1[3]);
       }
     }
     if (valid < 32) {   // rows 16tt + 4g + i past the slice end
@@ -692,28 +717,38 @@ __device__ __forceinline__ void bcast_probs(const bf16x8 (&qf)[DC], const bf16x8
     asm volatile("" : "+v"(fl));
     asm volatile("" : "+s"(nag_t));
   }
+  // B2[token tok0 + r][agents 16t + 4g + i] (score units), loaded before the
+  // score products so that the loads travel while they run
   f32x4 S[KTC];
 #pragma unroll
-  for (int t = 0; t < KTC; ++t) {
-    S[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < DC; ++c)
-      S[t] = E::mma(Af[(t * DC + c) * 64 + fl], qf[c], S[t]);
-  }
+  for (int t = 0; t < KTC; ++t) S[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   if constexpr (MOD) {
-    if (mc.has_b2) {   // B2[token tok0 + r][agents 16t + 4g + i], in score units
+    if (mc.has_b2) {
       const int tok = tok0 + (lane & 15);
 #pragma unroll
       for (int t = 0; t < KTC; ++t) {
-        if (t % 4 == 0) asm volatile("" ::: "memory");   // 16 loads in flight at most
+        const int a0 = 16 * t + 4 * g;
+        if ((mc.nag & 3) == 0) {
+          const unsigned o = (tok < mc.N && a0 < nag_t) ? (unsigned)((tok * mc.nag + a0) * 4) : kOOB;
+          const float4 x = bits_f4(bld16<kPlain>(mc.b2, o));
+          S[t] = f32x4{x.x * mc.inv_scale, x.y * mc.inv_scale, x.z * mc.inv_scale,
+                       x.w * mc.inv_scale};
+        } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int a = 16 * t + 4 * g + i;
-          const unsigned o = (tok < mc.N && a < nag_t) ? (unsigned)((tok * mc.nag + a) * 4) : kOOB;
-          S[t][i] = fmaf(bld4<kPlain>(mc.b2, o), mc.inv_scale, S[t][i]);
+          for (int i = 0; i < 4; ++i) {
+            const unsigned o =
+                (tok < mc.N && a0 + i < nag_t) ? (unsigned)((tok * mc.nag + a0 + i) * 4) : kOOB;
+            S[t][i] = bld4<kPlain>(mc.b2, o) * mc.inv_scale;
+          }
         }
       }
     }
+  }
+#pragma unroll
+  for (int t = 0; t < KTC; ++t) {
+#pragma unroll
+    for (int c = 0; c < DC; ++c)
+      S[t] = E::mma(Af[(t * DC + c) * 64 + fl], qf[c], S[t]);
   }
 #pragma unroll
   for (int t = 0; t < KTC; ++t)
@@ -747,32 +782,47 @@ __device__ __forceinline__ void bcast_probs(const bf16x8 (&qf)[DC], const bf16x8
 }
 
 // Depth-wise 3 x 3 convolution of V at grid position (row, col) for
-// channels ch .. ch+3: bias + sum over the taps inside the grid of weight *
-// V (weights and bias from LDS, [9][32 DC] then [32 DC]).  Not inlined, so
-// that its loads stay within one call instead of being hoisted across the
-// caller's tiles.
+// channels ch .. ch+3 and ch+16 .. ch+19: bias + sum over the taps inside
+// the grid of weight * V (weights and bias from LDS, [9][32 DC] then
+// [32 DC]).  Not inlined, so that its 18 loads stay within one call instead
+// of being hoisted across the caller's tiles.
+struct F8 {
+  float4 lo, hi;
+};
 template <class E, int DC>
-__device__ __attribute__((noinline)) float4 dwc4(rsrc_t rv, const float* wl, int rows, int w,
-                                                 int row, int col, int ch, int d, int sn) {
-  const float4 b = *reinterpret_cast<const float4*>(wl + 9 * 32 * DC + ch);
-  float acc[4] = {b.x, b.y, b.z, b.w};
-  u32x2 v[9];
+__device__ __attribute__((noinline)) F8 dwc8(rsrc_t rv, const float* wl, int rows, int w, int row,
+                                             int col, int ch, int d, int sn) {
+  constexpr int DPAD = 32 * DC;
+  u32x2 v[2][9];
 #pragma unroll
   for (int tap = 0; tap < 9; ++tap) {
     const int rr = row + tap / 3 - 1, cc = col + tap % 3 - 1;
-    const bool in = rr >= 0 && rr < rows && cc >= 0 && cc < w && ch < d;
-    v[tap] = __builtin_amdgcn_raw_buffer_load_b64(
-        rv, in ? (int)(((rr * w + cc) * sn + ch) * 2) : (int)kOOB, 0, kPlain);
-  }
+    const bool in = rr >= 0 && rr < rows && cc >= 0 && cc < w;
 #pragma unroll
-  for (int tap = 0; tap < 9; ++tap) {
-    const float4 wt = *reinterpret_cast<const float4*>(wl + tap * 32 * DC + ch);
-    acc[0] = fmaf(wt.x, E::value((uint16_t)(v[tap][0] & 0xffffu)), acc[0]);
-    acc[1] = fmaf(wt.y, E::value((uint16_t)(v[tap][0] >> 16)), acc[1]);
-    acc[2] = fmaf(wt.z, E::value((uint16_t)(v[tap][1] & 0xffffu)), acc[2]);
-    acc[3] = fmaf(wt.w, E::value((uint16_t)(v[tap][1] >> 16)), acc[3]);
+    for (int h = 0; h < 2; ++h)
+      v[h][tap] = __builtin_amdgcn_raw_buffer_load_b64(
+          rv, (in && ch + 16 * h < d) ? (int)(((rr * w + cc) * sn + ch + 16 * h) * 2) : (int)kOOB,
+          0, kPlain);
   }
-  return float4{acc[0], acc[1], acc[2], acc[3]};
+  float acc[2][4];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const float4 b = *reinterpret_cast<const float4*>(wl + 9 * DPAD + ch + 16 * h);
+    acc[h][0] = b.x;
+    acc[h][1] = b.y;
+    acc[h][2] = b.z;
+    acc[h][3] = b.w;
+#pragma unroll
+    for (int tap = 0; tap < 9; ++tap) {
+      const float4 wt = *reinterpret_cast<const float4*>(wl + tap * DPAD + ch + 16 * h);
+      acc[h][0] = fmaf(wt.x, E::value((uint16_t)(v[h][tap][0] & 0xffffu)), acc[h][0]);
+      acc[h][1] = fmaf(wt.y, E::value((uint16_t)(v[h][tap][0] >> 16)), acc[h][1]);
+      acc[h][2] = fmaf(wt.z, E::value((uint16_t)(v[h][tap][1] & 0xffffu)), acc[h][2]);
+      acc[h][3] = fmaf(wt.w, E::value((uint16_t)(v[h][tap][1] >> 16)), acc[h][3]);
+    }
+  }
+  return F8{float4{acc[0][0], acc[0][1], acc[0][2], acc[0][3]},
+            float4{acc[1][0], acc[1][1], acc[1][2], acc[1][3]}};
 }
 
 // Stores one normalised 16-token output tile held in the matrix-core result
@@ -796,13 +846,17 @@ __device__ __forceinline__ void store_o_tile(const f32x4 (&O)[2 * DC], float inv
       const int row = tok < tok_end ? idiv(tok, mc.w, rcp_approx(mc.w)) : -4;
       const int col = tok - row * mc.w;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const float4 x =
-            dwc4<E, DC>(mc.rv, mc.wl, mc.N / mc.w, mc.w, row, col, 16 * dt + 4 * g, d, sn);
-        val[dt][0] += x.x;
-        val[dt][1] += x.y;
-        val[dt][2] += x.z;
-        val[dt][3] += x.w;
+      for (int dt = 0; dt < DT; dt += 2) {   // tiles dt and dt + 1 (channels +16)
+        const F8 x =
+            dwc8<E, DC>(mc.rv, mc.wl, mc.N / mc.w, mc.w, row, col, 16 * dt + 4 * g, d, sn);
+        val[dt][0] += x.lo.x;
+        val[dt][1] += x.lo.y;
+        val[dt][2] += x.lo.z;
+        val[dt][3] += x.lo.w;
+        val[dt + 1][0] += x.hi.x;
+        val[dt + 1][1] += x.hi.y;
+        val[dt + 1][2] += x.hi.z;
+        val[dt + 1][3] += x.hi.w;
       }
     }
   }
@@ -1197,9 +1251,28 @@ agent_mfma_kernel(MfmaParams p) {
       }
       __syncthreads();
       AA_STAMP(12);
+      // agent biases of this wave's blocks, loaded one block ahead
+      float4 b1c[ATW][2], b1n[ATW][2];
+      if constexpr (MOD) {
+        if (mc.has_b1 && tg < rblk)
+#pragma unroll
+          for (int a = 0; a < ATW; ++a) load_b1(mc, ATW * ag + a, rt0 + 32 * tg, b1c[a]);
+      }
       for (int b = tg; b < rblk; b += C::TG) {
+        if constexpr (MOD) {
+          if (mc.has_b1 && b + C::TG < rblk)
+#pragma unroll
+            for (int a = 0; a < ATW; ++a) load_b1(mc, ATW * ag + a, rt0 + 32 * (b + C::TG), b1n[a]);
+        }
         agg_block<E, C, DC, ATW, MOD>(st, Ks, Af, Vt, 32 * b, ag, min(32, n1 - (rt0 + 32 * b)),
-                                      p.sl2, mc, rt0 + 32 * b);
+                                      p.sl2, mc, b1c);
+        if constexpr (MOD) {
+#pragma unroll
+          for (int a = 0; a < ATW; ++a) {
+            b1c[a][0] = b1n[a][0];
+            b1c[a][1] = b1n[a][1];
+          }
+        }
 #ifdef AGENT_ATTN_PHASE_TRACE
         if (b / C::TG < 4) {
           __builtin_amdgcn_s_waitcnt(0);
