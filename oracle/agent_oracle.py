@@ -170,3 +170,58 @@ def forward(Q, K, V, h: int, w: int, s: int, scale: float, A=None, bias_agg=None
     if dwc_weight is not None:
         O = O + dwc(V, h, w, dwc_weight, dwc_bias)
     return O, A, V_A
+
+
+# ------------------------------------------------------------------ backward
+
+def pool_agents_backward(dA: np.ndarray, h: int, w: int, s: int) -> np.ndarray:
+    """Gradient of pool_agents: each agent's gradient is spread evenly over
+    the tokens of its window (the pooling is a mean), and a token in two
+    windows (ragged grids) receives both shares.  dA: [B, H, s*s, d] ->
+    dQ: [B, H, h*w, d]."""
+    B, H, k, d = dA.shape
+    dgrid = np.zeros((B, H, h, w, d))
+    for i in range(s):
+        r0, r1 = window_bounds(i, h, s)
+        for j in range(s):
+            c0, c1 = window_bounds(j, w, s)
+            cnt = (r1 - r0) * (c1 - c0)
+            dgrid[:, :, r0:r1, c0:c1, :] += dA[:, :, i * s + j, None, None, :] / cnt
+    return dgrid.reshape(B, H, h * w, d)
+
+
+def softmax_backward(P: np.ndarray, dP: np.ndarray) -> np.ndarray:
+    """Gradient of a row softmax P = softmax(S) with respect to S:
+    dS = P * (dP - sum over the row of P * dP)."""
+    return P * (dP - (P * dP).sum(axis=-1, keepdims=True))
+
+
+def backward(Q, K, V, dO, h: int, w: int, s: int, scale: float, A=None):
+    """Gradients of the forward O = softmax(scale Q A^T) softmax(scale A K^T) V
+    with respect to Q, K, V (and A when the caller supplied it), by the chain
+    rule through the two Softmax attentions ([Paper] §4; [JSQMD] §1) and
+    the pooling (A = f(Q), [Paper] §6).  With pooled agents, Q receives the
+    gradient of the broadcast logits plus the pooled agents' gradient spread
+    over their windows.  Returns (dQ, dK, dV, dA) with dA None for pooled
+    agents, all float64.
+    """
+    Q, K, V, dO = (np.asarray(x, dtype=np.float64) for x in (Q, K, V, dO))
+    supplied = A is not None
+    A = np.asarray(A, dtype=np.float64) if supplied else pool_agents(Q, h, w, s)
+    KT = np.swapaxes(K, -1, -2)
+    P1 = softmax_last(scale * (A @ KT))                       # [B, H, k, N]
+    V_A = P1 @ V                                              # [B, H, k, d]
+    P2 = softmax_last(scale * (Q @ np.swapaxes(A, -1, -2)))   # [B, H, N, k]
+    # broadcast: O = P2 V_A
+    dV_A = np.swapaxes(P2, -1, -2) @ dO                       # [B, H, k, d]
+    dS2 = softmax_backward(P2, dO @ np.swapaxes(V_A, -1, -2))
+    dQ = scale * (dS2 @ A)
+    dA = scale * (np.swapaxes(dS2, -1, -2) @ Q)
+    # aggregation: V_A = P1 V
+    dV = np.swapaxes(P1, -1, -2) @ dV_A
+    dS1 = softmax_backward(P1, dV_A @ np.swapaxes(V, -1, -2))
+    dA = dA + scale * (dS1 @ K)
+    dK = scale * (np.swapaxes(dS1, -1, -2) @ A)
+    if supplied:
+        return dQ, dK, dV, dA
+    return dQ + pool_agents_backward(dA, h, w, s), dK, dV, None

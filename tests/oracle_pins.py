@@ -418,4 +418,88 @@ def pin_forward_module_is_library_composition(orc):
     assert np.allclose(O, ref, rtol=0, atol=1e-12)
 
 
+# ------------------------------------------------------------------ backward
+
+def _torch_forward(Q, K, V, h, w, s, scale, A=None):
+    """The forward composed of torch library routines (for autograd)."""
+    B, H, N, d = Q.shape
+    if A is None:
+        x = Q.reshape(B * H, h, w, d).permute(0, 3, 1, 2)
+        A = F.adaptive_avg_pool2d(x, (s, s)).permute(0, 2, 3, 1).reshape(B, H, s * s, d)
+    VA = F.scaled_dot_product_attention(A, K, V, scale=scale)
+    return F.scaled_dot_product_attention(Q, A, VA, scale=scale)
+
+
+def pin_backward_vs_torch_autograd(orc):
+    """Gradients equal torch's float64 autograd through adaptive pooling and
+    two scaled_dot_product_attention calls, on a ragged grid (windows share
+    a row) and with supplied agents."""
+    rng = _rng(71)
+    B, H, h, w, d, s, scale = 2, 2, 5, 7, 3, 2, 0.7
+    N = h * w
+    Q, K, V, dO = (rng.standard_normal((B, H, N, d)) for _ in range(4))
+    for A in (None, rng.standard_normal((B, H, s * s, d))):
+        dQ, dK, dV, dA = orc.backward(Q, K, V, dO, h, w, s, scale, A=A)
+        tq, tk, tv = (_t(x).requires_grad_(True) for x in (Q, K, V))
+        ta = None if A is None else _t(A).requires_grad_(True)
+        _torch_forward(tq, tk, tv, h, w, s, scale, ta).backward(_t(dO))
+        for got, ref in ((dQ, tq.grad), (dK, tk.grad), (dV, tv.grad)):
+            assert np.allclose(got, ref.numpy(), rtol=0, atol=1e-12)
+        if A is None:
+            assert dA is None
+        else:
+            assert np.allclose(dA, ta.grad.numpy(), rtol=0, atol=1e-12)
+
+
+def pin_backward_finite_differences(orc):
+    """Central differences of the loss sum(dO * O) along single coordinates
+    of Q, K, V and supplied A, on a tiny ragged case."""
+    rng = _rng(72)
+    B, H, h, w, d, s, scale, eps = 1, 1, 3, 4, 2, 2, 0.8, 1e-6
+    N = h * w
+    Q, K, V, dO = (rng.standard_normal((B, H, N, d)) for _ in range(4))
+    A0 = rng.standard_normal((B, H, s * s, d))
+    for A in (None, A0):
+        grads = orc.backward(Q, K, V, dO, h, w, s, scale, A=A)
+        names = ("Q", "K", "V") + (("A",) if A is not None else ())
+        for gi, name in enumerate(names):
+            for _ in range(4):
+                base = {"Q": Q, "K": K, "V": V, "A": A}
+                idx = tuple(int(rng.integers(0, n)) for n in base[name].shape)
+                vals = []
+                for sign in (1, -1):
+                    pert = {k_: (None if v_ is None else v_.copy()) for k_, v_ in base.items()}
+                    pert[name][idx] += sign * eps
+                    O, _, _ = orc.forward(pert["Q"], pert["K"], pert["V"], h, w, s, scale,
+                                          A=pert["A"])
+                    vals.append(float((dO * O).sum()))
+                fd = (vals[0] - vals[1]) / (2 * eps)
+                assert abs(fd - grads[gi][idx]) < 1e-7, (name, idx, fd, grads[gi][idx])
+
+
+def pin_backward_sums(orc):
+    """Closed forms of sums over the tokens: the key gradients sum to zero
+    (the output is invariant to translating every key, as each softmax row
+    is to a constant shift) and the value gradients sum to the sum of dO
+    (O is a row-stochastic mixing of the values)."""
+    rng = _rng(73)
+    B, H, h, w, d, s = 2, 3, 6, 6, 4, 3
+    Q, K, V, dO = (rng.standard_normal((B, H, h * w, d)) for _ in range(4))
+    _, dK, dV, _ = orc.backward(Q, K, V, dO, h, w, s, 0.6)
+    assert np.allclose(dK.sum(axis=2), 0.0, rtol=0, atol=1e-12)
+    assert np.allclose(dV.sum(axis=2), dO.sum(axis=2), rtol=0, atol=1e-12)
+
+
+def pin_pool_backward_is_adjoint(orc):
+    """<pool(Q), G> = <Q, pool_backward(G)> for random Q and G (the
+    pooling's gradient is its adjoint), ragged and divisible grids."""
+    rng = _rng(74)
+    for (h, w, s) in ((7, 5, 3), (8, 8, 4), (2, 9, 2)):
+        Q = rng.standard_normal((1, 2, h * w, 3))
+        G = rng.standard_normal((1, 2, s * s, 3))
+        lhs = float((orc.pool_agents(Q, h, w, s) * G).sum())
+        rhs = float((Q * orc.pool_agents_backward(G, h, w, s)).sum())
+        assert abs(lhs - rhs) < 1e-12
+
+
 ALL_PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_")]

@@ -187,6 +187,51 @@ def _forward_biases_swapped(Q, K, V, h, w, s, scale, A=None, bias_agg=None, bias
                          bias_bcast=sw(bias_agg), dwc_weight=dwc_weight, dwc_bias=dwc_bias)
 
 
+def _softmax_bw_no_centering(P, dP):
+    return P * dP
+
+
+def _softmax_bw_transposed_sum(P, dP):
+    return P * (dP - (P * dP).sum(axis=-2, keepdims=True))
+
+
+def _pool_bw_sum(dA, h, w, s):
+    """spread without dividing by the window size."""
+    B, H, k, d = dA.shape
+    g = np.zeros((B, H, h, w, d))
+    for i in range(s):
+        r0, r1 = orc.window_bounds(i, h, s)
+        for j in range(s):
+            c0, c1 = orc.window_bounds(j, w, s)
+            g[:, :, r0:r1, c0:c1, :] += dA[:, :, i * s + j, None, None, :]
+    return g.reshape(B, H, h * w, d)
+
+
+def _backward_wrong_probs_for_dv(Q, K, V, dO, h, w, s, scale, A=None):
+    """dV through the unnormalised aggregation weights exp(S1 - max)."""
+    dQ, dK, dV, dA = _orig_backward(Q, K, V, dO, h, w, s, scale, A=A)
+    Q, K = np.asarray(Q, float), np.asarray(K, float)
+    A_ = orc.pool_agents(Q, h, w, s) if A is None else np.asarray(A, float)
+    S1 = scale * (A_ @ np.swapaxes(K, -1, -2))
+    E1 = np.exp(S1 - S1.max(axis=-1, keepdims=True))
+    P2 = orc.softmax_last(scale * (Q @ np.swapaxes(A_, -1, -2)))
+    dV_A = np.swapaxes(P2, -1, -2) @ np.asarray(dO, float)
+    return dQ, dK, np.swapaxes(E1, -1, -2) @ dV_A, dA
+
+
+def _backward_no_pool_term(Q, K, V, dO, h, w, s, scale, A=None):
+    """pooled agents treated as constants (their gradient not sent to Q)."""
+    dQ, dK, dV, dA = _orig_backward(Q, K, V, dO, h, w, s, scale, A=np.asarray(
+        orc.pool_agents(np.asarray(Q, float), h, w, s)) if A is None else A)
+    return dQ, dK, dV, (None if A is None else dA)
+
+
+def _backward_dk_unscaled(Q, K, V, dO, h, w, s, scale, A=None):
+    dQ, dK, dV, dA = _orig_backward(Q, K, V, dO, h, w, s, scale, A=A)
+    return dQ, dK / scale, dV, dA
+
+
+_orig_backward = orc.backward
 _orig_dwc = orc.dwc
 _orig_forward = orc.forward
 
@@ -201,6 +246,12 @@ MUTANTS = {
     "dwc_bias_dropped": ("dwc", _dwc_no_bias),
     "forward_dwc_of_queries": ("forward", _forward_dwc_of_queries),
     "forward_biases_swapped": ("forward", _forward_biases_swapped),
+    "softmax_backward_uncentred": ("softmax_backward", _softmax_bw_no_centering),
+    "softmax_backward_column_sum": ("softmax_backward", _softmax_bw_transposed_sum),
+    "pool_backward_not_averaged": ("pool_agents_backward", _pool_bw_sum),
+    "backward_values_wrong": ("backward", _backward_wrong_probs_for_dv),
+    "backward_agents_held_constant": ("backward", _backward_no_pool_term),
+    "backward_key_gradient_unscaled": ("backward", _backward_dk_unscaled),
     "pool_column_major": ("pool_agents", _pool_column_major),
     "window_floor_stop": ("window_bounds", _window_floor),
     "pool_sum_not_mean": ("pool_agents", _pool_sum),
