@@ -32,6 +32,9 @@ _SIGNATURES = {
                                    [_c_float, _c_int, _vp, _c_size, _vp]),
     "agent_attn_forward_module": (_c_int, [_vp] * 9 + [_c_int] * 6 + [_c_float, _c_int, _vp,
                                                                        _c_size, _vp]),
+    "agent_attn_backward_workspace_bytes": (_c_size, [_c_int] * 7),
+    "agent_attn_backward": (_c_int, [_vp] * 9 + [_c_int] * 6 + [_c_float, _c_int, _vp, _c_size,
+                                                                 _vp]),
     "agent_attn_pool": (_c_int, [_vp, _vp] + [_c_int] * 7 + [_vp]),
     "agent_attn_aggregate_workspace_bytes": (_c_size, [_c_int] * 6),
     "agent_attn_aggregate": (_c_int, [_vp] * 4 + [_c_int] * 5 + [_c_float, _c_int, _vp, _c_size,
@@ -266,6 +269,41 @@ def agent_attn_forward_module(q, k, v, grid_hw, s, scale=None, agents=None, bias
                                          code, ws_ptr, ws_size, _stream(q.device))
     _check(rc)
     return out
+
+
+def agent_attn_backward(q, k, v, dout, grid_hw, s, scale=None, agents=None, workspace=None):
+    """Gradients (dq, dk, dv, dagents) of the forward agent_attn_forward(q, k,
+    v, grid_hw, s, scale, agents) for the output gradient dout.  dagents is
+    None for pooled agents (their gradient is part of dq).  Dense
+    [B, H, h*w, d] GPU tensors of one dtype; runs on torch's current stream."""
+    L = lib()
+    _dev_tensor(q, "q")
+    B, H, N, d = q.shape
+    h, w = (int(x) for x in grid_hw)
+    if h * w != N:
+        raise ValueError(f"grid {h}x{w} does not match N={N}")
+    for name, t in (("k", k), ("v", v), ("dout", dout)):
+        _dev_tensor(t, name)
+        _same(q, t, name, q.shape, q.dtype)
+    if agents is not None:
+        _dev_tensor(agents, "agents")
+        _same(q, agents, "agents", (B, H, int(s) * int(s), d), q.dtype)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    da = torch.empty_like(agents) if agents is not None else None
+    code = _dtype_code(q)
+    with torch.cuda.device(q.device):
+        need = L.agent_attn_backward_workspace_bytes(B, H, h, w, d, int(s), code)
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        rc = L.agent_attn_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(agents), _ptr(dq),
+                                   _ptr(dk), _ptr(dv), _ptr(da), B, H, h, w, d, int(s),
+                                   float(scale), code, _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(),
+                                   _stream(q.device))
+    _check(rc)
+    return dq, dk, dv, da
 
 
 def agent_attn_forward_cached(q, k, v, grid_hw, s, scale=None, agents=None, out=None):

@@ -17,6 +17,7 @@
 #include "common.hpp"
 #include "kernels_mfma.hpp"
 #include "kernels_scalar.hpp"
+#include "kernels_backward.hpp"
 
 namespace {
 
@@ -398,7 +399,7 @@ int launch_widen(const Dims& D, const void* src, float* dst, hipStream_t st) {
 template <typename T>
 int launch_aggregate(const Dims& D, const float* A, const void* k, const void* v, float* VA,
                      float* part, int chunk, int nchunks, float sl2, hipStream_t st,
-                     const float* bias1 = nullptr) {
+                     const float* bias1 = nullptr, float* lse = nullptr) {
   const long blocks = D.BH * nchunks;
   if (D.d <= 64)
     hipLaunchKernelGGL((aa::aggregate_partial_scalar<T, 64>), dim3((unsigned)blocks), dim3(256), 0,
@@ -410,7 +411,7 @@ int launch_aggregate(const Dims& D, const float* A, const void* k, const void* v
                        nchunks, D.strides(), bias1);
   AA_LAUNCH_CHECK("agent_aggregate launch");
   hipLaunchKernelGGL(aa::merge_partials_kernel, dim3((unsigned)(D.BH * D.nag)), dim3(128), 0, st,
-                     part, VA, D.d, D.nag, nchunks);
+                     part, VA, D.d, D.nag, nchunks, lse);
   AA_LAUNCH_CHECK("agent_aggregate merge launch");
   return AGENT_ATTN_OK;
 }
@@ -742,6 +743,117 @@ int forward_ws(const void* q, const void* k, const void* v, void* out, const voi
   return dispatch_forward(D, P, q, k, v, out, agents, scale, workspace, (hipStream_t)stream, mt);
 }
 
+// ------------------------------------------------------------- backward
+// Workspace of the backward pass (float32 regions, 256-byte aligned): A,
+// V_A, dV_A, dA [B*H, k, d]; lse1, D1 [B*H, k]; lse2, D2 [B*H, N]; two
+// per-chunk partial sets [B*H, chunks, k, d]; the aggregation's partials.
+struct BwdPlan {
+  int chunk = 0, nchunks = 0;
+  size_t off_A, off_VA, off_dVA, off_dA, off_lse1, off_D1, off_lse2, off_D2, off_p1, off_p2,
+      off_agg, bytes;
+};
+
+BwdPlan make_bwd_plan(const Dims& D) {
+  BwdPlan P;
+  aggregate_split(D, P.chunk, P.nchunks);
+  const size_t kd = (size_t)D.BH * D.nag * D.d * 4, k1 = (size_t)D.BH * D.nag * 4;
+  const size_t n1 = (size_t)D.BH * D.N * 4, pk = (size_t)D.BH * P.nchunks * D.nag * D.d * 4;
+  const size_t agg = (size_t)D.BH * P.nchunks * D.nag * (D.d + 2) * 4;
+  size_t o = 0;
+  auto take = [&](size_t b) {
+    const size_t at = o;
+    o = align_up(o + b, 256);
+    return at;
+  };
+  P.off_A = take(kd);
+  P.off_VA = take(kd);
+  P.off_dVA = take(kd);
+  P.off_dA = take(kd);
+  P.off_lse1 = take(k1);
+  P.off_D1 = take(k1);
+  P.off_lse2 = take(n1);
+  P.off_D2 = take(n1);
+  P.off_p1 = take(pk);
+  P.off_p2 = take(pk);
+  P.off_agg = take(agg);
+  P.bytes = o;
+  return P;
+}
+
+template <typename T, int MAXD>
+int run_backward_t(const Dims& D, const BwdPlan& P, const void* q, const void* k, const void* v,
+                   const void* dout, const void* agents, void* dq, void* dk, void* dv,
+                   void* dagents, float scale, char* ws, hipStream_t st) {
+  float* A = (float*)(ws + P.off_A);
+  float* VA = (float*)(ws + P.off_VA);
+  float* dVA = (float*)(ws + P.off_dVA);
+  float* dA = (float*)(ws + P.off_dA);
+  float* lse1 = (float*)(ws + P.off_lse1);
+  float* D1 = (float*)(ws + P.off_D1);
+  float* lse2 = (float*)(ws + P.off_lse2);
+  float* D2 = (float*)(ws + P.off_D2);
+  float* p1 = (float*)(ws + P.off_p1);
+  float* p2 = (float*)(ws + P.off_p2);
+  float* agg = (float*)(ws + P.off_agg);
+  const float sl2 = scale * aa::kLog2e;
+  const aa::Strides sx = D.strides();
+  // forward quantities: agents, V_A and the aggregation's log-sum-exp
+  int rc = agents ? launch_widen<T>(D, agents, A, st) : launch_pool<T>(D, q, A, st);
+  if (rc) return rc;
+  rc = launch_aggregate<T>(D, A, k, v, VA, agg, P.chunk, P.nchunks, sl2, st, nullptr, lse1);
+  if (rc) return rc;
+  const int nqblk = (int)((D.N + 255) / 256);
+  const dim3 tok_grid((unsigned)(D.BH * nqblk)), ag_grid((unsigned)(D.BH * P.nchunks));
+  hipLaunchKernelGGL((aa::bwd_token_stats<T, MAXD>), tok_grid, dim3(256), 0, st, (const T*)q,
+                     (const T*)dout, A, VA, lse2, D2, (int)D.N, D.d, D.nag, sl2, nqblk, sx);
+  AA_LAUNCH_CHECK("backward token statistics launch");
+  // broadcast softmax: dV_A and its part of dA
+  hipLaunchKernelGGL((aa::bwd_agent_pass<T, MAXD, true>), ag_grid, dim3(256), 0, st, (const T*)q,
+                     (const T*)dout, A, VA, VA, lse2, D2, nullptr, nullptr, p1, p2, (int)D.N, D.d,
+                     D.nag, sl2, P.chunk, P.nchunks, sx);
+  AA_LAUNCH_CHECK("backward broadcast agent pass launch");
+  const long kd = D.BH * D.nag * D.d;
+  const unsigned sgrid = (unsigned)std::min<long>((kd + 255) / 256, 65536);
+  hipLaunchKernelGGL(aa::bwd_sum_chunks, dim3(sgrid), dim3(256), 0, st, p1, dVA, D.BH, D.nag, D.d,
+                     P.nchunks, 1.0f, 0);
+  hipLaunchKernelGGL(aa::bwd_sum_chunks, dim3(sgrid), dim3(256), 0, st, p2, dA, D.BH, D.nag, D.d,
+                     P.nchunks, scale, 0);
+  AA_LAUNCH_CHECK("backward chunk sum launch");
+  // aggregation softmax: its part of dA (and D1)
+  hipLaunchKernelGGL((aa::bwd_agent_pass<T, MAXD, false>), ag_grid, dim3(256), 0, st, (const T*)k,
+                     (const T*)v, A, dVA, VA, nullptr, nullptr, lse1, D1, nullptr, p2, (int)D.N,
+                     D.d, D.nag, sl2, P.chunk, P.nchunks, sx);
+  AA_LAUNCH_CHECK("backward aggregation agent pass launch");
+  hipLaunchKernelGGL(aa::bwd_sum_chunks, dim3(sgrid), dim3(256), 0, st, p2, dA, D.BH, D.nag, D.d,
+                     P.nchunks, scale, 1);
+  AA_LAUNCH_CHECK("backward chunk sum launch");
+  // token gradients
+  hipLaunchKernelGGL((aa::bwd_token_pass<T, MAXD, false>), tok_grid, dim3(256), 0, st,
+                     (const T*)q, (const T*)dout, A, VA, lse2, D2, nullptr, nullptr,
+                     agents ? nullptr : dA, (T*)dq, (T*)nullptr, (int)D.N, D.d, D.nag, sl2, scale,
+                     nqblk, sx, D.h, D.w, D.s);
+  AA_LAUNCH_CHECK("backward query gradient launch");
+  hipLaunchKernelGGL((aa::bwd_token_pass<T, MAXD, true>), tok_grid, dim3(256), 0, st, (const T*)k,
+                     (const T*)v, A, dVA, nullptr, nullptr, lse1, D1, nullptr, (T*)dk, (T*)dv,
+                     (int)D.N, D.d, D.nag, sl2, scale, nqblk, sx, D.h, D.w, D.s);
+  AA_LAUNCH_CHECK("backward key/value gradient launch");
+  if (agents) {
+    hipLaunchKernelGGL(aa::bwd_store_agents<T>, dim3(sgrid), dim3(256), 0, st, dA, (T*)dagents,
+                       kd);
+    AA_LAUNCH_CHECK("backward agent gradient launch");
+  }
+  return AGENT_ATTN_OK;
+}
+
+template <typename T>
+int run_backward(const Dims& D, const BwdPlan& P, const void* q, const void* k, const void* v,
+                 const void* dout, const void* agents, void* dq, void* dk, void* dv,
+                 void* dagents, float scale, char* ws, hipStream_t st) {
+  if (D.d <= 64)
+    return run_backward_t<T, 64>(D, P, q, k, v, dout, agents, dq, dk, dv, dagents, scale, ws, st);
+  return run_backward_t<T, 128>(D, P, q, k, v, dout, agents, dq, dk, dv, dagents, scale, ws, st);
+}
+
 }  // namespace
 
 extern "C" {
@@ -904,6 +1016,62 @@ int agent_attn_broadcast(const void* q, const float* agents_f32, const float* ag
   mp.agents_f32_in = agents_f32;
   mp.values_f32_in = agent_values_f32;
   return run_mfma_phases(D, mp, mfma_dc(D.d), aa::PH_BCAST, false, st);
+}
+
+size_t agent_attn_backward_workspace_bytes(int B, int H, int h, int w, int d, int s, int dtype) {
+  Dims D;
+  if (check_grid(D, B, H, h, w, d, s, dtype)) return 0;
+  if (D.BH == 0) return 0;
+  return make_bwd_plan(D).bytes;
+}
+
+int agent_attn_backward(const void* q, const void* k, const void* v, const void* dout,
+                        const void* agents, void* dq, void* dk, void* dv, void* dagents, int B,
+                        int H, int h, int w, int d, int s, float scale, int dtype,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  Dims D;
+  int rc = check_grid(D, B, H, h, w, d, s, dtype);
+  if (rc) return rc;
+  rc = check_scale(scale);
+  if (rc) return rc;
+  if (D.BH == 0) return AGENT_ATTN_OK;
+  if (!q || !k || !v || !dout || !dq || !dk || !dv)
+    return fail(AGENT_ATTN_ERR_NULL, "q, k, v, dout, dq, dk and dv must be non-NULL");
+  if (agents && !dagents)
+    return fail(AGENT_ATTN_ERR_NULL, "supplied agents need dagents for their gradient");
+  const void* all[9] = {q, k, v, dout, agents, dq, dk, dv, agents ? dagents : nullptr};
+  for (const void* p : all)
+    if (misaligned(p)) return fail(AGENT_ATTN_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  const size_t tb = (size_t)D.span() * elem_size(dtype);
+  const size_t ab = (size_t)D.BH * D.nag * D.d * elem_size(dtype);
+  const size_t sizes[9] = {tb, tb, tb, tb, ab, tb, tb, tb, ab};
+  for (int o = 5; o < 9; ++o) {   // outputs against inputs and each other
+    if (!all[o]) continue;
+    for (int i = 0; i < 9; ++i)
+      if (i != o && all[i] && ranges_overlap(all[o], sizes[o], all[i], sizes[i]))
+        return fail(AGENT_ATTN_ERR_ALIAS, "a gradient output overlaps another tensor argument");
+  }
+  const BwdPlan P = make_bwd_plan(D);
+  if (!workspace || workspace_bytes < P.bytes)
+    return fail(AGENT_ATTN_ERR_WORKSPACE, "workspace of %zu bytes at %p; %zu bytes needed",
+                workspace_bytes, workspace, P.bytes);
+  if (((uintptr_t)workspace & 255u) != 0)
+    return fail(AGENT_ATTN_ERR_ALIGN, "workspace must be 256-byte aligned");
+  for (int i = 0; i < 9; ++i)
+    if (all[i] && ranges_overlap(workspace, P.bytes, all[i], sizes[i]))
+      return fail(AGENT_ATTN_ERR_ALIAS, "workspace overlaps a tensor argument");
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  switch (dtype) {
+    case AGENT_ATTN_F32:
+      return run_backward<float>(D, P, q, k, v, dout, agents, dq, dk, dv, dagents, scale, ws, st);
+    case AGENT_ATTN_BF16:
+      return run_backward<aa::bf16_t>(D, P, q, k, v, dout, agents, dq, dk, dv, dagents, scale,
+                                      ws, st);
+    default:
+      return run_backward<aa::half_t>(D, P, q, k, v, dout, agents, dq, dk, dv, dagents, scale,
+                                      ws, st);
+  }
 }
 
 long agent_attn_set_wait_limit(long polls) {

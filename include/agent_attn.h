@@ -160,6 +160,34 @@ int agent_attn_forward_module(const void* q, const void* k, const void* v,
                               float scale, int dtype, void* workspace,
                               size_t workspace_bytes, void* stream);
 
+/* Scratch bytes agent_attn_backward needs for these sizes (0 for invalid
+ * sizes or an empty batch). */
+size_t agent_attn_backward_workspace_bytes(int B, int H, int h, int w, int d,
+                                           int s, int dtype);
+
+/* Backward pass of the operator (agent_attn_forward): the gradients of a
+ * loss L through O = softmax(scale Q A^T) softmax(scale A K^T) V, given
+ * dout = dL/dO (source: "Agent Attention: On the Integration of Softmax and
+ * Linear Attention", §4: two Softmax attentions, whose gradients follow
+ * by the chain rule; §6: A = f(Q), the pooling, whose gradient spreads each
+ * agent's gradient evenly over the tokens of its window).
+ *   dq, dk, dv : outputs, [B, H, N, d] of dtype, dense;
+ *   agents     : NULL (pooled from q: dq then includes the pooling's share),
+ *                or the caller's agents [B, H, s*s, d], whose gradient goes
+ *                to dagents [B, H, s*s, d] of dtype (required then, else
+ *                ignored).
+ * The forward is recomputed inside (nothing is saved between the calls);
+ * arithmetic is float32.  workspace: at least
+ * agent_attn_backward_workspace_bytes(...) bytes, 256-byte aligned, contents
+ * free.  Outputs may not overlap any argument, nor the workspace any tensor
+ * (AGENT_ATTN_ERR_ALIAS).  Validation and errors otherwise as
+ * agent_attn_forward_ws; the call allocates nothing. */
+int agent_attn_backward(const void* q, const void* k, const void* v,
+                        const void* dout, const void* agents, void* dq,
+                        void* dk, void* dv, void* dagents, int B, int H, int h,
+                        int w, int d, int s, float scale, int dtype,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
 /* Step 1 alone: agents_f32 [B, H, s*s, d] (float32) = 2-D average pool of q. */
 int agent_attn_pool(const void* q, float* agents_f32, int B, int H, int h,
                     int w, int d, int s, int dtype, void* stream);

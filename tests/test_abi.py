@@ -190,3 +190,28 @@ def test_module_forward_validates_its_parameters(L):
     assert modfwd(L, b1=good, ws=None) == ERR_WS
     # a DWC bias without weights is ignored (no alias check against it)
     assert modfwd(L, wb=ctypes.c_void_p(P[3].value + 64), ws_bytes=10) == ERR_WS
+
+
+# ---------------------------------------------------------------- backward
+
+def bwd(L, *, q=P[0], k=P[1], v=P[2], dout=P[3], agents=None, dq=P[4], dk=P[5], dv=P[6],
+        da=None, B=2, H=3, h=8, w=8, d=64, s=4, scale=0.125, dtype=1, ws=WS, ws_bytes=1 << 40):
+    return L.agent_attn_backward(q, k, v, dout, agents, dq, dk, dv, da, B, H, h, w, d, s, scale,
+                                 dtype, ws, ws_bytes, None)
+
+
+def test_backward_validation(L):
+    assert L.agent_attn_backward_workspace_bytes(2, 3, 8, 8, 64, 4, 1) > 0
+    assert L.agent_attn_backward_workspace_bytes(2, 3, 8, 8, 12, 4, 1) == 0
+    assert bwd(L, dq=None) == ERR_NULL
+    assert bwd(L, agents=P[7]) == ERR_NULL                       # agents without dagents
+    assert bwd(L, dk=ctypes.c_void_p(P[4].value + 64)) == ERR_ALIAS   # dk inside dq
+    assert bwd(L, dv=P[0]) == ERR_ALIAS                          # dv on q
+    assert bwd(L, dq=ctypes.c_void_p(P[4].value + 8)) == ERR_ALIGN
+    assert bwd(L, d=12) == ERR_UNSUP
+    assert bwd(L, scale=0.0) == ERR_SCALE
+    assert bwd(L, dtype=4) == ERR_DTYPE
+    assert bwd(L, ws=None) == ERR_WS
+    assert bwd(L, ws_bytes=16) == ERR_WS
+    assert bwd(L, ws=ctypes.c_void_p(P[3].value)) == ERR_ALIAS
+    assert bwd(L, B=0) == OK
