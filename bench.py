@@ -26,6 +26,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 matrix cores
+FP32_VECTOR_PEAK_TFLOPS = 157.3   # MI355X fp32 vector arithmetic
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "efficient_attention_vision_amd", "csrc")
 FUSED_KERNEL = "agent_mfma_kernel"
@@ -280,6 +281,9 @@ def main():
     ap.add_argument("--module", action="store_true",
                     help="time the full module forward: agent biases in both attentions and "
                          "the depth-wise 3x3 convolution of V (agent_attn_forward_module)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward pass (agent_attn_backward: gradients of q, k, v "
+                         "from the output gradient, forward recomputed inside)")
     ap.add_argument("--dtype", choices=("bf16", "f16"), default=None,
                     help="16-bit element type of the tensors (default: the workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -319,7 +323,7 @@ def main():
     if args.dtype and wl.dtype != "f32":
         import dataclasses
         wl = dataclasses.replace(wl, dtype=args.dtype)
-    if args.module and args.layout != "bhnd":
+    if (args.module or args.backward) and args.layout != "bhnd":
         print("bench.py: --module takes the dense layout only", file=sys.stderr)
         sys.exit(2)
     dev = torch.device("cuda:0")
@@ -351,9 +355,17 @@ def main():
                "dwc_weight": torch.randn((wl.H * wl.d, 3, 3), generator=gen, device=dev) / 3,
                "dwc_bias": 0.5 * torch.randn((wl.H * wl.d,), generator=gen, device=dev)}
 
+    if args.backward:
+        bws = torch.empty(max(1, _binding.agent_attn_backward_workspace_bytes(
+            wl.B, wl.H, wl.h, wl.w, wl.d, wl.s, {"f32": 0, "bf16": 1, "f16": 2}[wl.dtype])),
+            dtype=torch.uint8, device=dev)
+
     def step(i):
         q, k, v, a, o = sets[i % R]
-        if args.module:
+        if args.backward:   # the output buffer of the set serves as dO
+            eav.agent_attn_backward(q, k, v, o, (wl.h, wl.w), wl.s, wl.scale, agents=a,
+                                    workspace=bws)
+        elif args.module:
             eav.agent_attn_forward_module(q, k, v, (wl.h, wl.w), wl.s, wl.scale, agents=a, out=o,
                                           workspace=ws, **mod)
         else:
@@ -408,19 +420,28 @@ def main():
     if args.module:   # + the two biases (read once, shared by the batch), + 9 MACs per output
         abytes += 2 * wl.H * wl.k * wl.N * 4
         aflops += 18 * wl.B * wl.H * wl.N * wl.d
+    if args.backward:  # q, k, v, dO read and dq, dk, dv written; 8 + 16 products of N k d MACs
+        abytes = abytes // 4 * 7
+        aflops = aflops * 3
     achieved_gbs = abytes / (kernel_us * 1e-6) / 1e9
     achieved_tflops = aflops / (kernel_us * 1e-6) / 1e12
     # counters were taken on the plain bf16 dense kernel: other variants report none
-    plain = not args.module and args.layout == "bhnd" and wl.dtype in ("bf16", "f32")
+    plain = (not args.module and not args.backward and args.layout == "bhnd"
+             and wl.dtype in ("bf16", "f32"))
     traffic = measured_traffic(wl.name) if plain else None
-    if wl.k >= 256:
+    if args.backward:   # float32 vector arithmetic (no matrix cores)
+        roof = {"bound": "alu", "achieved": achieved_tflops, "peak": FP32_VECTOR_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved_tflops / FP32_VECTOR_PEAK_TFLOPS,
+                "traffic": traffic}
+    elif wl.k >= 256:
         roof = {"bound": "mfma", "achieved": achieved_tflops, "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": achieved_tflops / BF16_PEAK_TFLOPS, "traffic": traffic}
     else:
         roof = {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": traffic}
     line = {
-        "metric": "agent-attn fwd tokens/s (B*H*N/s) + achieved HBM GB/s at N=3136,k=49 bf16",
+        "metric": ("agent-attn bwd tokens/s (B*H*N/s)" if args.backward else
+                   "agent-attn fwd tokens/s (B*H*N/s) + achieved HBM GB/s at N=3136,k=49 bf16"),
         "value": value,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -437,7 +458,8 @@ def main():
                    "supplied_agents": wl.supplied_agents, "rotating_sets": R,
                    "layout": "[B,N,H,d] storage" if args.layout == "bnhd" else "[B,H,N,d]",
                    **({"module_terms": ["agent biases B1, B2", "depth-wise 3x3 conv of V"]}
-                      if args.module else {})},
+                      if args.module else {}),
+                   **({"pass": "backward (dq, dk, dv)"} if args.backward else {})},
         "roofline": roof,
         "kernel_us_per_launch": kernel_us,
         "eager_launch_us": {"median": pct(0.5), "p10": pct(0.1), "p90": pct(0.9)},

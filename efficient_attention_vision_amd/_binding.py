@@ -143,6 +143,10 @@ def agent_attn_workspace_bytes(B, H, h, w, d, s, dtype_code) -> int:
     return int(lib().agent_attn_workspace_bytes(B, H, h, w, d, s, dtype_code))
 
 
+def agent_attn_backward_workspace_bytes(B, H, h, w, d, s, dtype_code) -> int:
+    return int(lib().agent_attn_backward_workspace_bytes(B, H, h, w, d, s, dtype_code))
+
+
 def _strided_view(t, name):
     """A [B, H, N, d] GPU tensor whose channels are contiguous (any strides
     for the other three dimensions, e.g. a [B, N, H, d] tensor transposed)."""
