@@ -18,6 +18,7 @@
 #include "kernels_mfma.hpp"
 #include "kernels_scalar.hpp"
 #include "kernels_backward.hpp"
+#include "kernels_gemm.hpp"
 
 namespace {
 
@@ -399,7 +400,7 @@ int launch_widen(const Dims& D, const void* src, float* dst, hipStream_t st) {
 template <typename T>
 int launch_aggregate(const Dims& D, const float* A, const void* k, const void* v, float* VA,
                      float* part, int chunk, int nchunks, float sl2, hipStream_t st,
-                     const float* bias1 = nullptr, float* lse = nullptr) {
+                     const float* bias1 = nullptr) {
   const long blocks = D.BH * nchunks;
   if (D.d <= 64)
     hipLaunchKernelGGL((aa::aggregate_partial_scalar<T, 64>), dim3((unsigned)blocks), dim3(256), 0,
@@ -411,7 +412,7 @@ int launch_aggregate(const Dims& D, const float* A, const void* k, const void* v
                        nchunks, D.strides(), bias1);
   AA_LAUNCH_CHECK("agent_aggregate launch");
   hipLaunchKernelGGL(aa::merge_partials_kernel, dim3((unsigned)(D.BH * D.nag)), dim3(128), 0, st,
-                     part, VA, D.d, D.nag, nchunks, lse);
+                     part, VA, D.d, D.nag, nchunks);
   AA_LAUNCH_CHECK("agent_aggregate merge launch");
   return AGENT_ATTN_OK;
 }
@@ -745,20 +746,22 @@ int forward_ws(const void* q, const void* k, const void* v, void* out, const voi
 
 // ------------------------------------------------------------- backward
 // Workspace of the backward pass (float32 regions, 256-byte aligned): A,
-// V_A, dV_A, dA [B*H, k, d]; lse1, D1 [B*H, k]; lse2, D2 [B*H, N]; two
-// per-chunk partial sets [B*H, chunks, k, d]; the aggregation's partials.
+// V_A, dV_A, dA [B*H, k, d]; P2 and dS2 [B*H, N, k]; P1 and dS1 [B*H, k, N];
+// dQ, dK, dV accumulators [B*H, N, d]; the split-K partial sums of the
+// products over the tokens.
+constexpr int kBwdSplit = 256;   // tokens per split of the products over N
+
 struct BwdPlan {
-  int chunk = 0, nchunks = 0;
-  size_t off_A, off_VA, off_dVA, off_dA, off_lse1, off_D1, off_lse2, off_D2, off_p1, off_p2,
-      off_agg, bytes;
+  int splits = 1;
+  size_t off_A, off_VA, off_dVA, off_dA, off_P2, off_dS2, off_P1, off_dS1, off_dQ, off_dK,
+      off_dV, off_part, bytes;
 };
 
 BwdPlan make_bwd_plan(const Dims& D) {
   BwdPlan P;
-  aggregate_split(D, P.chunk, P.nchunks);
-  const size_t kd = (size_t)D.BH * D.nag * D.d * 4, k1 = (size_t)D.BH * D.nag * 4;
-  const size_t n1 = (size_t)D.BH * D.N * 4, pk = (size_t)D.BH * P.nchunks * D.nag * D.d * 4;
-  const size_t agg = (size_t)D.BH * P.nchunks * D.nag * (D.d + 2) * 4;
+  P.splits = (int)((D.N + kBwdSplit - 1) / kBwdSplit);
+  const size_t kd = (size_t)D.BH * D.nag * D.d * 4;
+  const size_t nk = (size_t)D.BH * D.N * D.nag * 4, nd = (size_t)D.BH * D.N * D.d * 4;
   size_t o = 0;
   auto take = [&](size_t b) {
     const size_t at = o;
@@ -769,79 +772,38 @@ BwdPlan make_bwd_plan(const Dims& D) {
   P.off_VA = take(kd);
   P.off_dVA = take(kd);
   P.off_dA = take(kd);
-  P.off_lse1 = take(k1);
-  P.off_D1 = take(k1);
-  P.off_lse2 = take(n1);
-  P.off_D2 = take(n1);
-  P.off_p1 = take(pk);
-  P.off_p2 = take(pk);
-  P.off_agg = take(agg);
+  P.off_P2 = take(nk);
+  P.off_dS2 = take(nk);
+  P.off_P1 = take(nk);
+  P.off_dS1 = take(nk);
+  P.off_dQ = take(nd);
+  P.off_dK = take(nd);
+  P.off_dV = take(nd);
+  P.off_part = take(kd * P.splits);
   P.bytes = o;
   return P;
 }
 
-template <typename T, int MAXD>
-int run_backward_t(const Dims& D, const BwdPlan& P, const void* q, const void* k, const void* v,
-                   const void* dout, const void* agents, void* dq, void* dk, void* dv,
-                   void* dagents, float scale, char* ws, hipStream_t st) {
-  float* A = (float*)(ws + P.off_A);
-  float* VA = (float*)(ws + P.off_VA);
-  float* dVA = (float*)(ws + P.off_dVA);
-  float* dA = (float*)(ws + P.off_dA);
-  float* lse1 = (float*)(ws + P.off_lse1);
-  float* D1 = (float*)(ws + P.off_D1);
-  float* lse2 = (float*)(ws + P.off_lse2);
-  float* D2 = (float*)(ws + P.off_D2);
-  float* p1 = (float*)(ws + P.off_p1);
-  float* p2 = (float*)(ws + P.off_p2);
-  float* agg = (float*)(ws + P.off_agg);
-  const float sl2 = scale * aa::kLog2e;
-  const aa::Strides sx = D.strides();
-  // forward quantities: agents, V_A and the aggregation's log-sum-exp
-  int rc = agents ? launch_widen<T>(D, agents, A, st) : launch_pool<T>(D, q, A, st);
-  if (rc) return rc;
-  rc = launch_aggregate<T>(D, A, k, v, VA, agg, P.chunk, P.nchunks, sl2, st, nullptr, lse1);
-  if (rc) return rc;
-  const int nqblk = (int)((D.N + 255) / 256);
-  const dim3 tok_grid((unsigned)(D.BH * nqblk)), ag_grid((unsigned)(D.BH * P.nchunks));
-  hipLaunchKernelGGL((aa::bwd_token_stats<T, MAXD>), tok_grid, dim3(256), 0, st, (const T*)q,
-                     (const T*)dout, A, VA, lse2, D2, (int)D.N, D.d, D.nag, sl2, nqblk, sx);
-  AA_LAUNCH_CHECK("backward token statistics launch");
-  // broadcast softmax: dV_A and its part of dA
-  hipLaunchKernelGGL((aa::bwd_agent_pass<T, MAXD, true>), ag_grid, dim3(256), 0, st, (const T*)q,
-                     (const T*)dout, A, VA, VA, lse2, D2, nullptr, nullptr, p1, p2, (int)D.N, D.d,
-                     D.nag, sl2, P.chunk, P.nchunks, sx);
-  AA_LAUNCH_CHECK("backward broadcast agent pass launch");
-  const long kd = D.BH * D.nag * D.d;
-  const unsigned sgrid = (unsigned)std::min<long>((kd + 255) / 256, 65536);
-  hipLaunchKernelGGL(aa::bwd_sum_chunks, dim3(sgrid), dim3(256), 0, st, p1, dVA, D.BH, D.nag, D.d,
-                     P.nchunks, 1.0f, 0);
-  hipLaunchKernelGGL(aa::bwd_sum_chunks, dim3(sgrid), dim3(256), 0, st, p2, dA, D.BH, D.nag, D.d,
-                     P.nchunks, scale, 0);
-  AA_LAUNCH_CHECK("backward chunk sum launch");
-  // aggregation softmax: its part of dA (and D1)
-  hipLaunchKernelGGL((aa::bwd_agent_pass<T, MAXD, false>), ag_grid, dim3(256), 0, st, (const T*)k,
-                     (const T*)v, A, dVA, VA, nullptr, nullptr, lse1, D1, nullptr, p2, (int)D.N,
-                     D.d, D.nag, sl2, P.chunk, P.nchunks, sx);
-  AA_LAUNCH_CHECK("backward aggregation agent pass launch");
-  hipLaunchKernelGGL(aa::bwd_sum_chunks, dim3(sgrid), dim3(256), 0, st, p2, dA, D.BH, D.nag, D.d,
-                     P.nchunks, scale, 1);
-  AA_LAUNCH_CHECK("backward chunk sum launch");
-  // token gradients
-  hipLaunchKernelGGL((aa::bwd_token_pass<T, MAXD, false>), tok_grid, dim3(256), 0, st,
-                     (const T*)q, (const T*)dout, A, VA, lse2, D2, nullptr, nullptr,
-                     agents ? nullptr : dA, (T*)dq, (T*)nullptr, (int)D.N, D.d, D.nag, sl2, scale,
-                     nqblk, sx, D.h, D.w, D.s);
-  AA_LAUNCH_CHECK("backward query gradient launch");
-  hipLaunchKernelGGL((aa::bwd_token_pass<T, MAXD, true>), tok_grid, dim3(256), 0, st, (const T*)k,
-                     (const T*)v, A, dVA, nullptr, nullptr, lse1, D1, nullptr, (T*)dk, (T*)dv,
-                     (int)D.N, D.d, D.nag, sl2, scale, nqblk, sx, D.h, D.w, D.s);
-  AA_LAUNCH_CHECK("backward key/value gradient launch");
-  if (agents) {
-    hipLaunchKernelGGL(aa::bwd_store_agents<T>, dim3(sgrid), dim3(256), 0, st, dA, (T*)dagents,
-                       kd);
-    AA_LAUNCH_CHECK("backward agent gradient launch");
-  }
+// part = alpha * A B for every head (M x N results, contraction K), split
+// over K in chunks of kchunk (splits = ceil(K / kchunk)).
+template <typename TA, typename TB>
+int launch_bgemm(const aa::MatRef& A, const aa::MatRef& B, float* part, int M, int N, int K,
+                 int kchunk, long batch, float alpha, hipStream_t st) {
+  const int splits = (K + kchunk - 1) / kchunk;
+  const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 63) / 64),
+                  (unsigned)(batch * splits));
+  hipLaunchKernelGGL((aa::bgemm_f32<TA, TB>), grid, dim3(256), 0, st, A, B, part, M, N, K, kchunk,
+                     splits, batch, alpha);
+  AA_LAUNCH_CHECK("backward product launch");
+  return AGENT_ATTN_OK;
+}
+
+int launch_sum_splits(const float* part, float* out, long n, int splits, float factor,
+                      int accumulate, hipStream_t st) {
+  const unsigned grid = (unsigned)std::min<long>((n + 255) / 256, 65536);
+  hipLaunchKernelGGL(aa::sum_splits, dim3(grid), dim3(256), 0, st, part, out, n, splits, factor,
+                     accumulate);
+  AA_LAUNCH_CHECK("backward split sum launch");
   return AGENT_ATTN_OK;
 }
 
@@ -849,9 +811,95 @@ template <typename T>
 int run_backward(const Dims& D, const BwdPlan& P, const void* q, const void* k, const void* v,
                  const void* dout, const void* agents, void* dq, void* dk, void* dv,
                  void* dagents, float scale, char* ws, hipStream_t st) {
-  if (D.d <= 64)
-    return run_backward_t<T, 64>(D, P, q, k, v, dout, agents, dq, dk, dv, dagents, scale, ws, st);
-  return run_backward_t<T, 128>(D, P, q, k, v, dout, agents, dq, dk, dv, dagents, scale, ws, st);
+  float* A = (float*)(ws + P.off_A);
+  float* VA = (float*)(ws + P.off_VA);
+  float* dVA = (float*)(ws + P.off_dVA);
+  float* dA = (float*)(ws + P.off_dA);
+  float* P2 = (float*)(ws + P.off_P2);
+  float* dS2 = (float*)(ws + P.off_dS2);
+  float* P1 = (float*)(ws + P.off_P1);
+  float* dS1 = (float*)(ws + P.off_dS1);
+  float* dQ = (float*)(ws + P.off_dQ);
+  float* dK = (float*)(ws + P.off_dK);
+  float* dV = (float*)(ws + P.off_dV);
+  float* part = (float*)(ws + P.off_part);
+  const float sl2 = scale * aa::kLog2e;
+  const long BH = D.BH, N = D.N, kk = D.nag, d = D.d;
+  // operands: [N, d] of type T, and float32 [k, d], [N, k], [k, N] per head
+  const aa::MatRef Qm{q, N * d, d, 1}, Km{k, N * d, d, 1}, Vm{v, N * d, d, 1},
+      dOm{dout, N * d, d, 1};
+  const aa::MatRef KmT{k, N * d, 1, d}, VmT{v, N * d, 1, d};
+  const aa::MatRef Am{A, kk * d, d, 1}, AmT{A, kk * d, 1, d}, VAmT{VA, kk * d, 1, d},
+      dVAm{dVA, kk * d, d, 1};
+  const aa::MatRef P2T{P2, N * kk, 1, kk}, dS2m{dS2, N * kk, kk, 1}, dS2T{dS2, N * kk, 1, kk};
+  const aa::MatRef dS1m{dS1, kk * N, N, 1}, dS1T{dS1, kk * N, 1, N}, P1m{P1, kk * N, N, 1},
+      P1T{P1, kk * N, 1, N};
+  const int KN = kBwdSplit, KALL = 1 << 30;   // split over tokens / no split
+  const long nkd = BH * kk * d;
+  // forward quantities: agents; P1 = softmax(scale A K^T); V_A = P1 V
+  int rc = agents ? launch_widen<T>(D, agents, A, st) : launch_pool<T>(D, q, A, st);
+  if (rc) return rc;
+  if ((rc = launch_bgemm<float, T>(Am, KmT, P1, (int)kk, (int)N, (int)d, KALL, BH, 1.f, st)))
+    return rc;
+  hipLaunchKernelGGL(aa::row_softmax_log2, dim3((unsigned)(BH * kk)), dim3(256), 0, st, P1,
+                     (int)N, sl2);
+  AA_LAUNCH_CHECK("backward aggregation probabilities launch");
+  if ((rc = launch_bgemm<float, T>(P1m, Vm, part, (int)kk, (int)d, (int)N, KN, BH, 1.f, st)))
+    return rc;
+  if ((rc = launch_sum_splits(part, VA, nkd, P.splits, 1.f, 0, st))) return rc;
+  // P2 = softmax(scale Q A^T)
+  if ((rc = launch_bgemm<T, float>(Qm, AmT, P2, (int)N, (int)kk, (int)d, KALL, BH, 1.f, st)))
+    return rc;
+  hipLaunchKernelGGL(aa::row_softmax_log2, dim3((unsigned)(BH * N)), dim3(256), 0, st, P2,
+                     (int)kk, sl2);
+  AA_LAUNCH_CHECK("backward broadcast probabilities launch");
+  // dV_A = P2^T dO
+  if ((rc = launch_bgemm<float, T>(P2T, dOm, part, (int)kk, (int)d, (int)N, KN, BH, 1.f, st)))
+    return rc;
+  if ((rc = launch_sum_splits(part, dVA, nkd, P.splits, 1.f, 0, st))) return rc;
+  // dS2 = P2 (dO V_A^T - rowsum)
+  if ((rc = launch_bgemm<T, float>(dOm, VAmT, dS2, (int)N, (int)kk, (int)d, KALL, BH, 1.f, st)))
+    return rc;
+  hipLaunchKernelGGL(aa::softmax_grad_rows, dim3((unsigned)(BH * N)), dim3(256), 0, st, P2, dS2,
+                     (int)kk);
+  AA_LAUNCH_CHECK("backward broadcast softmax gradient launch");
+  // dQ = scale dS2 A;  dA = scale dS2^T Q
+  if ((rc = launch_bgemm<float, float>(dS2m, Am, dQ, (int)N, (int)d, (int)kk, KALL, BH, scale,
+                                       st)))
+    return rc;
+  if ((rc = launch_bgemm<float, T>(dS2T, Qm, part, (int)kk, (int)d, (int)N, KN, BH, 1.f, st)))
+    return rc;
+  if ((rc = launch_sum_splits(part, dA, nkd, P.splits, scale, 0, st))) return rc;
+  // dS1 = P1 (dV_A V^T - rowsum)
+  if ((rc = launch_bgemm<float, T>(dVAm, VmT, dS1, (int)kk, (int)N, (int)d, KALL, BH, 1.f, st)))
+    return rc;
+  hipLaunchKernelGGL(aa::softmax_grad_rows, dim3((unsigned)(BH * kk)), dim3(256), 0, st, P1, dS1,
+                     (int)N);
+  AA_LAUNCH_CHECK("backward aggregation softmax gradient launch");
+  // dA += scale dS1 K;  dK = scale dS1^T A;  dV = P1^T dV_A
+  if ((rc = launch_bgemm<float, T>(dS1m, Km, part, (int)kk, (int)d, (int)N, KN, BH, 1.f, st)))
+    return rc;
+  if ((rc = launch_sum_splits(part, dA, nkd, P.splits, scale, 1, st))) return rc;
+  if ((rc = launch_bgemm<float, float>(dS1T, Am, dK, (int)N, (int)d, (int)kk, KALL, BH, scale,
+                                       st)))
+    return rc;
+  if ((rc = launch_bgemm<float, float>(P1T, dVAm, dV, (int)N, (int)d, (int)kk, KALL, BH, 1.f,
+                                       st)))
+    return rc;
+  // outputs in the tensors' type; dq with the pooling's share of dA
+  const long nnd = BH * N * d;
+  const unsigned g_nd = (unsigned)std::min<long>((nnd + 255) / 256, 65536);
+  hipLaunchKernelGGL(aa::finish_dq<T>, dim3(g_nd), dim3(256), 0, st, dQ, agents ? nullptr : dA,
+                     (T*)dq, BH, (int)N, (int)d, (int)kk, D.h, D.w, D.s);
+  hipLaunchKernelGGL(aa::store_as<T>, dim3(g_nd), dim3(256), 0, st, dK, (T*)dk, nnd);
+  hipLaunchKernelGGL(aa::store_as<T>, dim3(g_nd), dim3(256), 0, st, dV, (T*)dv, nnd);
+  AA_LAUNCH_CHECK("backward output launch");
+  if (agents) {
+    const unsigned g_kd = (unsigned)std::min<long>((nkd + 255) / 256, 65536);
+    hipLaunchKernelGGL(aa::store_as<T>, dim3(g_kd), dim3(256), 0, st, dA, (T*)dagents, nkd);
+    AA_LAUNCH_CHECK("backward agent gradient launch");
+  }
+  return AGENT_ATTN_OK;
 }
 
 }  // namespace
@@ -1052,6 +1100,10 @@ int agent_attn_backward(const void* q, const void* k, const void* v, const void*
         return fail(AGENT_ATTN_ERR_ALIAS, "a gradient output overlaps another tensor argument");
   }
   const BwdPlan P = make_bwd_plan(D);
+  if (D.BH * P.splits > 65535)   // grid z of the products over the tokens
+    return fail(AGENT_ATTN_ERR_UNSUPPORTED,
+                "the backward pass takes B*H*ceil(N/%d) <= 65535 (here %ld)", kBwdSplit,
+                D.BH * P.splits);
   if (!workspace || workspace_bytes < P.bytes)
     return fail(AGENT_ATTN_ERR_WORKSPACE, "workspace of %zu bytes at %p; %zu bytes needed",
                 workspace_bytes, workspace, P.bytes);

@@ -149,7 +149,7 @@ aggregate_partial_scalar(const float* __restrict__ A, const T* __restrict__ K,
 // with M = max_j m_j.  Block = (bh, agent), threads over channels.
 __global__ void __launch_bounds__(128)
 merge_partials_kernel(const float* __restrict__ part, float* __restrict__ VA, int d, int nag,
-                      int nchunks, float* __restrict__ lse = nullptr) {
+                      int nchunks) {
   const int agent = blockIdx.x % nag;
   const long bh = blockIdx.x / nag;
   const long stride = (long)nag * (d + 2);
@@ -159,8 +159,6 @@ merge_partials_kernel(const float* __restrict__ part, float* __restrict__ VA, in
   float L = 0.f;
   for (int j = 0; j < nchunks; ++j) L += p0[j * stride + 1] * fast_exp2(p0[j * stride] - M);
   const float inv = 1.0f / L;
-  // log2 of the softmax denominator in the scores' log2 units (backward)
-  if (lse && threadIdx.x == 0) lse[bh * nag + agent] = M + __log2f(L);
   for (int c = threadIdx.x; c < d; c += blockDim.x) {
     float acc = 0.f;
     for (int j = 0; j < nchunks; ++j)
