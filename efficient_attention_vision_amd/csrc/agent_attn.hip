@@ -850,8 +850,8 @@ int run_backward(const Dims& D, const BwdPlan& P, const void* q, const void* k, 
   // P2 = softmax(scale Q A^T)
   if ((rc = launch_bgemm<T, float>(Qm, AmT, P2, (int)N, (int)kk, (int)d, KALL, BH, 1.f, st)))
     return rc;
-  hipLaunchKernelGGL(aa::row_softmax_log2, dim3((unsigned)(BH * N)), dim3(256), 0, st, P2,
-                     (int)kk, sl2);
+  hipLaunchKernelGGL(aa::softmax_short, dim3((unsigned)((BH * N + 3) / 4)), dim3(256), 0, st, P2,
+                     BH * N, (int)kk, sl2);
   AA_LAUNCH_CHECK("backward broadcast probabilities launch");
   // dV_A = P2^T dO
   if ((rc = launch_bgemm<float, T>(P2T, dOm, part, (int)kk, (int)d, (int)N, KN, BH, 1.f, st)))
@@ -860,8 +860,8 @@ int run_backward(const Dims& D, const BwdPlan& P, const void* q, const void* k, 
   // dS2 = P2 (dO V_A^T - rowsum)
   if ((rc = launch_bgemm<T, float>(dOm, VAmT, dS2, (int)N, (int)kk, (int)d, KALL, BH, 1.f, st)))
     return rc;
-  hipLaunchKernelGGL(aa::softmax_grad_rows, dim3((unsigned)(BH * N)), dim3(256), 0, st, P2, dS2,
-                     (int)kk);
+  hipLaunchKernelGGL(aa::softmax_grad_short, dim3((unsigned)((BH * N + 3) / 4)), dim3(256), 0, st,
+                     P2, dS2, BH * N, (int)kk);
   AA_LAUNCH_CHECK("backward broadcast softmax gradient launch");
   // dQ = scale dS2 A;  dA = scale dS2^T Q
   if ((rc = launch_bgemm<float, float>(dS2m, Am, dQ, (int)N, (int)d, (int)kk, KALL, BH, scale,

@@ -125,6 +125,69 @@ row_softmax_log2(float* __restrict__ S, int L, float sl2) {
   for (int i = threadIdx.x; i < L; i += 256) row[i] = fast_exp2(row[i] * sl2 - m) * inv;
 }
 
+// Wave-wide sum and max (64 lanes).
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
+// Short rows (L <= 256, the agents of a token): one wave per row, four rows
+// per block.  softmax_short: row = softmax(sl2 * row) in place;
+// softmax_grad_short: dP <- P * (dP - sum(P * dP)) in place.
+__global__ void __launch_bounds__(256)
+softmax_short(float* __restrict__ S, long rows, int L, float sl2) {
+  const long r = blockIdx.x * 4L + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const int lane = threadIdx.x & 63;
+  float* row = S + r * L;
+  float x[4];
+  float m = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int i = lane + 64 * e;
+    x[e] = i < L ? row[i] * sl2 : -INFINITY;
+    m = fmaxf(m, x[e]);
+  }
+  m = wave_max(m);
+  float l = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x[e] = lane + 64 * e < L ? fast_exp2(x[e] - m) : 0.f;
+    l += x[e];
+  }
+  const float inv = 1.0f / wave_sum(l);
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if (lane + 64 * e < L) row[lane + 64 * e] = x[e] * inv;
+}
+
+__global__ void __launch_bounds__(256)
+softmax_grad_short(const float* __restrict__ P, float* __restrict__ dP, long rows, int L) {
+  const long r = blockIdx.x * 4L + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const int lane = threadIdx.x & 63;
+  const float* p = P + r * L;
+  float* g = dP + r * L;
+  float pv[4], gv[4], s = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int i = lane + 64 * e;
+    pv[e] = i < L ? p[i] : 0.f;
+    gv[e] = i < L ? g[i] : 0.f;
+    s = fmaf(pv[e], gv[e], s);
+  }
+  const float D = wave_sum(s);
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if (lane + 64 * e < L) g[lane + 64 * e] = pv[e] * (gv[e] - D);
+}
+
 // In place, one block per row of length L: dP <- P * (dP - sum(P * dP)), the
 // gradient of a row softmax with respect to its (scaled) logits.
 __global__ void __launch_bounds__(256)
