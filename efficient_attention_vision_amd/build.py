@@ -12,8 +12,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libagent_attn.so")
-SOURCES = ["agent_attn.hip"] + [f"mfma_dc{dc}_{t}.hip" for dc in (1, 2, 4)
-                               for t in ("bf16", "f16")]
+SOURCES = (["agent_attn.hip"] + [f"mfma_dc{dc}_{t}.hip" for dc in (1, 2, 4)
+                                for t in ("bf16", "f16")]
+           + [f"bwd_mfma_{t}.hip" for t in ("bf16", "f16")])
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 COMPILE_FLAGS = [

@@ -19,6 +19,7 @@
 #include "kernels_scalar.hpp"
 #include "kernels_backward.hpp"
 #include "kernels_gemm.hpp"
+#include "kernels_bwd_mfma.hpp"
 
 namespace {
 
@@ -902,6 +903,89 @@ int run_backward(const Dims& D, const BwdPlan& P, const void* q, const void* k, 
   return AGENT_ATTN_OK;
 }
 
+// Matrix-core backward (16-bit tensors, up to 64 agents): token-tiled
+// passes with the k x d operands in LDS (kernels_bwd_mfma.hpp).
+struct MfmaBwdPlan {
+  bool use = false;
+  int KT = 0, DT = 0;
+  aa::bw::Pass pp[3];   // stats, bcast, agg
+  size_t off_A = 0, off_VA = 0, off_dVA = 0, off_dA = 0, off_lse = 0, off_D1 = 0, off_dQ = 0,
+         off_part = 0, bytes = 0;
+};
+
+// About two workgroups per CU over the batch, in whole steps of `step` tokens.
+aa::bw::Pass bwd_pass(const Dims& D, int cus, int step) {
+  const long per_head = std::max<long>(1, 2L * cus / D.BH);
+  long T = (D.N + per_head - 1) / per_head;
+  T = (T + step - 1) / step * step;
+  return aa::bw::Pass{(int)((D.N + T - 1) / T), (int)T};
+}
+
+MfmaBwdPlan make_mfma_bwd_plan(const Dims& D, int cus) {
+  MfmaBwdPlan P;
+  if (D.dtype == AGENT_ATTN_F32 || D.nag > 64 || D.d > 128) return P;
+  if (D.BH * D.N * D.d >= (1L << 31)) return P;   // 32-bit element indices
+  P.KT = D.nag <= 32 ? 2 : 4;
+  P.DT = D.d <= 32 ? 1 : D.d <= 64 ? 2 : 4;
+  P.pp[0] = bwd_pass(D, cus, aa::bw::kStatTok);
+  P.pp[1] = P.pp[2] = bwd_pass(D, cus, aa::bw::kStep);
+  const size_t kd = (size_t)D.BH * D.nag * D.d * 4, kp = (size_t)D.BH * 16 * P.KT * 4;
+  const size_t nd = (size_t)D.BH * D.N * D.d * 4;
+  size_t o = 0;
+  auto take = [&](size_t b) {
+    const size_t at = o;
+    o = align_up(o + b, 256);
+    return at;
+  };
+  P.off_A = take(kd);
+  P.off_VA = take(kd);
+  P.off_dVA = take(kd);
+  P.off_dA = take(kd);
+  P.off_lse = take(kp);
+  P.off_D1 = take(kp);
+  P.off_dQ = take(nd);
+  P.off_part = take((size_t)aa::bw::part_floats(P.KT, P.DT, D.BH, P.pp) * 4);
+  P.bytes = o;
+  P.use = true;
+  return P;
+}
+
+template <class El>
+int run_backward_mfma(const Dims& D, const MfmaBwdPlan& P, const void* q, const void* k,
+                      const void* v, const void* dout, const void* agents, void* dq, void* dk,
+                      void* dv, void* dagents, float scale, char* ws, hipStream_t st) {
+  aa::bw::BwdParams p{};
+  p.q = (const uint16_t*)q;
+  p.k = (const uint16_t*)k;
+  p.v = (const uint16_t*)v;
+  p.dout = (const uint16_t*)dout;
+  p.dk = (uint16_t*)dk;
+  p.dv = (uint16_t*)dv;
+  p.A = (float*)(ws + P.off_A);
+  p.VA = (float*)(ws + P.off_VA);
+  p.lse = (float*)(ws + P.off_lse);
+  p.dVA = (float*)(ws + P.off_dVA);
+  p.dA = (float*)(ws + P.off_dA);
+  p.D1 = (float*)(ws + P.off_D1);
+  p.dQ = (float*)(ws + P.off_dQ);
+  p.part = (float*)(ws + P.off_part);
+  p.agents_in = (const uint16_t*)agents;
+  p.dq = (uint16_t*)dq;
+  p.dagents = (uint16_t*)dagents;
+  p.BH = (int)D.BH;
+  p.N = (int)D.N;
+  p.d = D.d;
+  p.nag = D.nag;
+  p.h = D.h;
+  p.w = D.w;
+  p.s = D.s;
+  p.sl2 = scale * aa::kLog2e;
+  p.scale = scale;
+  const int e = aa::bw::run_backward_mfma<El>(p, P.KT, P.DT, P.pp, st);
+  if (e) return hip_fail((hipError_t)e, "backward matrix-core launch");
+  return AGENT_ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1070,7 +1154,8 @@ size_t agent_attn_backward_workspace_bytes(int B, int H, int h, int w, int d, in
   Dims D;
   if (check_grid(D, B, H, h, w, d, s, dtype)) return 0;
   if (D.BH == 0) return 0;
-  return make_bwd_plan(D).bytes;
+  const MfmaBwdPlan M = make_mfma_bwd_plan(D, device_cus());
+  return M.use ? M.bytes : make_bwd_plan(D).bytes;
 }
 
 int agent_attn_backward(const void* q, const void* k, const void* v, const void* dout,
@@ -1098,6 +1183,23 @@ int agent_attn_backward(const void* q, const void* k, const void* v, const void*
     for (int i = 0; i < 9; ++i)
       if (i != o && all[i] && ranges_overlap(all[o], sizes[o], all[i], sizes[i]))
         return fail(AGENT_ATTN_ERR_ALIAS, "a gradient output overlaps another tensor argument");
+  }
+  const MfmaBwdPlan M = make_mfma_bwd_plan(D, device_cus());
+  if (M.use) {
+    if (!workspace || workspace_bytes < M.bytes)
+      return fail(AGENT_ATTN_ERR_WORKSPACE, "workspace of %zu bytes at %p; %zu bytes needed",
+                  workspace_bytes, workspace, M.bytes);
+    if (((uintptr_t)workspace & 255u) != 0)
+      return fail(AGENT_ATTN_ERR_ALIGN, "workspace must be 256-byte aligned");
+    for (int i = 0; i < 9; ++i)
+      if (all[i] && ranges_overlap(workspace, M.bytes, all[i], sizes[i]))
+        return fail(AGENT_ATTN_ERR_ALIAS, "workspace overlaps a tensor argument");
+    hipStream_t st = (hipStream_t)stream;
+    if (dtype == AGENT_ATTN_BF16)
+      return run_backward_mfma<aa::ElemBF16>(D, M, q, k, v, dout, agents, dq, dk, dv,
+                                                         dagents, scale, (char*)workspace, st);
+    return run_backward_mfma<aa::ElemF16>(D, M, q, k, v, dout, agents, dq, dk, dv,
+                                                      dagents, scale, (char*)workspace, st);
   }
   const BwdPlan P = make_bwd_plan(D);
   if (D.BH * P.splits > 65535)   // grid z of the products over the tokens
