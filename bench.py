@@ -429,7 +429,13 @@ def main():
     plain = (not args.module and not args.backward and args.layout == "bhnd"
              and wl.dtype in ("bf16", "f32"))
     traffic = measured_traffic(wl.name) if plain else None
-    if args.backward:   # float32 vector arithmetic (no matrix cores)
+    # 16-bit tensors with up to 64 agents: token-tiled matrix-core passes,
+    # HBM-bound (about 1.7 k flop per byte); otherwise float32 products
+    mfma_bwd = args.backward and wl.dtype != "f32" and wl.k <= 64
+    if mfma_bwd:
+        roof = {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": traffic}
+    elif args.backward:   # float32 vector arithmetic (no matrix cores)
         roof = {"bound": "alu", "achieved": achieved_tflops, "peak": FP32_VECTOR_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": achieved_tflops / FP32_VECTOR_PEAK_TFLOPS,
                 "traffic": traffic}
@@ -459,7 +465,9 @@ def main():
                    "layout": "[B,N,H,d] storage" if args.layout == "bnhd" else "[B,H,N,d]",
                    **({"module_terms": ["agent biases B1, B2", "depth-wise 3x3 conv of V"]}
                       if args.module else {}),
-                   **({"pass": "backward (dq, dk, dv)"} if args.backward else {})},
+                   **({"pass": "backward (dq, dk, dv)",
+                       "backward_path": ("matrix-core token passes" if mfma_bwd
+                                         else "float32 products")} if args.backward else {})},
         "roofline": roof,
         "kernel_us_per_launch": kernel_us,
         "eager_launch_us": {"median": pct(0.5), "p10": pct(0.1), "p90": pct(0.9)},

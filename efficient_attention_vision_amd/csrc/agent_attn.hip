@@ -913,9 +913,16 @@ struct MfmaBwdPlan {
          off_part = 0, bytes = 0;
 };
 
-// About two workgroups per CU over the batch, in whole steps of `step` tokens.
-aa::bw::Pass bwd_pass(const Dims& D, int cus, int step) {
-  const long per_head = std::max<long>(1, 2L * cus / D.BH);
+// Workgroups per CU that the token-tiled passes aim for over the batch
+// (stats, and bcast / agg), in whole steps of tokens.
+#ifndef AA_BWD_STATS_WPC
+#define AA_BWD_STATS_WPC 2
+#endif
+#ifndef AA_BWD_TILE_WPC
+#define AA_BWD_TILE_WPC 2
+#endif
+aa::bw::Pass bwd_pass(const Dims& D, int cus, int step, int per_cu) {
+  const long per_head = std::max<long>(1, (long)per_cu * cus / D.BH);
   long T = (D.N + per_head - 1) / per_head;
   T = (T + step - 1) / step * step;
   return aa::bw::Pass{(int)((D.N + T - 1) / T), (int)T};
@@ -925,10 +932,11 @@ MfmaBwdPlan make_mfma_bwd_plan(const Dims& D, int cus) {
   MfmaBwdPlan P;
   if (D.dtype == AGENT_ATTN_F32 || D.nag > 64 || D.d > 128) return P;
   if (D.BH * D.N * D.d >= (1L << 31)) return P;   // 32-bit element indices
+  if (D.BH > 65535 || D.BH * D.nag * D.d * 8 >= (1L << 31)) return P;   // grid shapes
   P.KT = D.nag <= 32 ? 2 : 4;
   P.DT = D.d <= 32 ? 1 : D.d <= 64 ? 2 : 4;
-  P.pp[0] = bwd_pass(D, cus, aa::bw::kStatTok);
-  P.pp[1] = P.pp[2] = bwd_pass(D, cus, aa::bw::kStep);
+  P.pp[0] = bwd_pass(D, cus, aa::bw::kStatTok, AA_BWD_STATS_WPC);
+  P.pp[1] = P.pp[2] = bwd_pass(D, cus, aa::bw::kStep, AA_BWD_TILE_WPC);
   const size_t kd = (size_t)D.BH * D.nag * D.d * 4, kp = (size_t)D.BH * 16 * P.KT * 4;
   const size_t nd = (size_t)D.BH * D.N * D.d * 4;
   size_t o = 0;
@@ -981,6 +989,9 @@ int run_backward_mfma(const Dims& D, const MfmaBwdPlan& P, const void* q, const 
   p.s = D.s;
   p.sl2 = scale * aa::kLog2e;
   p.scale = scale;
+#ifdef AGENT_ATTN_PHASE_TRACE
+  p.trace = g_trace;
+#endif
   const int e = aa::bw::run_backward_mfma<El>(p, P.KT, P.DT, P.pp, st);
   if (e) return hip_fail((hipError_t)e, "backward matrix-core launch");
   return AGENT_ATTN_OK;

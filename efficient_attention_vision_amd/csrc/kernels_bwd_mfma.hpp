@@ -115,7 +115,23 @@ struct BwdParams {
   int h, w, s;            // token grid and agent grid side
   int P, T;               // workgroups per head and tokens per workgroup of the pass
   float sl2, scale;       // scale * log2(e), scale
+  long long* trace;       // phase timestamps (trace builds only)
 };
+
+// Phase timestamps for profiling builds (-DAGENT_ATTN_PHASE_TRACE): 16
+// wall-clock stamps per workgroup of each token-tiled pass (region 0 stats,
+// 1 bcast, 2 agg; 4096 workgroups each).  Compiled out otherwise.
+#ifdef AGENT_ATTN_PHASE_TRACE
+#define BW_STAMP(region, i)                                                                  \
+  do {                                                                                       \
+    if (p.trace && threadIdx.x == 0 && blockIdx.x < 4096)                                    \
+      p.trace[((long)(region) * 4096 + blockIdx.x) * 16 + (i)] = (long long)wall_clock64();  \
+  } while (0)
+#else
+#define BW_STAMP(region, i) \
+  do {                      \
+  } while (0)
+#endif
 
 // ------------------------------------------------------------------ helpers
 __device__ __forceinline__ bf16x8 as_frag(uint4 x) { return __builtin_bit_cast(bf16x8, x); }
@@ -267,6 +283,7 @@ __global__ void __launch_bounds__(kThr) bwd_stats_kernel(BwdParams p) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
   const int t0 = slot * p.T, t1 = min(p.N, t0 + p.T);
   const long hd = (long)head * p.N * p.d;
+  BW_STAMP(0, 0);
   uint16_t* sAh = (uint16_t*)smem;
   uint16_t* sAl = sAh + C::KP * C::RS;
   uint16_t* sVT = sAl + C::KP * C::RS + wave * C::DP * kVS;
@@ -280,9 +297,11 @@ __global__ void __launch_bounds__(kThr) bwd_stats_kernel(BwdParams p) {
     load_frags<DT>(kf[h], rk, tok, tok < t1, p.d, g);
     load_frags<DT>(vf[h], rv, tok, tok < t1, p.d, g);
   }
+  BW_STAMP(0, 1);
   stage_kd<El, C::KP, C::DP, C::RS, C::TS>(sAh, sAl, nullptr, nullptr,
                                            p.A + (long)head * p.nag * p.d, p.nag, p.d, tid);
   __syncthreads();
+  BW_STAMP(0, 2);
   float m[KT], ls[KT];
   f32x4 U[KT][C::DB];
 #pragma unroll
@@ -341,6 +360,7 @@ __global__ void __launch_bounds__(kThr) bwd_stats_kernel(BwdParams p) {
       for (int db = 0; db < C::DB; ++db) U[kb][db] *= f;
       split8<El>(pv[0], pv[1], pbh[kb], pbl[kb]);
     }
+    BW_STAMP(0, 3);
     // the next step's rows
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -364,7 +384,9 @@ __global__ void __launch_bounds__(kThr) bwd_stats_kernel(BwdParams p) {
   // combine the four waves: common max, then sums of the rescaled partials
 #pragma unroll
   for (int kb = 0; kb < KT; ++kb) ls[kb] = group4_sum(ls[kb]);
+  BW_STAMP(0, 4);
   __syncthreads();   // the agents and the V^T rows are dead from here
+  BW_STAMP(0, 5);
   float* sU = (float*)smem;                       // [2][KP][DP]
   float* sM = sU + 2 * C::KP * C::DP;             // [kNW][KP]
   float* sL = sM + kNW * C::KP;                   // [kNW][KP]
@@ -416,7 +438,22 @@ __global__ void __launch_bounds__(kThr) bwd_stats_kernel(BwdParams p) {
       for (int db = 0; db < C::DB; ++db) *uaddr(1, kb, db) = U[kb][db];
   }
   __syncthreads();
-  if (wave == 0) {
+  BW_STAMP(0, 6);
+  if (wave == 0 && p.P == 1) {
+    // the workgroup holds the whole head: lse and V_A directly
+#pragma unroll
+    for (int kb = 0; kb < KT; ++kb) {
+      const int a = 16 * kb + r;
+      if (a >= p.nag) continue;
+      if (g == 0) p.lse[(long)head * C::KP + a] = Mt[kb] + log2f(Lt[kb]);
+      const float inv = 1.0f / Lt[kb];
+      float* va = p.VA + ((long)head * p.nag + a) * p.d;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+        if (16 * db + 4 * g < p.d)
+          *reinterpret_cast<f32x4*>(va + 16 * db + 4 * g) = (U[kb][db] + *uaddr(1, kb, db)) * inv;
+    }
+  } else if (wave == 0) {
     float* base = p.part + ((long)head * p.P + slot) * C::PART_STATS;
 #pragma unroll
     for (int kb = 0; kb < KT; ++kb) {
@@ -432,6 +469,7 @@ __global__ void __launch_bounds__(kThr) bwd_stats_kernel(BwdParams p) {
       }
     }
   }
+  BW_STAMP(0, 7);
 }
 
 // Reductions over the workgroup partials of a head: one 256-thread block per
@@ -453,13 +491,29 @@ __device__ __forceinline__ void block4_add(float& x0, float& x1, int wave, int l
   }
 }
 
+// Block -> (head, agent) of a reduction: WPA = 4 waves per agent (one agent
+// per block, many partials), or WPA = 1 (four agents per block, few
+// partials).  `wave` is the wave's index within its agent.
+template <int WPA>
+__device__ __forceinline__ bool red_item(const BwdParams& p, int& head, int& a, int& wave,
+                                         int& lane) {
+  const int w = threadIdx.x >> 6;
+  lane = threadIdx.x & 63;
+  const int item = WPA > 1 ? blockIdx.x : blockIdx.x * kNW + w;
+  wave = WPA > 1 ? w : 0;
+  if (item >= p.BH * p.nag) return false;
+  head = item / p.nag;
+  a = item - head * p.nag;
+  return true;
+}
+
 // lse[a] = M + log2(L) and V_A[a] = sum_j 2^(m_j - M) U_j[a] / L over the
 // head's stats partials (M = max_j m_j, L = sum_j 2^(m_j - M) l_j).
-template <int KT, int DT>
+template <int KT, int DT, int WPA>
 __global__ void __launch_bounds__(256) bwd_stats_merge(BwdParams p) {
   using C = Geo<KT, DT>;
-  const int head = blockIdx.x / p.nag, a = blockIdx.x - head * p.nag;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  int head, a, wave, lane;
+  if (!red_item<WPA>(p, head, a, wave, lane)) return;
   const float* base = p.part + (long)head * p.P * C::PART_STATS;
   float M = kNegBig;
   for (int j = lane; j < p.P; j += 64) M = fmaxf(M, base[j * C::PART_STATS + a]);
@@ -470,11 +524,11 @@ __global__ void __launch_bounds__(256) bwd_stats_merge(BwdParams p) {
   L = wsum(L);
   const int c1 = C::DP > 64 ? lane + 64 : lane;   // second channel (DP = 128 only)
   float u0 = 0.f, u1 = 0.f;
-  for (int j0 = wave; j0 < p.P; j0 += kNW * kRedBatch) {
+  for (int j0 = wave; j0 < p.P; j0 += WPA * kRedBatch) {
     float w[kRedBatch], x0[kRedBatch], x1[kRedBatch];
 #pragma unroll
     for (int e = 0; e < kRedBatch; ++e) {
-      const int j = min(j0 + kNW * e, p.P - 1);
+      const int j = min(j0 + WPA * e, p.P - 1);
       const float* pj = base + j * C::PART_STATS;
       w[e] = pj[a];
       x0[e] = pj[2 * C::KP + a * C::DP + (lane & (C::DP - 1))];
@@ -482,13 +536,15 @@ __global__ void __launch_bounds__(256) bwd_stats_merge(BwdParams p) {
     }
 #pragma unroll
     for (int e = 0; e < kRedBatch; ++e) {
-      const float we = j0 + kNW * e < p.P ? fast_exp2(w[e] - M) : 0.f;
+      const float we = j0 + WPA * e < p.P ? fast_exp2(w[e] - M) : 0.f;
       u0 += we * x0[e];
       u1 += we * x1[e];
     }
   }
-  block4_add(u0, u1, wave, lane);
-  if (wave != 0) return;
+  if (WPA > 1) {
+    block4_add(u0, u1, wave, lane);
+    if (wave != 0) return;
+  }
   const float inv = 1.0f / L;
   float* va = p.VA + ((long)head * p.nag + a) * p.d;
   if (lane < p.d) va[lane] = u0 * inv;
@@ -508,6 +564,7 @@ __global__ void __launch_bounds__(kThr) bwd_bcast_kernel(BwdParams p) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
   const int t0 = slot * p.T, t1 = min(p.N, t0 + p.T);
   const long hd = (long)head * p.N * p.d;
+  BW_STAMP(1, 0);
   uint16_t* sAh = (uint16_t*)smem;           // A rows, hi and lo
   uint16_t* sAl = sAh + C::KP * C::RS;
   uint16_t* sVh = sAl + C::KP * C::RS;       // V_A rows, hi and lo
@@ -529,10 +586,18 @@ __global__ void __launch_bounds__(kThr) bwd_bcast_kernel(BwdParams p) {
   stage_kd<El, C::KP, C::DP, C::RS, C::TS>(sVh, sVl, nullptr, nullptr, p.VA + ah, p.nag, p.d,
                                            tid);
   __syncthreads();
+  BW_STAMP(1, 1);
+  int step = 0;
   float* dQh = p.dQ + hd;
   f32x4 accA[C::TPW], accV[C::TPW];
 #pragma unroll
   for (int u = 0; u < C::TPW; ++u) accA[u] = accV[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // scores of padding agents get -inf (probability 0)
+  float nb[KT][4];
+#pragma unroll
+  for (int kb = 0; kb < KT; ++kb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) nb[kb][i] = 16 * kb + 4 * g + i < p.nag ? 0.f : -INFINITY;
   for (int tok0 = t0; tok0 < t1; tok0 += kStep) {
     const int tok = tok0 + col;
     const bool tv = tok < t1;
@@ -554,23 +619,22 @@ __global__ void __launch_bounds__(kThr) bwd_bcast_kernel(BwdParams p) {
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        x[kb][i] = a[i];
+        x[kb][i] = a[i] + nb[kb][i];
         dp[kb][i] = b[i];
       }
     }
-    float mx = kNegBig;
+    float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < KT; ++kb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (16 * kb + 4 * g + i < p.nag) mx = fmaxf(mx, x[kb][i]);
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, x[kb][i]);
     mx = group4_max(mx);
     float l = 0.f;
 #pragma unroll
     for (int kb = 0; kb < KT; ++kb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        x[kb][i] = 16 * kb + 4 * g + i < p.nag ? fast_exp2((x[kb][i] - mx) * p.sl2) : 0.f;
+        x[kb][i] = fast_exp2((x[kb][i] - mx) * p.sl2);
         l += x[kb][i];
       }
     l = group4_sum(l);
@@ -588,6 +652,7 @@ __global__ void __launch_bounds__(kThr) bwd_bcast_kernel(BwdParams p) {
     for (int kb = 0; kb < KT; ++kb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) dp[kb][i] = x[kb][i] * (dp[kb][i] - D);   // dS2
+    if (step < 2) BW_STAMP(1, 2 + 5 * step);
     // dQ = scale dS2 A: rows = channels 16 db + 4 g + i, column = token
     bf16x8 dsh[KT / 2], dsl[KT / 2];
 #pragma unroll
@@ -616,7 +681,9 @@ __global__ void __launch_bounds__(kThr) bwd_bcast_kernel(BwdParams p) {
       for (int i = 0; i < 4; ++i) stg0[(16 * kb + 4 * g + i) * kSS + col] = El::bits(dp[kb][i]);
 #pragma unroll
     for (int s = 0; s < DT; ++s) stage_col(stgT + (32 * s + 8 * g) * kSS + col, qf[s], kSS);
+    if (step < 2) BW_STAMP(1, 3 + 5 * step);
     __syncthreads();
+    if (step < 2) BW_STAMP(1, 4 + 5 * step);
 #pragma unroll
     for (int u = 0; u < C::TPW; ++u) {
       const int t = wave + kNW * u;
@@ -641,6 +708,7 @@ __global__ void __launch_bounds__(kThr) bwd_bcast_kernel(BwdParams p) {
 #pragma unroll
     for (int s = 0; s < DT; ++s) stage_col(stgT + (32 * s + 8 * g) * kSS + col, of[s], kSS);
     __syncthreads();
+    if (step < 2) BW_STAMP(1, 5 + 5 * step);
 #pragma unroll
     for (int u = 0; u < C::TPW; ++u) {
       const int t = wave + kNW * u;
@@ -661,6 +729,42 @@ __global__ void __launch_bounds__(kThr) bwd_bcast_kernel(BwdParams p) {
       qf[s2] = qn[s2];
       of[s2] = on[s2];
     }
+    if (step < 2) BW_STAMP(1, 6 + 5 * step);
+    ++step;
+  }
+  if (p.P == 1) {
+    // the workgroup holds the whole head: dA, dV_A and D1 = rowsum(dV_A V_A)
+    // directly; D1 from per-tile partial sums in LDS (staging rows are free)
+    float* sD = reinterpret_cast<float*>(stg0);   // [DB][KP]
+#pragma unroll
+    for (int u = 0; u < C::TPW; ++u) {
+      const int t = wave + kNW * u;
+      if (C::NTILE % kNW == 0 || t < C::NTILE) {
+        const int kb = t / C::DB, db = t - kb * C::DB, c = 16 * db + r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int a = 16 * kb + 4 * g + i;
+          float prod = 0.f;
+          if (a < p.nag && c < p.d) {
+            const long o = ((long)head * p.nag + a) * p.d + c;
+            p.dA[o] = accA[u][i] * p.scale;
+            p.dVA[o] = accV[u][i];
+            prod = accV[u][i] * p.VA[o];
+          }
+#pragma unroll
+          for (int m = 1; m < 16; m <<= 1) prod += __shfl_xor(prod, m);
+          if (r == 0) sD[db * C::KP + a] = prod;
+        }
+      }
+    }
+    __syncthreads();
+    if (tid < p.nag) {
+      float dd = 0.f;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) dd += sD[db * C::KP + tid];
+      p.D1[(long)head * C::KP + tid] = dd;
+    }
+    return;
   }
   float* base = p.part + ((long)head * p.P + slot) * C::PART_BCAST;
 #pragma unroll
@@ -676,23 +780,24 @@ __global__ void __launch_bounds__(kThr) bwd_bcast_kernel(BwdParams p) {
       }
     }
   }
+  BW_STAMP(1, 12);
 }
 
 // dA = scale sum_j dA_j and dV_A = sum_j dV_A_j over the head's bcast
 // partials, and D1[a] = sum_c dV_A[a][c] V_A[a][c].
-template <int KT, int DT>
+template <int KT, int DT, int WPA>
 __global__ void __launch_bounds__(256) bwd_reduce_bcast(BwdParams p) {
   using C = Geo<KT, DT>;
-  const int head = blockIdx.x / p.nag, a = blockIdx.x - head * p.nag;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  int head, a, wave, lane;
+  if (!red_item<WPA>(p, head, a, wave, lane)) return;
   const float* base = p.part + (long)head * p.P * C::PART_BCAST + a * C::DP;
   const int ca = lane & (C::DP - 1), cb = C::DP > 64 ? lane + 64 : lane;
   float sa0 = 0.f, sa1 = 0.f, sv0 = 0.f, sv1 = 0.f;
-  for (int j0 = wave; j0 < p.P; j0 += kNW * kRedBatch) {
+  for (int j0 = wave; j0 < p.P; j0 += WPA * kRedBatch) {
     float xa[kRedBatch], xb[kRedBatch], ya[kRedBatch], yb[kRedBatch];
 #pragma unroll
     for (int e = 0; e < kRedBatch; ++e) {
-      const float* pj = base + min(j0 + kNW * e, p.P - 1) * C::PART_BCAST;
+      const float* pj = base + min(j0 + WPA * e, p.P - 1) * C::PART_BCAST;
       xa[e] = pj[ca];
       xb[e] = pj[cb];
       ya[e] = pj[C::KP * C::DP + ca];
@@ -700,7 +805,7 @@ __global__ void __launch_bounds__(256) bwd_reduce_bcast(BwdParams p) {
     }
 #pragma unroll
     for (int e = 0; e < kRedBatch; ++e) {
-      if (j0 + kNW * e < p.P) {
+      if (j0 + WPA * e < p.P) {
         sa0 += xa[e];
         sa1 += xb[e];
         sv0 += ya[e];
@@ -708,10 +813,12 @@ __global__ void __launch_bounds__(256) bwd_reduce_bcast(BwdParams p) {
       }
     }
   }
-  block4_add(sa0, sa1, wave, lane);
-  __syncthreads();
-  block4_add(sv0, sv1, wave, lane);
-  if (wave != 0) return;
+  if (WPA > 1) {
+    block4_add(sa0, sa1, wave, lane);
+    __syncthreads();
+    block4_add(sv0, sv1, wave, lane);
+    if (wave != 0) return;
+  }
   const long o = ((long)head * p.nag + a) * p.d;
   float dd = 0.f;
   if (lane < p.d) {
@@ -739,6 +846,7 @@ __global__ void __launch_bounds__(kThr) bwd_agg_kernel(BwdParams p) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
   const int t0 = slot * p.T, t1 = min(p.N, t0 + p.T);
   const long hd = (long)head * p.N * p.d;
+  BW_STAMP(2, 0);
   uint16_t* sAh = (uint16_t*)smem;           // A rows, hi and lo
   uint16_t* sAl = sAh + C::KP * C::RS;
   uint16_t* sGh = sAl + C::KP * C::RS;       // dV_A rows, hi and lo
@@ -773,6 +881,8 @@ __global__ void __launch_bounds__(kThr) bwd_agg_kernel(BwdParams p) {
     }
   }
   __syncthreads();
+  BW_STAMP(2, 1);
+  int step = 0;
   uint16_t* dkh = p.dk + hd;
   uint16_t* dvh = p.dv + hd;
   f32x4 accA[C::TPW];
@@ -802,6 +912,7 @@ __global__ void __launch_bounds__(kThr) bwd_agg_kernel(BwdParams p) {
         ds[kb][i] = pr[kb][i] * (b[i] - Dr[kb][i]);
       }
     }
+    if (step < 2) BW_STAMP(2, 2 + 4 * step);
     // dk = scale dS1^T A and dv = P1^T dV_A: rows = channels, column = token
     bf16x8 dsh[KT / 2], dsl[KT / 2], ph[KT / 2];
 #pragma unroll
@@ -832,6 +943,7 @@ __global__ void __launch_bounds__(kThr) bwd_agg_kernel(BwdParams p) {
         *reinterpret_cast<uint2*>(dvh + o) = uint2{El::pack2(av[0], av[1]), El::pack2(av[2], av[3])};
       }
     }
+    if (step < 2) BW_STAMP(2, 3 + 4 * step);
     // dA += dS1 K over the step's tokens
 #pragma unroll
     for (int kb = 0; kb < KT; ++kb)
@@ -840,6 +952,7 @@ __global__ void __launch_bounds__(kThr) bwd_agg_kernel(BwdParams p) {
 #pragma unroll
     for (int s = 0; s < DT; ++s) stage_col(stgT + (32 * s + 8 * g) * kSS + col, kf[s], kSS);
     __syncthreads();
+    if (step < 2) BW_STAMP(2, 4 + 4 * step);
 #pragma unroll
     for (int u = 0; u < C::TPW; ++u) {
       const int t = wave + kNW * u;
@@ -857,6 +970,23 @@ __global__ void __launch_bounds__(kThr) bwd_agg_kernel(BwdParams p) {
       kf[s2] = kn[s2];
       vf[s2] = vn[s2];
     }
+    if (step < 2) BW_STAMP(2, 5 + 4 * step);
+    ++step;
+  }
+  if (p.P == 1) {   // the workgroup holds the whole head: add to dA directly
+#pragma unroll
+    for (int u = 0; u < C::TPW; ++u) {
+      const int t = wave + kNW * u;
+      if (C::NTILE % kNW == 0 || t < C::NTILE) {
+        const int kb = t / C::DB, db = t - kb * C::DB, c = 16 * db + r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int a = 16 * kb + 4 * g + i;
+          if (a < p.nag && c < p.d) p.dA[((long)head * p.nag + a) * p.d + c] += accA[u][i] * p.scale;
+        }
+      }
+    }
+    return;
   }
   float* base = p.part + ((long)head * p.P + slot) * C::PART_AGG;
 #pragma unroll
@@ -868,35 +998,38 @@ __global__ void __launch_bounds__(kThr) bwd_agg_kernel(BwdParams p) {
       for (int i = 0; i < 4; ++i) base[(16 * kb + 4 * g + i) * C::DP + 16 * db + r] = accA[u][i];
     }
   }
+  BW_STAMP(2, 10);
 }
 
 // dA += scale sum_j dA_j over the head's agg partials.
-template <int KT, int DT>
+template <int KT, int DT, int WPA>
 __global__ void __launch_bounds__(256) bwd_reduce_agg(BwdParams p) {
   using C = Geo<KT, DT>;
-  const int head = blockIdx.x / p.nag, a = blockIdx.x - head * p.nag;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  int head, a, wave, lane;
+  if (!red_item<WPA>(p, head, a, wave, lane)) return;
   const float* base = p.part + (long)head * p.P * C::PART_AGG + a * C::DP;
   const int ca = lane & (C::DP - 1), cb = C::DP > 64 ? lane + 64 : lane;
   float s0 = 0.f, s1 = 0.f;
-  for (int j0 = wave; j0 < p.P; j0 += kNW * kRedBatch) {
+  for (int j0 = wave; j0 < p.P; j0 += WPA * kRedBatch) {
     float xa[kRedBatch], xb[kRedBatch];
 #pragma unroll
     for (int e = 0; e < kRedBatch; ++e) {
-      const float* pj = base + min(j0 + kNW * e, p.P - 1) * C::PART_AGG;
+      const float* pj = base + min(j0 + WPA * e, p.P - 1) * C::PART_AGG;
       xa[e] = pj[ca];
       xb[e] = pj[cb];
     }
 #pragma unroll
     for (int e = 0; e < kRedBatch; ++e) {
-      if (j0 + kNW * e < p.P) {
+      if (j0 + WPA * e < p.P) {
         s0 += xa[e];
         s1 += xb[e];
       }
     }
   }
-  block4_add(s0, s1, wave, lane);
-  if (wave != 0) return;
+  if (WPA > 1) {
+    block4_add(s0, s1, wave, lane);
+    if (wave != 0) return;
+  }
   const long o = ((long)head * p.nag + a) * p.d;
   if (lane < p.d) p.dA[o + lane] += s0 * p.scale;
   if (C::DP > 64 && lane + 64 < p.d) p.dA[o + lane + 64] += s1 * p.scale;
@@ -904,14 +1037,16 @@ __global__ void __launch_bounds__(256) bwd_reduce_agg(BwdParams p) {
 
 // ------------------------------------------------------------------ pooling and dq
 // A = 2-D average pool of q over the s x s windows (rows [i h / s, ceil((i+1)
-// h / s)), likewise for columns).  A group of 8 lanes per (head, agent,
-// 8-channel chunk); lane u sums the window's tokens u, u + 8, ...
+// h / s)), likewise for columns).  A group of U lanes (a power of two up to
+// 64, about the window size) per (head, agent, 8-channel chunk); lane u sums
+// the window's tokens u, u + U, ... and the group adds its U sums.
 template <class El>
 __global__ void __launch_bounds__(256) bwd_pool(const uint16_t* __restrict__ q,
                                                 float* __restrict__ A, int BH, int N, int h,
-                                                int w, int d, int s) {
+                                                int w, int d, int s, int U) {
   const int nag = s * s, nch = d >> 3;
-  const int item = blockIdx.x * 32 + (threadIdx.x >> 3), u = threadIdx.x & 7;
+  const int gid = blockIdx.x * 256 + threadIdx.x;
+  const int item = gid / U, u = gid & (U - 1);
   const bool live = item < BH * nag * nch;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   int bh = 0, agent = 0, ch = 0, cnt = 1;
@@ -927,7 +1062,7 @@ __global__ void __launch_bounds__(256) bwd_pool(const uint16_t* __restrict__ q,
     cnt = (r1 - r0) * ww;
     const uint16_t* qh = q + (long)bh * N * d + ch * 8;
 #pragma unroll 4
-    for (int t = u; t < cnt; t += 8) {
+    for (int t = u; t < cnt; t += U) {
       const int rr = r0 + t / ww, cc = c0 + t % ww;
       const uint4 x = *reinterpret_cast<const uint4*>(qh + (long)(rr * w + cc) * d);
       const unsigned wd[4] = {x.x, x.y, x.z, x.w};
@@ -939,8 +1074,7 @@ __global__ void __launch_bounds__(256) bwd_pool(const uint16_t* __restrict__ q,
       }
     }
   }
-#pragma unroll
-  for (int o = 1; o < 8; o <<= 1)
+  for (int o = 1; o < U; o <<= 1)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], o);
   if (live && u == 0) {
@@ -954,36 +1088,47 @@ __global__ void __launch_bounds__(256) bwd_pool(const uint16_t* __restrict__ q,
 
 // dq (16-bit) = dQ + the pooling's share of dA: each window's agent gradient
 // divided by its token count, for every window holding the token (dA null:
-// supplied agents, dq = dQ).  One thread per (head, token, 8-channel chunk).
+// supplied agents, dq = dQ).  One thread per (token, 8-channel chunk) of head
+// blockIdx.y.  When s divides h and w the windows tile the grid and a token
+// lies in exactly one (`tiled`); otherwise windows may overlap and the
+// three candidates around r s / h (and c s / w) are tested.
 template <class El>
 __global__ void __launch_bounds__(256) bwd_finish_dq(const float* __restrict__ dQ,
                                                      const float* __restrict__ dA,
-                                                     uint16_t* __restrict__ dq, int BH, int N,
-                                                     int h, int w, int d, int s) {
+                                                     uint16_t* __restrict__ dq, int N, int h,
+                                                     int w, int d, int s, int tiled) {
   const int nch = d >> 3;
-  const int gid = blockIdx.x * 256 + threadIdx.x;
-  if (gid >= BH * N * nch) return;
-  const int ch = gid % nch, bn = gid / nch;
-  const long e0 = (long)bn * d + ch * 8;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= N * nch) return;
+  const int bh = blockIdx.y;
+  const int n = idx / nch, ch = idx - n * nch;
+  const long e0 = ((long)bh * N + n) * d + ch * 8;
   float4 a = *reinterpret_cast<const float4*>(dQ + e0);
   float4 b = *reinterpret_cast<const float4*>(dQ + e0 + 4);
+  auto add = [&](const float* pa, float inv) {
+    const float4 x = *reinterpret_cast<const float4*>(pa);
+    const float4 y = *reinterpret_cast<const float4*>(pa + 4);
+    a = float4{a.x + x.x * inv, a.y + x.y * inv, a.z + x.z * inv, a.w + x.w * inv};
+    b = float4{b.x + y.x * inv, b.y + y.y * inv, b.z + y.z * inv, b.w + y.w * inv};
+  };
   if (dA) {
-    const int n = bn % N, bh = bn / N, nag = s * s;
+    const int nag = s * s;
     const int r = n / w, cc = n - r * w;
-    const int i0 = max(0, (r * s) / h - 1), i1 = min(s - 1, (r * s) / h + 1);
-    const int j0 = max(0, (cc * s) / w - 1), j1 = min(s - 1, (cc * s) / w + 1);
-    for (int i = i0; i <= i1; ++i) {
-      const int rs = (i * h) / s, re = ((i + 1) * h + s - 1) / s;
-      if (r < rs || r >= re) continue;
-      for (int j = j0; j <= j1; ++j) {
-        const int cs = (j * w) / s, ce = ((j + 1) * w + s - 1) / s;
-        if (cc < cs || cc >= ce) continue;
-        const float inv = 1.0f / (float)((re - rs) * (ce - cs));
-        const float* pa = dA + ((long)bh * nag + i * s + j) * d + ch * 8;
-        const float4 x = *reinterpret_cast<const float4*>(pa);
-        const float4 y = *reinterpret_cast<const float4*>(pa + 4);
-        a = float4{a.x + x.x * inv, a.y + x.y * inv, a.z + x.z * inv, a.w + x.w * inv};
-        b = float4{b.x + y.x * inv, b.y + y.y * inv, b.z + y.z * inv, b.w + y.w * inv};
+    const float* dAh = dA + (long)bh * nag * d + ch * 8;
+    if (tiled) {
+      const int wh = h / s, wwid = w / s;
+      add(dAh + ((r / wh) * s + cc / wwid) * d, 1.0f / (float)(wh * wwid));
+    } else {
+      const int i0 = max(0, (r * s) / h - 1), i1 = min(s - 1, (r * s) / h + 1);
+      const int j0 = max(0, (cc * s) / w - 1), j1 = min(s - 1, (cc * s) / w + 1);
+      for (int i = i0; i <= i1; ++i) {
+        const int rs = (i * h) / s, re = ((i + 1) * h + s - 1) / s;
+        if (r < rs || r >= re) continue;
+        for (int j = j0; j <= j1; ++j) {
+          const int cs = (j * w) / s, ce = ((j + 1) * w + s - 1) / s;
+          if (cc < cs || cc >= ce) continue;
+          add(dAh + (i * s + j) * d, 1.0f / (float)((re - rs) * (ce - cs)));
+        }
       }
     }
   }
@@ -1022,39 +1167,49 @@ struct Lds {
 template <class El, int KT, int DT>
 int run_passes(BwdParams p, const Pass (&pp)[3], hipStream_t st) {
   using C = Geo<KT, DT>;
-  const unsigned waves_grid = (unsigned)(p.BH * p.nag);   // one block per (head, agent)
+  // reductions: four waves per agent from 8 partials, else one
+  const unsigned items = (unsigned)(p.BH * p.nag);
+  auto rgrid = [&](int P) { return dim3(P > 8 ? items : (items + kNW - 1) / kNW); };
   const int nkd = p.BH * p.nag * p.d;
   const unsigned g_kd = (unsigned)std::min(4096, (nkd + 255) / 256);
   hipError_t e;
   if (p.agents_in) {
     bwd_widen<El><<<dim3(g_kd), dim3(256), 0, st>>>(p.agents_in, const_cast<float*>(p.A), nkd);
   } else {
-    const int items = p.BH * p.nag * (p.d / 8);
-    bwd_pool<El><<<dim3((unsigned)((items + 31) / 32)), dim3(256), 0, st>>>(
-        p.q, const_cast<float*>(p.A), p.BH, p.N, p.h, p.w, p.d, p.s);
+    // lanes per window: about an eighth of its tokens (largest window), 1 to 8
+    const int wmax = ((p.h + p.s - 1) / p.s + 1) * ((p.w + p.s - 1) / p.s + 1);
+    int U = 1;
+    while (U < 8 && 8 * U < wmax) U <<= 1;
+    const long threads = (long)p.BH * p.nag * (p.d / 8) * U;
+    bwd_pool<El><<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st>>>(
+        p.q, const_cast<float*>(p.A), p.BH, p.N, p.h, p.w, p.d, p.s, U);
   }
   if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   p.P = pp[0].P;
   p.T = pp[0].T;
   bwd_stats_kernel<El, KT, DT><<<dim3((unsigned)(p.BH * p.P)), dim3(kThr), C::STATS, st>>>(p);
   if ((e = hipGetLastError()) != hipSuccess) return (int)e;
-  bwd_stats_merge<KT, DT><<<dim3(waves_grid), dim3(256), 0, st>>>(p);
+  if (p.P > 8) bwd_stats_merge<KT, DT, 4><<<rgrid(p.P), dim3(256), 0, st>>>(p);
+  else if (p.P > 1) bwd_stats_merge<KT, DT, 1><<<rgrid(p.P), dim3(256), 0, st>>>(p);
   if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   p.P = pp[1].P;
   p.T = pp[1].T;
   bwd_bcast_kernel<El, KT, DT><<<dim3((unsigned)(p.BH * p.P)), dim3(kThr), C::BCAST, st>>>(p);
   if ((e = hipGetLastError()) != hipSuccess) return (int)e;
-  bwd_reduce_bcast<KT, DT><<<dim3(waves_grid), dim3(256), 0, st>>>(p);
+  if (p.P > 8) bwd_reduce_bcast<KT, DT, 4><<<rgrid(p.P), dim3(256), 0, st>>>(p);
+  else if (p.P > 1) bwd_reduce_bcast<KT, DT, 1><<<rgrid(p.P), dim3(256), 0, st>>>(p);
   if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   p.P = pp[2].P;
   p.T = pp[2].T;
   bwd_agg_kernel<El, KT, DT><<<dim3((unsigned)(p.BH * p.P)), dim3(kThr), C::AGG, st>>>(p);
   if ((e = hipGetLastError()) != hipSuccess) return (int)e;
-  bwd_reduce_agg<KT, DT><<<dim3(waves_grid), dim3(256), 0, st>>>(p);
+  if (p.P > 8) bwd_reduce_agg<KT, DT, 4><<<rgrid(p.P), dim3(256), 0, st>>>(p);
+  else if (p.P > 1) bwd_reduce_agg<KT, DT, 1><<<rgrid(p.P), dim3(256), 0, st>>>(p);
   if ((e = hipGetLastError()) != hipSuccess) return (int)e;
-  const int nq = p.BH * p.N * (p.d / 8);
-  bwd_finish_dq<El><<<dim3((unsigned)((nq + 255) / 256)), dim3(256), 0, st>>>(
-      p.dQ, p.agents_in ? nullptr : p.dA, p.dq, p.BH, p.N, p.h, p.w, p.d, p.s);
+  const int nq = p.N * (p.d / 8);
+  const int tiled = (p.h % p.s == 0 && p.w % p.s == 0) ? 1 : 0;
+  bwd_finish_dq<El><<<dim3((unsigned)((nq + 255) / 256), (unsigned)p.BH), dim3(256), 0, st>>>(
+      p.dQ, p.agents_in ? nullptr : p.dA, p.dq, p.N, p.h, p.w, p.d, p.s, tiled);
   if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   if (p.agents_in) bwd_narrow<El><<<dim3(g_kd), dim3(256), 0, st>>>(p.dA, p.dagents, nkd);
   return (int)hipGetLastError();

@@ -65,6 +65,14 @@ CASES = [
     inputs.custom("bwd_supplied_f16", B=1, H=3, h=12, w=12, d=64, s=4, dtype="f16",
                   supplied_agents=True),
     inputs.custom("bwd_one_agent", B=2, H=1, h=6, w=5, d=64, s=1),
+    # matrix-core path: head dims below one 32-channel slab and between slabs,
+    # many token workgroups per head (two batches of partials per wave in the
+    # reductions), supplied bf16 agents at 64 agents
+    inputs.custom("bwd_d32_k49", B=2, H=2, h=14, w=14, d=32, s=7),
+    inputs.custom("bwd_d24_f16", B=1, H=2, h=12, w=10, d=24, s=3, dtype="f16"),
+    inputs.custom("bwd_d96_k36", B=1, H=2, h=16, w=16, d=96, s=6),
+    inputs.custom("bwd_one_head_4096", B=1, H=1, h=64, w=64, d=64, s=8),
+    inputs.custom("bwd_supplied_k64", B=2, H=2, h=16, w=16, d=64, s=8, supplied_agents=True),
 ]
 
 
