@@ -10,6 +10,8 @@ Sources (web pages about Agent Attention, Han et al., arXiv 2312.08874):
            Attention" (paperlayer.ai summary of arXiv 2312.08874v3).
   [JSQMD]  "Agent Attention：Transformer计算量太大？试试这个'代理令牌'的轻量化方案"
            (jsqmd.com news article).
+  [CoreUI] "别再死磕Softmax了！清华黄高团队新作Agent Attention…" (coreui.cn
+           article).
 
 What is computed, for every batch b and head h independently:
   1. agents:      A = 2-D average pool of Q over the h x w token grid down to
@@ -33,7 +35,10 @@ Readings where the pages leave a step open:
   * one scale factor (1/sqrt(d) in every workload) is applied in both
     softmaxes, as in the [JSQMD] §1 pseudocode.
   * the broadcast keys are the agents A (not V_A); projections are not part
-    of this operator.
+    of this operator (module_forward adds them around it: q, k, v from one
+    packed Linear of the token features in the order q, k, v, heads split
+    head-major, q, k, v and the concatenated heads held in the tensor
+    format, an optional output Linear).
   * module enhancements ([Paper] §4 Module Enhancements and Implementation
     Details), optional: agent biases B1 and B2 enter the two attentions as
     additive terms of the scaled logits, softmax(scale A K^T + B1) and
@@ -170,6 +175,69 @@ def forward(Q, K, V, h: int, w: int, s: int, scale: float, A=None, bias_agg=None
     if dwc_weight is not None:
         O = O + dwc(V, h, w, dwc_weight, dwc_bias)
     return O, A, V_A
+
+
+# ------------------------------------------------------------ full module
+
+def round_to_format(x: np.ndarray, fmt: str) -> np.ndarray:
+    """x rounded to nearest-even in the tensor format fmt ("f32", "bf16" or
+    "f16") and widened back to float64: the value a tensor of that format
+    holds.  bf16 keeps the top 16 bits of the float32 pattern (8-bit
+    significand)."""
+    x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
+    if fmt == "f32":
+        return x32.astype(np.float64)
+    if fmt == "f16":
+        return x32.astype(np.float16).astype(np.float64)
+    assert fmt == "bf16", fmt
+    u = x32.view(np.uint32)
+    r = ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))
+         & np.uint32(0xFFFF0000))
+    return r.view(np.float32).astype(np.float64)
+
+
+def module_forward(X, W_qkv, b_qkv, W_out, b_out, H: int, h: int, w: int, s: int,
+                   scale: float, fmt: str, A=None, bias_agg=None, bias_bcast=None,
+                   dwc_weight=None, dwc_bias=None):
+    """The attention module on token features X [B, N, C] ([Paper] §3
+    Preliminaries: the projections W_Q, W_K, W_V map the channels to per-head
+    queries, keys and values; §4: agent attention with the agent biases and the depth-wise
+    convolution term; [CoreUI] §3.1: AgentAttention(dim, num_heads, num_agents)
+    maps [B, N, dim] to [B, N, dim]).
+
+    q, k, v = X W_qkv^T + b_qkv split along the 3C outputs in that order,
+    each [B, N, C] read as H heads of d = C / H channels (channel c of head
+    hd is feature hd*d + c); they are held in the tensor format fmt, as the
+    output of a Linear layer in that format is.  O = forward(q, k, v, ...)
+    per head, concatenated back to [B, N, C]; with W_out, that concatenation
+    is held in fmt and y = O W_out^T + b_out, else y = O.  Weights in the
+    Linear layout [out_features, in_features]; b_qkv, W_out, b_out may be
+    None.  Returns y [B, N, C] float64 (unrounded).
+    """
+    X = np.asarray(X, dtype=np.float64)
+    B, N, C = X.shape
+    assert C % H == 0 and N == h * w
+    d = C // H
+    W_qkv = np.asarray(W_qkv, dtype=np.float64)
+    assert W_qkv.shape == (3 * C, C)
+    qkv = X @ W_qkv.T
+    if b_qkv is not None:
+        qkv = qkv + np.asarray(b_qkv, dtype=np.float64)
+    qkv = round_to_format(qkv, fmt)
+
+    def heads(t):   # [B, N, C] -> [B, H, N, d]
+        return np.ascontiguousarray(t.reshape(B, N, H, d).transpose(0, 2, 1, 3))
+
+    q, k, v = heads(qkv[..., :C]), heads(qkv[..., C:2 * C]), heads(qkv[..., 2 * C:])
+    O, _, _ = forward(q, k, v, h, w, s, scale, A=A, bias_agg=bias_agg, bias_bcast=bias_bcast,
+                      dwc_weight=dwc_weight, dwc_bias=dwc_bias)
+    o = O.transpose(0, 2, 1, 3).reshape(B, N, C)
+    if W_out is None:
+        return o
+    y = round_to_format(o, fmt) @ np.asarray(W_out, dtype=np.float64).T
+    if b_out is not None:
+        y = y + np.asarray(b_out, dtype=np.float64)
+    return y
 
 
 # ------------------------------------------------------------------ backward

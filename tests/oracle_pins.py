@@ -502,4 +502,110 @@ def pin_pool_backward_is_adjoint(orc):
         assert abs(lhs - rhs) < 1e-12
 
 
+# ------------------------------------------------------------- full module
+
+def _torch_round(x, fmt):
+    """Rounding through torch's own dtype conversions (RNE)."""
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[fmt]
+    return x.to(dt).to(torch.float64)
+
+
+def _torch_module(X, Wqkv, bqkv, Wout, bout, H, h, w, s, scale, fmt, B1=None, B2=None, Wd=None,
+                  bd=None):
+    """The module from torch routines: F.linear, dtype casts, adaptive
+    pooling, two scaled_dot_product_attention calls (with the biases as
+    additive masks) and conv2d."""
+    Xt = _t(X)
+    B, N, C = X.shape
+    d = C // H
+    qkv = _torch_round(F.linear(Xt, _t(Wqkv), None if bqkv is None else _t(bqkv)), fmt)
+    q, k, v = (qkv[..., i * C:(i + 1) * C].reshape(B, N, H, d).permute(0, 2, 1, 3)
+               for i in range(3))
+    x = q.reshape(B * H, h, w, d).permute(0, 3, 1, 2)
+    A = F.adaptive_avg_pool2d(x, (s, s)).permute(0, 2, 3, 1).reshape(B, H, s * s, d)
+    m1 = None if B1 is None else _t(B1)[None]
+    m2 = None if B2 is None else _t(B2)[None]
+    VA = F.scaled_dot_product_attention(A, k, v, attn_mask=m1, scale=scale)
+    O = F.scaled_dot_product_attention(q, A, VA, attn_mask=m2, scale=scale)
+    if Wd is not None:
+        O = O + _t(_dwc_torch(v.numpy(), h, w, Wd, bd))
+    o = O.permute(0, 2, 1, 3).reshape(B, N, C)
+    if Wout is None:
+        return o.numpy()
+    return F.linear(_torch_round(o, fmt), _t(Wout), None if bout is None else _t(bout)).numpy()
+
+
+def pin_round_to_format(orc):
+    """Rounding to bf16 / f16 / f32 equals torch's dtype conversions, and
+    hand cases of round-to-nearest-even: 1 + 2^-8 (a tie) goes to 1, 1 +
+    3 * 2^-8 to 1 + 2^-6 in bf16, 1 + 2^-11 (a tie) to 1 in f16."""
+    rng = _rng(81)
+    x = rng.standard_normal(4096) * np.exp(rng.uniform(-20, 20, 4096))
+    for fmt in ("bf16", "f16", "f32"):
+        ref = _torch_round(_t(np.clip(x, -6e4, 6e4) if fmt == "f16" else x), fmt).numpy()
+        got = orc.round_to_format(np.clip(x, -6e4, 6e4) if fmt == "f16" else x, fmt)
+        assert np.array_equal(got, ref), fmt
+    assert orc.round_to_format(np.array([1 + 2.0 ** -8]), "bf16")[0] == 1.0
+    assert orc.round_to_format(np.array([1 + 3 * 2.0 ** -8]), "bf16")[0] == 1 + 2.0 ** -6
+    assert orc.round_to_format(np.array([1 + 2.0 ** -11]), "f16")[0] == 1.0
+
+
+def pin_module_is_library_composition(orc):
+    """The module (projections, heads, pooling, two attentions with both
+    biases, DWC, output projection) equals its composition from torch
+    routines, in bf16 and f32 formats, with and without the output Linear."""
+    rng = _rng(82)
+    B, H, h, w, s, d = 2, 3, 5, 6, 2, 4
+    N, C, k = h * w, H * d, s * s
+    X = rng.standard_normal((B, N, C))
+    Wqkv = rng.standard_normal((3 * C, C)) / math.sqrt(C)
+    bqkv = rng.standard_normal(3 * C) * 0.3
+    Wout = rng.standard_normal((C, C)) / math.sqrt(C)
+    bout = rng.standard_normal(C) * 0.3
+    B1, B2 = rng.standard_normal((H, k, N)), rng.standard_normal((H, N, k))
+    Wd, bd = rng.standard_normal((C, 3, 3)) / 3, rng.standard_normal(C) * 0.5
+    for fmt in ("bf16", "f32"):
+        for wo, bo in ((Wout, bout), (None, None)):
+            got = orc.module_forward(X, Wqkv, bqkv, wo, bo, H, h, w, s, 0.5, fmt, bias_agg=B1,
+                                     bias_bcast=B2, dwc_weight=Wd, dwc_bias=bd)
+            ref = _torch_module(X, Wqkv, bqkv, wo, bo, H, h, w, s, 0.5, fmt, B1, B2, Wd, bd)
+            assert np.allclose(got, ref, rtol=0, atol=1e-12), fmt
+
+
+def pin_module_constant_values(orc):
+    """Value projection zero with bias c: every value row is c, so every
+    output row is round(c) W_out^T + b_out whatever the queries and keys."""
+    rng = _rng(83)
+    B, H, h, w, s, d = 2, 2, 4, 4, 2, 4
+    N, C = h * w, H * d
+    X = rng.standard_normal((B, N, C))
+    Wqkv = rng.standard_normal((3 * C, C))
+    Wqkv[2 * C:] = 0.0
+    bqkv = np.zeros(3 * C)
+    c = rng.standard_normal(C)
+    bqkv[2 * C:] = c
+    Wout, bout = rng.standard_normal((C, C)), rng.standard_normal(C)
+    got = orc.module_forward(X, Wqkv, bqkv, Wout, bout, H, h, w, s, 0.7, "bf16")
+    cb = orc.round_to_format(c, "bf16")
+    ref = orc.round_to_format(cb, "bf16") @ Wout.T + bout
+    assert np.allclose(got, np.broadcast_to(ref, got.shape), rtol=0, atol=1e-12)
+
+
+def pin_module_uniform_scores(orc):
+    """Query and key projections zero: every score is 0, both softmaxes are
+    uniform, and every output row is the token mean of the values (per head,
+    concatenated), y = mean(v) W_out^T + b_out."""
+    rng = _rng(84)
+    B, H, h, w, s, d = 1, 2, 3, 5, 2, 4
+    N, C = h * w, H * d
+    X = rng.standard_normal((B, N, C))
+    Wqkv = rng.standard_normal((3 * C, C))
+    Wqkv[:2 * C] = 0.0
+    Wout, bout = rng.standard_normal((C, C)), rng.standard_normal(C)
+    got = orc.module_forward(X, Wqkv, None, Wout, bout, H, h, w, s, 0.9, "f32")
+    v = _torch_round(_t(X @ Wqkv[2 * C:].T), "f32").numpy()
+    ref = _torch_round(_t(v.mean(axis=1)), "f32").numpy() @ Wout.T + bout
+    assert np.allclose(got, np.broadcast_to(ref[:, None, :], got.shape), rtol=0, atol=1e-12)
+
+
 ALL_PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_")]

@@ -235,6 +235,45 @@ _orig_backward = orc.backward
 _orig_dwc = orc.dwc
 _orig_forward = orc.forward
 
+# ------------------------------------------------------------- module mutants
+
+_real_module_forward = orc.module_forward
+_real_round = orc.round_to_format
+
+
+def _module_variant(swap_qk=False, channel_major=False, drop_out_bias=False, no_round=False):
+    real = _real_module_forward
+
+    def f(X, W_qkv, b_qkv, W_out, b_out, H, h, w, s, scale, fmt, **kw):
+        C = np.asarray(X).shape[-1]
+        W = np.array(W_qkv, dtype=np.float64)
+        b = None if b_qkv is None else np.array(b_qkv, dtype=np.float64)
+        if swap_qk:
+            W[:C], W[C:2 * C] = W[C:2 * C].copy(), W[:C].copy()
+            if b is not None:
+                b[:C], b[C:2 * C] = b[C:2 * C].copy(), b[:C].copy()
+        if channel_major:   # heads read as [d, H] instead of [H, d]
+            d = C // H
+            perm = np.arange(C).reshape(d, H).T.reshape(-1)
+            W = np.concatenate([W[i * C:(i + 1) * C][perm] for i in range(3)])
+            if b is not None:
+                b = np.concatenate([b[i * C:(i + 1) * C][perm] for i in range(3)])
+            if W_out is not None:
+                W_out = np.asarray(W_out)[:, perm]
+        if no_round:
+            fmt = "f32"
+        return real(X, W, b, W_out, None if drop_out_bias else b_out, H, h, w, s, scale, fmt,
+                    **kw)
+    return f
+
+
+def _round_truncate(x, fmt):
+    x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
+    if fmt == "bf16":
+        return (x32.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32).astype(np.float64)
+    return _real_round(x, fmt)
+
+
 MUTANTS = {
     "aggregate_bias_inside_scale": ("aggregate", _agg_bias_scaled),
     "aggregate_bias_dropped": ("aggregate", _agg_bias_dropped),
@@ -268,6 +307,11 @@ MUTANTS = {
     "forward_agents_as_values": ("forward", _forward_agents_as_values),
     "forward_pools_keys": ("forward", _forward_pool_keys),
     "forward_skips_aggregation": ("forward", _forward_skip_aggregation),
+    "module_swaps_queries_keys": ("module_forward", _module_variant(swap_qk=True)),
+    "module_heads_channel_major": ("module_forward", _module_variant(channel_major=True)),
+    "module_drops_output_bias": ("module_forward", _module_variant(drop_out_bias=True)),
+    "module_skips_rounding": ("module_forward", _module_variant(no_round=True)),
+    "round_truncates": ("round_to_format", _round_truncate),
 }
 
 
