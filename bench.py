@@ -281,6 +281,10 @@ def main():
     ap.add_argument("--module", action="store_true",
                     help="time the full module forward: agent biases in both attentions and "
                          "the depth-wise 3x3 convolution of V (agent_attn_forward_module)")
+    ap.add_argument("--projections", action="store_true",
+                    help="time the attention module on token features: q/k/v projection, the "
+                         "module forward (biases, DWC) and the output projection "
+                         "(agent_attn_module_forward)")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (agent_attn_backward: gradients of q, k, v "
                          "from the output gradient, forward recomputed inside)")
@@ -323,6 +327,8 @@ def main():
     if args.dtype and wl.dtype != "f32":
         import dataclasses
         wl = dataclasses.replace(wl, dtype=args.dtype)
+    if args.projections:
+        args.module = True
     if (args.module or args.backward) and args.layout != "bhnd":
         print("bench.py: --module takes the dense layout only", file=sys.stderr)
         sys.exit(2)
@@ -355,6 +361,17 @@ def main():
                "dwc_weight": torch.randn((wl.H * wl.d, 3, 3), generator=gen, device=dev) / 3,
                "dwc_bias": 0.5 * torch.randn((wl.H * wl.d,), generator=gen, device=dev)}
 
+    C = wl.H * wl.d
+    if args.projections:   # token features per set; weights (N(0, 1/C)) and biases shared
+        xs = [torch.randn((wl.B, wl.N, C), generator=gen, device=dev).to(dt) for _ in range(R)]
+        wqkv = (torch.randn((3 * C, C), generator=gen, device=dev) / math.sqrt(C)).to(dt)
+        wout = (torch.randn((C, C), generator=gen, device=dev) / math.sqrt(C)).to(dt)
+        bqkv = 0.1 * torch.randn((3 * C,), generator=gen, device=dev)
+        bout = 0.1 * torch.randn((C,), generator=gen, device=dev)
+        ys = [torch.empty_like(x) for x in xs[:2]]
+        pws = torch.zeros(max(1, _binding.lib().agent_attn_module_workspace_bytes(
+            wl.B, wl.H, wl.h, wl.w, wl.d, wl.s, {"f32": 0, "bf16": 1, "f16": 2}[wl.dtype])),
+            dtype=torch.uint8, device=dev)
     if args.backward:
         bws = torch.empty(max(1, _binding.agent_attn_backward_workspace_bytes(
             wl.B, wl.H, wl.h, wl.w, wl.d, wl.s, {"f32": 0, "bf16": 1, "f16": 2}[wl.dtype])),
@@ -365,6 +382,10 @@ def main():
         if args.backward:   # the output buffer of the set serves as dO
             eav.agent_attn_backward(q, k, v, o, (wl.h, wl.w), wl.s, wl.scale, agents=a,
                                     workspace=bws)
+        elif args.projections:
+            eav.agent_attn_module_forward(xs[i % R], wqkv, (wl.h, wl.w), wl.s, wl.H, wl.scale,
+                                          b_qkv=bqkv, w_out=wout, b_out=bout, agents=a,
+                                          out=ys[i % 2], workspace=pws, **mod)
         elif args.module:
             eav.agent_attn_forward_module(q, k, v, (wl.h, wl.w), wl.s, wl.scale, agents=a, out=o,
                                           workspace=ws, **mod)
@@ -423,6 +444,10 @@ def main():
     if args.backward:  # q, k, v, dO read and dq, dk, dv written; 8 + 16 products of N k d MACs
         abytes = abytes // 4 * 7
         aflops = aflops * 3
+    if args.projections:   # x read and y written (q, k, v, o are intermediates), the
+        # weights and the two biases; + 4 C MACs per token and output channel (projections)
+        abytes = 2 * wl.B * wl.N * C * wl.es + 4 * C * C * wl.es + 2 * wl.H * wl.k * wl.N * 4
+        aflops += 8 * wl.B * wl.N * C * C
     achieved_gbs = abytes / (kernel_us * 1e-6) / 1e9
     achieved_tflops = aflops / (kernel_us * 1e-6) / 1e12
     # counters were taken on the plain bf16 dense kernel: other variants report none
@@ -447,6 +472,8 @@ def main():
                 "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": traffic}
     line = {
         "metric": ("agent-attn bwd tokens/s (B*H*N/s)" if args.backward else
+                   "agent-attn module fwd tokens/s (B*N*H/s), x -> y with projections"
+                   if args.projections else
                    "agent-attn fwd tokens/s (B*H*N/s) + achieved HBM GB/s at N=3136,k=49 bf16"),
         "value": value,
         "unit": "tokens/s",
@@ -465,6 +492,8 @@ def main():
                    "layout": "[B,N,H,d] storage" if args.layout == "bnhd" else "[B,H,N,d]",
                    **({"module_terms": ["agent biases B1, B2", "depth-wise 3x3 conv of V"]}
                       if args.module else {}),
+                   **({"projections": ["x -> q, k, v (C -> 3C)", "o -> y (C -> C)"], "C": C}
+                      if args.projections else {}),
                    **({"pass": "backward (dq, dk, dv)",
                        "backward_path": ("matrix-core token passes" if mfma_bwd
                                          else "float32 products")} if args.backward else {})},

@@ -10,6 +10,6 @@ library is loaded on first use.
 from ._binding import (AgentAttnError, EXPORTED, LIB_PATH, agent_attn_aggregate,  # noqa: F401
                        agent_attn_backward,
                        agent_attn_broadcast, agent_attn_forward, agent_attn_forward_cached,
-                       agent_attn_forward_module,
+                       agent_attn_forward_module, agent_attn_module_forward,
                        agent_attn_pool, agent_attn_read_faults, agent_attn_release,
                        agent_attn_set_wait_limit, agent_attn_workspace_bytes, lib)

@@ -32,6 +32,9 @@ _SIGNATURES = {
                                    [_c_float, _c_int, _vp, _c_size, _vp]),
     "agent_attn_forward_module": (_c_int, [_vp] * 9 + [_c_int] * 6 + [_c_float, _c_int, _vp,
                                                                        _c_size, _vp]),
+    "agent_attn_module_workspace_bytes": (_c_size, [_c_int] * 7),
+    "agent_attn_module_forward": (_c_int, [_vp] * 11 + [_c_int] * 6 + [_c_float, _c_int, _vp,
+                                                                        _c_size, _vp]),
     "agent_attn_backward_workspace_bytes": (_c_size, [_c_int] * 7),
     "agent_attn_backward": (_c_int, [_vp] * 9 + [_c_int] * 6 + [_c_float, _c_int, _vp, _c_size,
                                                                  _vp]),
@@ -271,6 +274,66 @@ def agent_attn_forward_module(q, k, v, grid_hw, s, scale=None, agents=None, bias
                                          _ptr(bias_agg), _ptr(bias_bcast), _ptr(dwc_weight),
                                          _ptr(dwc_bias), B, H, h, w, d, int(s), float(scale),
                                          code, ws_ptr, ws_size, _stream(q.device))
+    _check(rc)
+    return out
+
+
+def agent_attn_module_forward(x, w_qkv, grid_hw, s, num_heads, scale=None, b_qkv=None,
+                              w_out=None, b_out=None, agents=None, bias_agg=None,
+                              bias_bcast=None, dwc_weight=None, dwc_bias=None, out=None,
+                              workspace=None):
+    """The attention module on token features x [B, h*w, C]: q, k, v = x
+    w_qkv^T + b_qkv (order q, k, v; H = num_heads heads of d = C / H
+    channels), agent attention with the optional module terms, y = o w_out^T
+    + b_out (y = o, heads side by side, without w_out).  Weights in the
+    Linear layout [out, in] and x's dtype; biases float32.  Returns y
+    [B, h*w, C]; runs on torch's current stream."""
+    L = lib()
+    _dev_tensor(x, "x", ndim=3)
+    B, N, C = x.shape
+    H = int(num_heads)
+    if H < 1 or C % H:
+        raise ValueError(f"C={C} is not a multiple of num_heads={H}")
+    d = C // H
+    h, w = (int(t) for t in grid_hw)
+    if h * w != N:
+        raise ValueError(f"grid {h}x{w} does not match N={N}")
+    k_ag = int(s) * int(s)
+    _dev_tensor(w_qkv, "w_qkv", ndim=2)
+    _same(x, w_qkv, "w_qkv", (3 * C, C), x.dtype)
+    if w_out is not None:
+        _dev_tensor(w_out, "w_out", ndim=2)
+        _same(x, w_out, "w_out", (C, C), x.dtype)
+    if agents is not None:
+        _dev_tensor(agents, "agents")
+        _same(x, agents, "agents", (B, H, k_ag, d), x.dtype)
+    shapes = {"b_qkv": (3 * C,), "b_out": (C,), "bias_agg": (H, k_ag, N),
+              "bias_bcast": (H, N, k_ag), "dwc_weight": (H * d, 3, 3), "dwc_bias": (H * d,)}
+    params = {"b_qkv": b_qkv, "b_out": b_out, "bias_agg": bias_agg, "bias_bcast": bias_bcast,
+              "dwc_weight": dwc_weight, "dwc_bias": dwc_bias}
+    for name, t in params.items():
+        if t is None:
+            continue
+        _dev_tensor(t, name, ndim=len(shapes[name]))
+        _same(x, t, name, shapes[name], torch.float32)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(x)
+    else:
+        _dev_tensor(out, "out", ndim=3)
+        _same(x, out, "out", x.shape, x.dtype)
+    code = _dtype_code(x)
+    with torch.cuda.device(x.device):
+        need = L.agent_attn_module_workspace_bytes(B, H, h, w, d, int(s), code)
+        if workspace is None:   # leading synchronisation bytes zero, as the call leaves them
+            workspace = cached_workspace(x.device, max(1, need))
+        ws_size = workspace.numel() * workspace.element_size()
+        rc = L.agent_attn_module_forward(
+            _ptr(x), _ptr(w_qkv), _ptr(b_qkv), _ptr(w_out), _ptr(b_out), _ptr(agents),
+            _ptr(bias_agg), _ptr(bias_bcast), _ptr(dwc_weight), _ptr(dwc_bias), _ptr(out),
+            B, H, h, w, d, int(s), float(scale), code, _ptr(workspace), ws_size,
+            _stream(x.device))
     _check(rc)
     return out
 

@@ -14,7 +14,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libagent_attn.so")
 SOURCES = (["agent_attn.hip"] + [f"mfma_dc{dc}_{t}.hip" for dc in (1, 2, 4)
                                 for t in ("bf16", "f16")]
-           + [f"bwd_mfma_{t}.hip" for t in ("bf16", "f16")])
+           + [f"bwd_mfma_{t}.hip" for t in ("bf16", "f16")] + ["proj.hip"])
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 COMPILE_FLAGS = [

@@ -20,6 +20,7 @@
 #include "kernels_backward.hpp"
 #include "kernels_gemm.hpp"
 #include "kernels_bwd_mfma.hpp"
+#include "kernels_proj.hpp"
 
 namespace {
 
@@ -997,6 +998,24 @@ int run_backward_mfma(const Dims& D, const MfmaBwdPlan& P, const void* q, const 
   return AGENT_ATTN_OK;
 }
 
+// Workspace of the module with projections: the attention's own workspace
+// first (so that the leading synchronisation bytes are the same as
+// agent_attn_forward_ws's), then q, k, v [3][B, H, N, d] and o [B, H, N, d]
+// in the tensors' format.
+struct ModulePlan {
+  size_t off_attn = 0, attn_bytes = 0, off_qkv = 0, off_o = 0, bytes = 0;
+};
+
+ModulePlan make_module_plan(const Dims& D) {
+  ModulePlan P;
+  const size_t t = (size_t)D.BH * D.N * D.d * elem_size(D.dtype);
+  P.attn_bytes = make_plan(D, device_cus()).bytes;
+  P.off_qkv = align_up(P.attn_bytes, 256);
+  P.off_o = align_up(P.off_qkv + 3 * t, 256);
+  P.bytes = P.off_o + t;
+  return P;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1039,6 +1058,103 @@ int agent_attn_forward_module(const void* q, const void* k, const void* v, void*
   mt.dwc_b = dwc_bias;
   return forward_ws(q, k, v, out, agents, B, H, h, w, d, s, scale, dtype, workspace,
                     workspace_bytes, stream, nullptr, mt);
+}
+
+size_t agent_attn_module_workspace_bytes(int B, int H, int h, int w, int d, int s, int dtype) {
+  Dims D;
+  if (check_grid(D, B, H, h, w, d, s, dtype)) return 0;
+  if (D.BH == 0) return 0;
+  return make_module_plan(D).bytes;
+}
+
+int agent_attn_module_forward(const void* x, const void* w_qkv, const float* b_qkv,
+                              const void* w_out, const float* b_out, const void* agents,
+                              const float* bias_agg, const float* bias_bcast,
+                              const float* dwc_weight, const float* dwc_bias, void* y, int B,
+                              int H, int h, int w, int d, int s, float scale, int dtype,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  Dims D;
+  int rc = check_grid(D, B, H, h, w, d, s, dtype);
+  if (rc) return rc;
+  rc = check_scale(scale);
+  if (rc) return rc;
+  if (D.BH == 0) return AGENT_ATTN_OK;
+  if (!x || !w_qkv || !y) return fail(AGENT_ATTN_ERR_NULL, "x, w_qkv and y must be non-NULL");
+  const long C = (long)H * d, M = (long)B * D.N;
+  if (M * C * 4 >= (1L << 31) || 3 * C * C * 4 >= (1L << 31))
+    return fail(AGENT_ATTN_ERR_UNSUPPORTED,
+                "the projections take B*N*C*4 and 3*C*C*4 below 2^31 bytes (C = H*d = %ld)", C);
+  if (misaligned(x) || misaligned(w_qkv) || misaligned(w_out) || misaligned(y) ||
+      misaligned(agents))
+    return fail(AGENT_ATTN_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  if (((uintptr_t)b_qkv & 3u) || ((uintptr_t)b_out & 3u))
+    return fail(AGENT_ATTN_ERR_ALIGN, "biases must be 4-byte aligned");
+  const size_t es = elem_size(dtype);
+  const size_t xb = (size_t)(M * C) * es, wqb = (size_t)(3 * C * C) * es, wob = (size_t)(C * C) * es;
+  const size_t ab = (size_t)D.BH * D.nag * d * es;
+  const void* ins[5] = {x, w_qkv, w_out, agents, nullptr};
+  const size_t insz[5] = {xb, wqb, wob, ab, 0};
+  const void* bs[2] = {b_qkv, b_out};
+  const size_t bsz[2] = {(size_t)(3 * C) * 4, (size_t)C * 4};
+  for (int i = 0; i < 4; ++i)
+    if (ins[i] && ranges_overlap(y, xb, ins[i], insz[i]))
+      return fail(AGENT_ATTN_ERR_ALIAS, "y overlaps an input");
+  for (int i = 0; i < 2; ++i)
+    if (bs[i] && ranges_overlap(y, xb, bs[i], bsz[i]))
+      return fail(AGENT_ATTN_ERR_ALIAS, "y overlaps a bias");
+  const ModulePlan P = make_module_plan(D);
+  if (!workspace || workspace_bytes < P.bytes)
+    return fail(AGENT_ATTN_ERR_WORKSPACE, "workspace of %zu bytes at %p; %zu bytes needed",
+                workspace_bytes, workspace, P.bytes);
+  if (((uintptr_t)workspace & 255u) != 0)
+    return fail(AGENT_ATTN_ERR_ALIGN, "workspace must be 256-byte aligned");
+  if (ranges_overlap(workspace, P.bytes, y, xb))
+    return fail(AGENT_ATTN_ERR_ALIAS, "workspace overlaps y");
+  for (int i = 0; i < 4; ++i)
+    if (ins[i] && ranges_overlap(workspace, P.bytes, ins[i], insz[i]))
+      return fail(AGENT_ATTN_ERR_ALIAS, "workspace overlaps an input");
+  for (int i = 0; i < 2; ++i)
+    if (bs[i] && ranges_overlap(workspace, P.bytes, bs[i], bsz[i]))
+      return fail(AGENT_ATTN_ERR_ALIAS, "workspace overlaps a bias");
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const size_t t = (size_t)D.BH * D.N * d * es;
+  char* q = ws + P.off_qkv;
+  char* o = ws + P.off_o;
+  aa::pj::ProjParams pp{};
+  pp.x = x;
+  pp.w = w_qkv;
+  pp.bias = b_qkv;
+  pp.y = q;
+  pp.M = (int)M;
+  pp.C = (int)C;
+  pp.Nout = (int)(3 * C);
+  pp.N = (int)D.N;
+  pp.H = H;
+  pp.d = d;
+  int e = aa::pj::launch_proj(pp, 0, dtype, st);
+  if (e) return hip_fail((hipError_t)e, "q, k, v projection launch");
+  ModTerms mt;
+  mt.bias_agg = bias_agg;
+  mt.bias_bcast = bias_bcast;
+  mt.dwc_w = dwc_weight;
+  mt.dwc_b = dwc_bias;
+  rc = forward_ws(q, q + t, q + 2 * t, o, agents, B, H, h, w, d, s, scale, dtype,
+                  ws + P.off_attn, P.attn_bytes, stream, nullptr, mt);
+  if (rc) return rc;
+  if (w_out) {
+    pp.x = o;
+    pp.w = w_out;
+    pp.bias = b_out;
+    pp.y = y;
+    pp.Nout = (int)C;
+    e = aa::pj::launch_proj(pp, 1, dtype, st);
+    if (e) return hip_fail((hipError_t)e, "output projection launch");
+  } else {
+    e = aa::pj::launch_heads_concat(o, y, (int)M, (int)D.N, H, d, dtype, st);
+    if (e) return hip_fail((hipError_t)e, "head concatenation launch");
+  }
+  return AGENT_ATTN_OK;
 }
 
 int agent_attn_forward(const void* q, const void* k, const void* v, void* out,

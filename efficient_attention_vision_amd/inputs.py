@@ -191,3 +191,30 @@ def make_module_terms(wl: Workload, seed: int, terms=("bias_agg", "bias_bcast", 
             "bias_bcast": b2 if "bias_bcast" in terms else None,
             "dwc_weight": w if "dwc" in terms else None,
             "dwc_bias": b if "dwc" in terms else None}
+
+
+@dataclasses.dataclass
+class ModuleInputs:
+    """Token features and projection parameters of the attention module."""
+    X: Operand            # [B, N, C], C = H d
+    W_qkv: Operand        # [3C, C] (Linear layout [out, in])
+    b_qkv: np.ndarray     # float32 [3C]
+    W_out: Operand        # [C, C]
+    b_out: np.ndarray     # float32 [C]
+
+
+def make_module_inputs(wl: Workload, seed: int) -> ModuleInputs:
+    """X ~ N(0, 1); weights ~ N(0, 1/C) (so that q, k, v and y are of order
+    one); biases ~ N(0, 0.1^2).  Drawn in the order X, W_qkv, b_qkv, W_out,
+    b_out from PCG64(seed + 104729), in float32, then rounded to the
+    workload's format (biases stay float32)."""
+    rng = np.random.Generator(np.random.PCG64(seed + 104729))
+    C = wl.H * wl.d
+    x = rng.standard_normal((wl.B, wl.N, C), dtype=np.float32)
+    sd = np.float32(1.0 / math.sqrt(C))
+    wqkv = rng.standard_normal((3 * C, C), dtype=np.float32) * sd
+    bqkv = rng.standard_normal(3 * C, dtype=np.float32) * np.float32(0.1)
+    wout = rng.standard_normal((C, C), dtype=np.float32) * sd
+    bout = rng.standard_normal(C, dtype=np.float32) * np.float32(0.1)
+    return ModuleInputs(_pack(x, wl.dtype), _pack(wqkv, wl.dtype), bqkv, _pack(wout, wl.dtype),
+                        bout)

@@ -160,6 +160,50 @@ int agent_attn_forward_module(const void* q, const void* k, const void* v,
                               float scale, int dtype, void* workspace,
                               size_t workspace_bytes, void* stream);
 
+/* Scratch bytes agent_attn_module_forward needs for these sizes (0 for
+ * invalid sizes or an empty batch). */
+size_t agent_attn_module_workspace_bytes(int B, int H, int h, int w, int d,
+                                         int s, int dtype);
+
+/* The attention module on token features (sources: "Agent Attention: On the
+ * Integration of Softmax and Linear Attention", §3 Preliminaries: the
+ * projections W_Q, W_K, W_V map channels to per-head queries, keys and
+ * values; §4: agent attention with the module terms; "别再死磕Softmax了！…",
+ * coreui.cn, §3.1: AgentAttention(dim, num_heads, num_agents) maps
+ * [B, N, dim] to [B, N, dim]):
+ *   q, k, v = x w_qkv^T + b_qkv   (the 3C outputs in the order q, k, v; each
+ *                                  read as H heads of d channels, feature
+ *                                  h*d + c = channel c of head h)
+ *   o       = agent_attn_forward_module(q, k, v, agents, module terms)
+ *   y       = o w_out^T + b_out   (o as [B, N, C], heads side by side)
+ * with C = H*d and N = h*w:
+ *   x      : [B, N, C] of dtype;
+ *   w_qkv  : [3C, C] of dtype (Linear layout [out, in]); b_qkv: NULL or
+ *            float32 [3C];
+ *   w_out  : NULL (y = o) or [C, C] of dtype; b_out: NULL or float32 [C];
+ *   agents, bias_agg, bias_bcast, dwc_weight, dwc_bias: as
+ *            agent_attn_forward_module;
+ *   y      : [B, N, C] of dtype.
+ * q, k, v and o are held in dtype inside the workspace (as the outputs of
+ * Linear layers of that format are); products accumulate in float32 and each
+ * result is rounded once.  Tensor pointers 16-byte aligned, biases 4-byte
+ * aligned (AGENT_ATTN_ERR_ALIGN); y may not overlap an input nor the
+ * workspace any argument (AGENT_ATTN_ERR_ALIAS); B*N*C*4 and 3*C*C*4 below
+ * 2^31 bytes (AGENT_ATTN_ERR_UNSUPPORTED).  workspace: at least
+ * agent_attn_module_workspace_bytes(...) bytes, 256-byte aligned, whose
+ * first AGENT_ATTN_SYNC_BYTES bytes must be zero before its first use and
+ * are left zero by every call (as for agent_attn_forward_ws).  Other
+ * validation and errors as agent_attn_forward_ws; the call allocates
+ * nothing. */
+int agent_attn_module_forward(const void* x, const void* w_qkv,
+                              const float* b_qkv, const void* w_out,
+                              const float* b_out, const void* agents,
+                              const float* bias_agg, const float* bias_bcast,
+                              const float* dwc_weight, const float* dwc_bias,
+                              void* y, int B, int H, int h, int w, int d,
+                              int s, float scale, int dtype, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
 /* Scratch bytes agent_attn_backward needs for these sizes (0 for invalid
  * sizes or an empty batch). */
 size_t agent_attn_backward_workspace_bytes(int B, int H, int h, int w, int d,
@@ -176,8 +220,12 @@ size_t agent_attn_backward_workspace_bytes(int B, int H, int h, int w, int d,
  *                or the caller's agents [B, H, s*s, d], whose gradient goes
  *                to dagents [B, H, s*s, d] of dtype (required then, else
  *                ignored).
- * The forward is recomputed inside (nothing is saved between the calls);
- * arithmetic is float32.  workspace: at least
+ * The forward is recomputed inside (nothing is saved between the calls).
+ * Arithmetic: float32 for float32 tensors and for more than 64 agents; for
+ * 16-bit tensors with up to 64 agents, matrix-core products accumulating in
+ * float32 whose non-exact operands (agents, V_A, dV_A, probabilities, score
+ * gradients) enter as pairs of 16-bit values where rounding would cancel.
+ * workspace: at least
  * agent_attn_backward_workspace_bytes(...) bytes, 256-byte aligned, contents
  * free.  Outputs may not overlap any argument, nor the workspace any tensor
  * (AGENT_ATTN_ERR_ALIAS).  Validation and errors otherwise as

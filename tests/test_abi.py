@@ -192,6 +192,38 @@ def test_module_forward_validates_its_parameters(L):
     assert modfwd(L, wb=ctypes.c_void_p(P[3].value + 64), ws_bytes=10) == ERR_WS
 
 
+# ------------------------------------------------ module with projections
+
+def projfwd(L, *, x=P[0], wqkv=P[1], bqkv=None, wout=None, bout=None, y=P[3], B=2, H=2, h=8,
+            w=8, d=32, s=4, scale=0.125, dtype=1, ws=WS, ws_bytes=1 << 40):
+    return L.agent_attn_module_forward(x, wqkv, bqkv, wout, bout, None, None, None, None, None,
+                                       y, B, H, h, w, d, s, scale, dtype, ws, ws_bytes, None)
+
+
+def test_projection_module_validation(L):
+    """The module with projections checks its own tensors on the host:
+    x [B, N, C] and y [B, N, C] with C = H d, weights, float32 biases."""
+    assert L.agent_attn_module_workspace_bytes(2, 2, 8, 8, 32, 4, 1) > 0
+    assert L.agent_attn_module_workspace_bytes(2, 2, 8, 8, 12, 4, 1) == 0
+    assert projfwd(L, x=None) == ERR_NULL
+    assert projfwd(L, wqkv=None) == ERR_NULL
+    assert projfwd(L, y=None) == ERR_NULL
+    assert projfwd(L, x=ctypes.c_void_p(P[0].value + 8)) == ERR_ALIGN
+    assert projfwd(L, wout=ctypes.c_void_p(P[2].value + 4)) == ERR_ALIGN
+    assert projfwd(L, bqkv=ctypes.c_void_p(P[5].value + 2)) == ERR_ALIGN
+    # y [2, 64, 64] bf16 covers 16 KiB from P3: an input starting inside it aliases
+    assert projfwd(L, x=ctypes.c_void_p(P[3].value + 4096)) == ERR_ALIAS
+    assert projfwd(L, bout=ctypes.c_void_p(P[3].value + 64)) == ERR_ALIAS
+    assert projfwd(L, ws=ctypes.c_void_p(P[3].value + 256)) == ERR_ALIAS
+    assert projfwd(L, ws=None) == ERR_WS
+    assert projfwd(L, ws_bytes=100) == ERR_WS
+    assert projfwd(L, d=12) == ERR_UNSUP
+    assert projfwd(L, scale=-1.0) == ERR_SCALE
+    assert projfwd(L, dtype=9) == ERR_DTYPE
+    # 3 C^2 * 4 bytes of weights past 2^31 (C = 16 * 128 * 8)
+    assert projfwd(L, H=16 * 8, d=128) == ERR_UNSUP
+
+
 # ---------------------------------------------------------------- backward
 
 def bwd(L, *, q=P[0], k=P[1], v=P[2], dout=P[3], agents=None, dq=P[4], dk=P[5], dv=P[6],

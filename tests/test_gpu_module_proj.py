@@ -1,0 +1,81 @@
+"""The attention module with its projections (agent_attn_module_forward) on
+the GPU against the float64 oracle's module_forward.
+
+x [B, N, C] -> q, k, v projections (head-major layouts written by the
+projection epilogue) -> agent attention with the module terms -> output
+projection (or the heads side by side).  Cases: the workloads' channel
+counts (C = 64, 384, 320), a ragged grid with token and feature tails
+(C = 48), float32 / bfloat16 / float16, supplied agents, no output
+projection, no module terms.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import efficient_attention_vision_amd as eav
+from efficient_attention_vision_amd import inputs
+from tests import parity
+from tests.gpu_util import f64_to_device, say, to_device, to_host_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def run_proj(wl, seed, out_proj=True, terms=("bias_agg", "bias_bcast", "dwc")):
+    say(f"[module+proj] {wl.name} B={wl.B} H={wl.H} grid={wl.h}x{wl.w} d={wl.d} s={wl.s} "
+        f"{wl.dtype} seed={seed} out_proj={out_proj} terms={','.join(terms) or '-'}")
+    mi = inputs.make_module_inputs(wl, seed)
+    mt = inputs.make_module_terms(wl, seed, terms)
+    agents = inputs.make_inputs(wl, seed).A if wl.supplied_agents else None
+    x, wqkv, wout = (to_device(t) for t in (mi.X, mi.W_qkv, mi.W_out))
+    bq, bo = f64_to_device(mi.b_qkv), f64_to_device(mi.b_out)
+    a = to_device(agents) if agents is not None else None
+    dev = {n: (None if t is None else f64_to_device(t)) for n, t in mt.items()}
+    y = eav.agent_attn_module_forward(x, wqkv, (wl.h, wl.w), wl.s, wl.H, wl.scale, b_qkv=bq,
+                                      w_out=wout if out_proj else None,
+                                      b_out=bo if out_proj else None, agents=a, **dev)
+    torch.cuda.synchronize()
+    assert eav.agent_attn_read_faults() == 0
+    ref = oracle.module_forward(mi.X.exact, mi.W_qkv.exact, mi.b_qkv,
+                                mi.W_out.exact if out_proj else None,
+                                mi.b_out if out_proj else None, wl.H, wl.h, wl.w, wl.s,
+                                wl.scale, wl.dtype,
+                                A=None if agents is None else agents.exact, **mt)
+    got = to_host_f64(y)
+    a_err, r_err = parity.errors(got, ref)
+    say(f"       max-abs {a_err:.3e}  relative {r_err:.3e}  max|y| {np.abs(ref).max():.2f}")
+    parity.assert_close(got, ref, wl.dtype, wl.name, kind="discriminating")
+
+
+def _f(wl, dtype):
+    return dataclasses.replace(wl, name=f"{wl.name}_{dtype}", dtype=dtype)
+
+
+PVT = dataclasses.replace(inputs.WORKLOADS["pvt_stage1"], B=4, name="pvt_stage1_b4")
+CASES = [
+    PVT,
+    _f(PVT, "f16"),
+    dataclasses.replace(inputs.WORKLOADS["deit_s"], B=8, name="deit_s_b8"),
+    dataclasses.replace(inputs.WORKLOADS["sd_unet"], B=1, name="sd_unet_b1"),
+    inputs.custom("proj_ragged_9x7_d24", B=3, H=2, h=9, w=7, d=24, s=3),
+    inputs.custom("proj_f32", B=2, H=2, h=8, w=8, d=32, s=4, dtype="f32"),
+    inputs.custom("proj_f32_ragged", B=1, H=3, h=7, w=5, d=40, s=2, dtype="f32"),
+    inputs.custom("proj_supplied", B=2, H=2, h=10, w=10, d=64, s=4, supplied_agents=True),
+]
+
+
+@pytest.mark.parametrize("wl", CASES, ids=lambda w: w.name)
+def test_module_with_projections(wl):
+    run_proj(wl, 90)
+
+
+@pytest.mark.parametrize("wl", [CASES[0], CASES[5]], ids=lambda w: w.name)
+def test_module_without_output_projection(wl):
+    run_proj(wl, 91, out_proj=False)
+
+
+@pytest.mark.parametrize("wl", [CASES[2], CASES[4]], ids=lambda w: w.name)
+def test_module_projections_only(wl):
+    run_proj(wl, 92, terms=())
