@@ -1081,9 +1081,10 @@ int agent_attn_module_forward(const void* x, const void* w_qkv, const float* b_q
   if (D.BH == 0) return AGENT_ATTN_OK;
   if (!x || !w_qkv || !y) return fail(AGENT_ATTN_ERR_NULL, "x, w_qkv and y must be non-NULL");
   const long C = (long)H * d, M = (long)B * D.N;
-  if (M * C * 4 >= (1L << 31) || 3 * C * C * 4 >= (1L << 31))
+  if (M * C * 4 >= (1L << 31) || 3 * C * C * 4 >= (1L << 31) || (M + 127) / 128 > 65535)
     return fail(AGENT_ATTN_ERR_UNSUPPORTED,
-                "the projections take B*N*C*4 and 3*C*C*4 below 2^31 bytes (C = H*d = %ld)", C);
+                "the projections take B*N*C*4 and 3*C*C*4 below 2^31 bytes and B*N below "
+                "2^23 tokens (C = H*d = %ld)", C);
   if (misaligned(x) || misaligned(w_qkv) || misaligned(w_out) || misaligned(y) ||
       misaligned(agents))
     return fail(AGENT_ATTN_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
