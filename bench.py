@@ -40,12 +40,16 @@ PMC_CMD = ("timeout -s KILL 120 rocprofv3 --pmc {c} --output-format csv -d $R/gp
 
 
 def kernel_sources_sha256() -> str:
-    """Hash of the HIP sources and the ABI header: HBM counters taken on an
-    older kernel are not reported."""
+    """Hash of the sources the forward's fused kernel is built and launched
+    from (its kernels, their instances, the host library that plans its
+    launches, the ABI header): HBM counters taken on an older kernel are not
+    reported."""
     import glob
     import hashlib
     h = hashlib.sha256()
-    files = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.hpp")))
+    files = sorted([os.path.join(CSRC, n) for n in ("common.hpp", "kernels_mfma.hpp",
+                                                     "agent_attn.hip")]
+                   + glob.glob(os.path.join(CSRC, "mfma_dc*.hip")))
     files.append(os.path.join(ROOT, "include", "agent_attn.h"))
     for f in files:
         h.update(os.path.basename(f).encode())
