@@ -207,6 +207,50 @@ def write_trace_summary(wl, trace_dir):
     print(path)
 
 
+PASS_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/{d}_{w} -o run "
+            "-- python3 $R/bench.py --workload {w} --no-cpu-baseline --{m} --steps 20 --warmup 2")
+PASS_NAMES = {"backward": ("bwd_passes", "ktb"), "projections": ("module_projections", "ktp")}
+
+
+def write_passes_summary(wl, mode, trace_dir):
+    """profiles/<path>_<workload>_kernel_trace.md: the library's kernels of a
+    multi-launch path (the backward, or the module with projections), from a
+    rocprofv3 --kernel-trace --stats run of this benchmark in that mode."""
+    import csv
+    name, tag = PASS_NAMES[mode]
+    stats = list(csv.DictReader(open(os.path.join(trace_dir, "run_kernel_stats.csv"))))
+    ours = [r for r in stats if "aa::" in r["Name"]]
+    rows = [
+        f"# Kernel trace: {mode} path, workload {wl.name}",
+        "",
+        f"Workload: B={wl.B} H={wl.H} grid {wl.h}x{wl.w} (N={wl.N}) d={wl.d} k={wl.k} {wl.dtype}.",
+        "Command (from /tmp with TMPDIR=/tmp, R = repository root):",
+        "",
+        "    " + PASS_CMD.format(d=tag, w=wl.name, m=mode),
+        f"    python3 bench.py --workload {wl.name} --passes-summary {mode} "
+        f"$R/gpurun_out/{tag}_{wl.name}",
+        "",
+        "The run makes 2 warm-up steps, 20 event-bracketed eager steps, then a graph of 20",
+        "steps replayed twice; every kernel below runs once per step.",
+        "",
+        "| kernel | calls | average us | min us | max us |",
+        "|---|---|---|---|---|",
+    ]
+    total = 0.0
+    for r in ours:
+        nm = r["Name"].split("(")[0].replace("void ", "")
+        nm = nm if len(nm) < 70 else nm[:67] + "..."
+        avg = float(r["AverageNs"]) / 1e3
+        total += avg
+        rows.append(f"| `{nm}` | {r['Calls']} | {avg:.1f} | {int(r['MinNs']) / 1e3:.1f} | "
+                    f"{int(r['MaxNs']) / 1e3:.1f} |")
+    rows += ["", f"- sum of the average kernel durations (one step): {total:.1f} us"]
+    path = os.path.join(PROFILES, f"{name}_{wl.name}_kernel_trace.md")
+    with open(path, "w") as fh:
+        fh.write("\n".join(rows) + "\n")
+    print(path)
+
+
 def algorithmic_bytes(wl) -> int:
     """Q, K, V read once and O written once (plus caller agents read once)."""
     b = 4 * wl.B * wl.H * wl.N * wl.d * wl.es
@@ -302,10 +346,21 @@ def main():
                     help="write the HBM counter summary of --workload from four rocprofv3 --pmc "
                          "output folders (kernel FETCH_SIZE, kernel WRITE_SIZE, copy FETCH_SIZE, "
                          "copy WRITE_SIZE) and exit")
+    ap.add_argument("--passes-summary", nargs=2, metavar=("MODE", "DIR"),
+                    help="write the kernel-trace summary of the backward ('backward') or the "
+                         "module with projections ('projections') of --workload from a "
+                         "rocprofv3 --kernel-trace --stats output folder and exit")
     ap.add_argument("--trace-summary", metavar="DIR",
                     help="write the kernel-trace summary of --workload from a rocprofv3 "
                          "--kernel-trace --stats output folder and exit")
     args = ap.parse_args()
+    if args.passes_summary:
+        from efficient_attention_vision_amd import inputs
+        mode, folder = args.passes_summary
+        if mode not in PASS_NAMES:
+            sys.exit(f"bench.py: --passes-summary takes one of {sorted(PASS_NAMES)}")
+        write_passes_summary(inputs.WORKLOADS[args.workload], mode, folder)
+        return
     if args.pmc_summary or args.trace_summary:
         from efficient_attention_vision_amd import inputs
         wl = inputs.WORKLOADS[args.workload]
