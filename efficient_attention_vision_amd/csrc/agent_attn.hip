@@ -11,6 +11,7 @@
 #include <cstdio>
 #include <mutex>
 #include <string>
+#include <type_traits>
 #include <vector>
 
 #include "agent_attn.h"
@@ -19,6 +20,7 @@
 #include "kernels_scalar.hpp"
 #include "kernels_backward.hpp"
 #include "kernels_gemm.hpp"
+#include "kernels_gemm_mfma.hpp"
 #include "kernels_bwd_mfma.hpp"
 #include "kernels_proj.hpp"
 
@@ -788,14 +790,24 @@ BwdPlan make_bwd_plan(const Dims& D) {
 
 // part = alpha * A B for every head (M x N results, contraction K), split
 // over K in chunks of kchunk (splits = ceil(K / kchunk)).
+// With 16-bit tensors (mfma) the products of two float32 operands (dQ, dK,
+// dV: contraction over the agents) run on matrix cores with bf16 operand
+// pairs (bgemm_mfma, about 2^-16 per term), 1.7x faster at 256 agents; the
+// others are bound by the memory traffic of the probability matrices and
+// measured no faster there, so they keep the float32 FMA kernel, as do
+// float32 tensors.
 template <typename TA, typename TB>
 int launch_bgemm(const aa::MatRef& A, const aa::MatRef& B, float* part, int M, int N, int K,
-                 int kchunk, long batch, float alpha, hipStream_t st) {
+                 int kchunk, long batch, float alpha, hipStream_t st, bool mfma) {
   const int splits = (K + kchunk - 1) / kchunk;
   const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 63) / 64),
                   (unsigned)(batch * splits));
-  hipLaunchKernelGGL((aa::bgemm_f32<TA, TB>), grid, dim3(256), 0, st, A, B, part, M, N, K, kchunk,
-                     splits, batch, alpha);
+  if (mfma && std::is_same<TA, float>::value && std::is_same<TB, float>::value)
+    hipLaunchKernelGGL((aa::bgemm_mfma<TA, TB>), grid, dim3(256), 0, st, A, B, part, M, N, K,
+                       kchunk, splits, batch, alpha);
+  else
+    hipLaunchKernelGGL((aa::bgemm_f32<TA, TB>), grid, dim3(256), 0, st, A, B, part, M, N, K,
+                       kchunk, splits, batch, alpha);
   AA_LAUNCH_CHECK("backward product launch");
   return AGENT_ATTN_OK;
 }
@@ -837,62 +849,84 @@ int run_backward(const Dims& D, const BwdPlan& P, const void* q, const void* k, 
   const aa::MatRef dS1m{dS1, kk * N, N, 1}, dS1T{dS1, kk * N, 1, N}, P1m{P1, kk * N, N, 1},
       P1T{P1, kk * N, 1, N};
   const int KN = kBwdSplit, KALL = 1 << 30;   // split over tokens / no split
+  const bool mm = !std::is_same<T, float>::value;   // 16-bit tensors: matrix-core products
   const long nkd = BH * kk * d;
   // forward quantities: agents; P1 = softmax(scale A K^T); V_A = P1 V
   int rc = agents ? launch_widen<T>(D, agents, A, st) : launch_pool<T>(D, q, A, st);
   if (rc) return rc;
-  if ((rc = launch_bgemm<float, T>(Am, KmT, P1, (int)kk, (int)N, (int)d, KALL, BH, 1.f, st)))
+  if ((rc = launch_bgemm<float, T>(Am, KmT, P1, (int)kk, (int)N, (int)d, KALL, BH, 1.f, st, mm)))
     return rc;
   hipLaunchKernelGGL(aa::row_softmax_log2, dim3((unsigned)(BH * kk)), dim3(256), 0, st, P1,
                      (int)N, sl2);
   AA_LAUNCH_CHECK("backward aggregation probabilities launch");
-  if ((rc = launch_bgemm<float, T>(P1m, Vm, part, (int)kk, (int)d, (int)N, KN, BH, 1.f, st)))
+  if ((rc = launch_bgemm<float, T>(P1m, Vm, part, (int)kk, (int)d, (int)N, KN, BH, 1.f, st, mm)))
     return rc;
   if ((rc = launch_sum_splits(part, VA, nkd, P.splits, 1.f, 0, st))) return rc;
   // P2 = softmax(scale Q A^T)
-  if ((rc = launch_bgemm<T, float>(Qm, AmT, P2, (int)N, (int)kk, (int)d, KALL, BH, 1.f, st)))
+  if ((rc = launch_bgemm<T, float>(Qm, AmT, P2, (int)N, (int)kk, (int)d, KALL, BH, 1.f, st, mm)))
     return rc;
   hipLaunchKernelGGL(aa::softmax_short, dim3((unsigned)((BH * N + 3) / 4)), dim3(256), 0, st, P2,
                      BH * N, (int)kk, sl2);
   AA_LAUNCH_CHECK("backward broadcast probabilities launch");
   // dV_A = P2^T dO
-  if ((rc = launch_bgemm<float, T>(P2T, dOm, part, (int)kk, (int)d, (int)N, KN, BH, 1.f, st)))
+  if ((rc = launch_bgemm<float, T>(P2T, dOm, part, (int)kk, (int)d, (int)N, KN, BH, 1.f, st, mm)))
     return rc;
   if ((rc = launch_sum_splits(part, dVA, nkd, P.splits, 1.f, 0, st))) return rc;
   // dS2 = P2 (dO V_A^T - rowsum)
-  if ((rc = launch_bgemm<T, float>(dOm, VAmT, dS2, (int)N, (int)kk, (int)d, KALL, BH, 1.f, st)))
+  if ((rc = launch_bgemm<T, float>(dOm, VAmT, dS2, (int)N, (int)kk, (int)d, KALL, BH, 1.f, st, mm)))
     return rc;
   hipLaunchKernelGGL(aa::softmax_grad_short, dim3((unsigned)((BH * N + 3) / 4)), dim3(256), 0, st,
                      P2, dS2, BH * N, (int)kk);
   AA_LAUNCH_CHECK("backward broadcast softmax gradient launch");
   // dQ = scale dS2 A;  dA = scale dS2^T Q
-  if ((rc = launch_bgemm<float, float>(dS2m, Am, dQ, (int)N, (int)d, (int)kk, KALL, BH, scale,
-                                       st)))
+  if ((rc = launch_bgemm<float, float>(dS2m, Am, dQ, (int)N, (int)d, (int)kk, KALL, BH, scale, st, mm)))
     return rc;
-  if ((rc = launch_bgemm<float, T>(dS2T, Qm, part, (int)kk, (int)d, (int)N, KN, BH, 1.f, st)))
+  if ((rc = launch_bgemm<float, T>(dS2T, Qm, part, (int)kk, (int)d, (int)N, KN, BH, 1.f, st, mm)))
     return rc;
   if ((rc = launch_sum_splits(part, dA, nkd, P.splits, scale, 0, st))) return rc;
   // dS1 = P1 (dV_A V^T - rowsum)
-  if ((rc = launch_bgemm<float, T>(dVAm, VmT, dS1, (int)kk, (int)N, (int)d, KALL, BH, 1.f, st)))
+  if ((rc = launch_bgemm<float, T>(dVAm, VmT, dS1, (int)kk, (int)N, (int)d, KALL, BH, 1.f, st, mm)))
     return rc;
   hipLaunchKernelGGL(aa::softmax_grad_rows, dim3((unsigned)(BH * kk)), dim3(256), 0, st, P1, dS1,
                      (int)N);
   AA_LAUNCH_CHECK("backward aggregation softmax gradient launch");
   // dA += scale dS1 K;  dK = scale dS1^T A;  dV = P1^T dV_A
-  if ((rc = launch_bgemm<float, T>(dS1m, Km, part, (int)kk, (int)d, (int)N, KN, BH, 1.f, st)))
+  if ((rc = launch_bgemm<float, T>(dS1m, Km, part, (int)kk, (int)d, (int)N, KN, BH, 1.f, st, mm)))
     return rc;
   if ((rc = launch_sum_splits(part, dA, nkd, P.splits, scale, 1, st))) return rc;
-  if ((rc = launch_bgemm<float, float>(dS1T, Am, dK, (int)N, (int)d, (int)kk, KALL, BH, scale,
-                                       st)))
+  if ((rc = launch_bgemm<float, float>(dS1T, Am, dK, (int)N, (int)d, (int)kk, KALL, BH, scale, st, mm)))
     return rc;
-  if ((rc = launch_bgemm<float, float>(P1T, dVAm, dV, (int)N, (int)d, (int)kk, KALL, BH, 1.f,
-                                       st)))
+  if ((rc = launch_bgemm<float, float>(P1T, dVAm, dV, (int)N, (int)d, (int)kk, KALL, BH, 1.f, st, mm)))
     return rc;
-  // outputs in the tensors' type; dq with the pooling's share of dA
+  // outputs in the tensors' type; dq with the pooling's share of dA (16-bit
+  // tensors: the vectorised finish of the matrix-core path, one thread per
+  // 8 channels of a token)
   const long nnd = BH * N * d;
   const unsigned g_nd = (unsigned)std::min<long>((nnd + 255) / 256, 65536);
-  hipLaunchKernelGGL(aa::finish_dq<T>, dim3(g_nd), dim3(256), 0, st, dQ, agents ? nullptr : dA,
-                     (T*)dq, BH, (int)N, (int)d, (int)kk, D.h, D.w, D.s);
+  const int tiled = (D.h % D.s == 0 && D.w % D.s == 0) ? 1 : 0;
+  const unsigned g_fq = (unsigned)((N * (d / 8) + 255) / 256);
+  if constexpr (std::is_same<T, aa::bf16_t>::value) {
+    if (BH <= 65535)
+      hipLaunchKernelGGL(aa::bw::bwd_finish_dq<aa::ElemBF16>, dim3(g_fq, (unsigned)BH), dim3(256),
+                         0, st, dQ, agents ? nullptr : dA, (uint16_t*)dq, (int)N, D.h, D.w,
+                         (int)d, D.s, tiled);
+    else
+      hipLaunchKernelGGL(aa::finish_dq<T>, dim3(g_nd), dim3(256), 0, st, dQ,
+                         agents ? nullptr : dA, (T*)dq, BH, (int)N, (int)d, (int)kk, D.h, D.w,
+                         D.s);
+  } else if constexpr (std::is_same<T, aa::half_t>::value) {
+    if (BH <= 65535)
+      hipLaunchKernelGGL(aa::bw::bwd_finish_dq<aa::ElemF16>, dim3(g_fq, (unsigned)BH), dim3(256),
+                         0, st, dQ, agents ? nullptr : dA, (uint16_t*)dq, (int)N, D.h, D.w,
+                         (int)d, D.s, tiled);
+    else
+      hipLaunchKernelGGL(aa::finish_dq<T>, dim3(g_nd), dim3(256), 0, st, dQ,
+                         agents ? nullptr : dA, (T*)dq, BH, (int)N, (int)d, (int)kk, D.h, D.w,
+                         D.s);
+  } else {
+    hipLaunchKernelGGL(aa::finish_dq<T>, dim3(g_nd), dim3(256), 0, st, dQ, agents ? nullptr : dA,
+                       (T*)dq, BH, (int)N, (int)d, (int)kk, D.h, D.w, D.s);
+  }
   hipLaunchKernelGGL(aa::store_as<T>, dim3(g_nd), dim3(256), 0, st, dK, (T*)dk, nnd);
   hipLaunchKernelGGL(aa::store_as<T>, dim3(g_nd), dim3(256), 0, st, dV, (T*)dv, nnd);
   AA_LAUNCH_CHECK("backward output launch");
