@@ -513,10 +513,15 @@ def main():
     plain = (not args.module and not args.backward and args.layout == "bhnd"
              and wl.dtype in ("bf16", "f32"))
     traffic = measured_traffic(wl.name) if plain else None
-    # 16-bit tensors with up to 64 agents: token-tiled matrix-core passes,
-    # HBM-bound (about 1.7 k flop per byte); otherwise float32 products
-    mfma_bwd = args.backward and wl.dtype != "f32" and wl.k <= 64
-    if mfma_bwd:
+    # 16-bit tensors with up to 256 agents: token-tiled matrix-core passes, at
+    # 24 k / 14 flop per byte; above the ridge (2.5 PFLOP/s over 8 TB/s, about
+    # 180 agents) the matrix cores bound them; otherwise float32 products
+    mfma_bwd = args.backward and wl.dtype != "f32" and wl.k <= 256
+    ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if mfma_bwd and aflops / abytes > ridge:
+        roof = {"bound": "mfma", "achieved": achieved_tflops, "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved_tflops / BF16_PEAK_TFLOPS, "traffic": traffic}
+    elif mfma_bwd:
         roof = {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": traffic}
     elif args.backward:   # float32 vector arithmetic (no matrix cores)

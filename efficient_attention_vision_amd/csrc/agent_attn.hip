@@ -944,8 +944,9 @@ struct MfmaBwdPlan {
   bool use = false;
   int KT = 0, DT = 0;
   aa::bw::Pass pp[3];   // stats, bcast, agg
+  int nch = 1;           // chunks of 64 agents (more than 64 agents)
   size_t off_A = 0, off_VA = 0, off_dVA = 0, off_dA = 0, off_lse = 0, off_D1 = 0, off_dQ = 0,
-         off_part = 0, bytes = 0;
+         off_part = 0, off_tst = 0, off_dKf = 0, off_dVf = 0, bytes = 0;
 };
 
 // Workgroups per CU that the token-tiled passes aim for over the batch
@@ -965,14 +966,16 @@ aa::bw::Pass bwd_pass(const Dims& D, int cus, int step, int per_cu) {
 
 MfmaBwdPlan make_mfma_bwd_plan(const Dims& D, int cus) {
   MfmaBwdPlan P;
-  if (D.dtype == AGENT_ATTN_F32 || D.nag > 64 || D.d > 128) return P;
+  if (D.dtype == AGENT_ATTN_F32 || D.nag > 256 || D.d > 128) return P;
   if (D.BH * D.N * D.d >= (1L << 31)) return P;   // 32-bit element indices
   if (D.BH > 65535 || D.BH * D.nag * D.d * 8 >= (1L << 31)) return P;   // grid shapes
   P.KT = D.nag <= 32 ? 2 : 4;
   P.DT = D.d <= 32 ? 1 : D.d <= 64 ? 2 : 4;
+  P.nch = (D.nag + 63) / 64;
   P.pp[0] = bwd_pass(D, cus, aa::bw::kStatTok, AA_BWD_STATS_WPC);
   P.pp[1] = P.pp[2] = bwd_pass(D, cus, aa::bw::kStep, AA_BWD_TILE_WPC);
-  const size_t kd = (size_t)D.BH * D.nag * D.d * 4, kp = (size_t)D.BH * 16 * P.KT * 4;
+  const size_t kd = (size_t)D.BH * D.nag * D.d * 4,
+               kp = (size_t)D.BH * P.nch * 16 * P.KT * 4;
   const size_t nd = (size_t)D.BH * D.N * D.d * 4;
   size_t o = 0;
   auto take = [&](size_t b) {
@@ -987,7 +990,13 @@ MfmaBwdPlan make_mfma_bwd_plan(const Dims& D, int cus) {
   P.off_lse = take(kp);
   P.off_D1 = take(kp);
   P.off_dQ = take(nd);
-  P.off_part = take((size_t)aa::bw::part_floats(P.KT, P.DT, D.BH, P.pp) * 4);
+  P.off_part = take((size_t)aa::bw::part_floats(P.KT, P.DT, D.BH * P.nch, P.pp) * 4);
+  if (P.nch > 1) {
+    // per-token softmax statistics of every chunk; float32 sums of dk and dv
+    P.off_tst = take((size_t)P.nch * D.BH * D.N * 16);
+    P.off_dKf = take(nd);
+    P.off_dVf = take(nd);
+  }
   P.bytes = o;
   P.use = true;
   return P;
@@ -1024,6 +1033,15 @@ int run_backward_mfma(const Dims& D, const MfmaBwdPlan& P, const void* q, const 
   p.s = D.s;
   p.sl2 = scale * aa::kLog2e;
   p.scale = scale;
+  p.nch = P.nch;
+  p.chunk = 0;
+  p.a0 = 0;
+  p.nagc = D.nag;
+  if (P.nch > 1) {
+    p.tst = (float*)(ws + P.off_tst);
+    p.dKf = (float*)(ws + P.off_dKf);
+    p.dVf = (float*)(ws + P.off_dVf);
+  }
 #ifdef AGENT_ATTN_PHASE_TRACE
   p.trace = g_trace;
 #endif

@@ -102,10 +102,10 @@ struct BwdParams {
   uint16_t* dv;
   const float* A;         // agents [BH, nag, d]
   float* VA;              // V_A [BH, nag, d]
-  float* lse;             // [BH, KP]: log2 of the aggregation softmax denominators
+  float* lse;             // [BH, nch, KP]: log2 of the aggregation softmax denominators
   float* dVA;             // [BH, nag, d]
   float* dA;              // [BH, nag, d]
-  float* D1;              // [BH, KP]
+  float* D1;              // [BH, nch, KP]
   float* dQ;              // [BH, N, d] float32 (without the pooling share)
   float* part;            // workgroup partials of the current pass
   const uint16_t* agents_in;   // caller agents [BH, nag, d], or null (pool q)
@@ -113,6 +113,12 @@ struct BwdParams {
   uint16_t* dagents;      // gradient of the caller agents (with agents_in)
   int BH, N, d, nag;
   int h, w, s;            // token grid and agent grid side
+  // agent chunks (more than 64 agents: chunks of 64 run one launch each)
+  int nch, chunk;         // chunks per head, this launch's chunk
+  int a0, nagc;           // first agent and agent count of the chunk
+  float* tst;             // [nch, BH, N, 4]: max, sum, sum of P dP of a chunk per token
+  float* dKf;             // [BH, N, d] float32 sums over chunks of dk, dv (nch > 1)
+  float* dVf;
   int P, T;               // workgroups per head and tokens per workgroup of the pass
   float sl2, scale;       // scale * log2(e), scale
   long long* trace;       // phase timestamps (trace builds only)
@@ -298,8 +304,10 @@ __global__ void __launch_bounds__(kThr) bwd_stats_kernel(BwdParams p) {
     load_frags<DT>(vf[h], rv, tok, tok < t1, p.d, g);
   }
   BW_STAMP(0, 1);
-  stage_kd<El, C::KP, C::DP, C::RS, C::TS>(sAh, sAl, nullptr, nullptr,
-                                           p.A + (long)head * p.nag * p.d, p.nag, p.d, tid);
+  const long agl = ((long)head * p.nag + p.a0) * p.d;   // the chunk's first agent row
+  const long vh = (long)head * p.nch + p.chunk;            // (head, chunk)
+  stage_kd<El, C::KP, C::DP, C::RS, C::TS>(sAh, sAl, nullptr, nullptr, p.A + agl, p.nagc, p.d,
+                                           tid);
   __syncthreads();
   BW_STAMP(0, 2);
   float m[KT], ls[KT];
@@ -444,17 +452,17 @@ __global__ void __launch_bounds__(kThr) bwd_stats_kernel(BwdParams p) {
 #pragma unroll
     for (int kb = 0; kb < KT; ++kb) {
       const int a = 16 * kb + r;
-      if (a >= p.nag) continue;
-      if (g == 0) p.lse[(long)head * C::KP + a] = Mt[kb] + log2f(Lt[kb]);
+      if (a >= p.nagc) continue;
+      if (g == 0) p.lse[vh * C::KP + a] = Mt[kb] + log2f(Lt[kb]);
       const float inv = 1.0f / Lt[kb];
-      float* va = p.VA + ((long)head * p.nag + a) * p.d;
+      float* va = p.VA + agl + (long)a * p.d;
 #pragma unroll
       for (int db = 0; db < C::DB; ++db)
         if (16 * db + 4 * g < p.d)
           *reinterpret_cast<f32x4*>(va + 16 * db + 4 * g) = (U[kb][db] + *uaddr(1, kb, db)) * inv;
     }
   } else if (wave == 0) {
-    float* base = p.part + ((long)head * p.P + slot) * C::PART_STATS;
+    float* base = p.part + (vh * p.P + slot) * C::PART_STATS;
 #pragma unroll
     for (int kb = 0; kb < KT; ++kb) {
       const int a = 16 * kb + r;
@@ -514,13 +522,15 @@ __global__ void __launch_bounds__(256) bwd_stats_merge(BwdParams p) {
   using C = Geo<KT, DT>;
   int head, a, wave, lane;
   if (!red_item<WPA>(p, head, a, wave, lane)) return;
-  const float* base = p.part + (long)head * p.P * C::PART_STATS;
+  const int c = a / C::KP, al = a - c * C::KP;   // agent chunk and index within it
+  const long vh = (long)head * p.nch + c;
+  const float* base = p.part + vh * p.P * C::PART_STATS;
   float M = kNegBig;
-  for (int j = lane; j < p.P; j += 64) M = fmaxf(M, base[j * C::PART_STATS + a]);
+  for (int j = lane; j < p.P; j += 64) M = fmaxf(M, base[j * C::PART_STATS + al]);
   M = wmax(M);
   float L = 0.f;
   for (int j = lane; j < p.P; j += 64)
-    L += base[j * C::PART_STATS + C::KP + a] * fast_exp2(base[j * C::PART_STATS + a] - M);
+    L += base[j * C::PART_STATS + C::KP + al] * fast_exp2(base[j * C::PART_STATS + al] - M);
   L = wsum(L);
   const int c1 = C::DP > 64 ? lane + 64 : lane;   // second channel (DP = 128 only)
   float u0 = 0.f, u1 = 0.f;
@@ -530,9 +540,9 @@ __global__ void __launch_bounds__(256) bwd_stats_merge(BwdParams p) {
     for (int e = 0; e < kRedBatch; ++e) {
       const int j = min(j0 + WPA * e, p.P - 1);
       const float* pj = base + j * C::PART_STATS;
-      w[e] = pj[a];
-      x0[e] = pj[2 * C::KP + a * C::DP + (lane & (C::DP - 1))];
-      x1[e] = pj[2 * C::KP + a * C::DP + c1];
+      w[e] = pj[al];
+      x0[e] = pj[2 * C::KP + al * C::DP + (lane & (C::DP - 1))];
+      x1[e] = pj[2 * C::KP + al * C::DP + c1];
     }
 #pragma unroll
     for (int e = 0; e < kRedBatch; ++e) {
@@ -549,14 +559,19 @@ __global__ void __launch_bounds__(256) bwd_stats_merge(BwdParams p) {
   float* va = p.VA + ((long)head * p.nag + a) * p.d;
   if (lane < p.d) va[lane] = u0 * inv;
   if (C::DP > 64 && lane + 64 < p.d) va[lane + 64] = u1 * inv;
-  if (lane == 0) p.lse[(long)head * C::KP + a] = M + log2f(L);
+  if (lane == 0) p.lse[vh * C::KP + al] = M + log2f(L);
 }
 
 // ------------------------------------------------------------------ bcast
 // Workgroup (head, slot) covers tokens [slot T, slot T + T) in steps of 64;
 // wave w holds tokens 16 w .. 16 w + 15 of a step (lane column r).
 // Partial layout per workgroup: dA[KP][DP] (unscaled), then dV_A[KP][DP].
-template <class El, int KT, int DT>
+// MODE 0: the head's agents form one chunk.  With several chunks of 64
+// agents the softmax over agents spans launches: MODE 1 records, per token
+// and chunk, the chunk's score maximum, its sum of exponentials and their
+// dP2-weighted sum; MODE 2 combines those into the full normalisation and
+// D = rowsum(P2 dP2), then runs the gradient products of its chunk.
+template <class El, int KT, int DT, int MODE>
 __global__ void __launch_bounds__(kThr) bwd_bcast_kernel(BwdParams p) {
   using C = Geo<KT, DT>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -574,7 +589,8 @@ __global__ void __launch_bounds__(kThr) bwd_bcast_kernel(BwdParams p) {
   uint16_t* stg0 = sCl + C::DP * C::TS;      // [agent][token]: dS2 hi, then P2 hi
   uint16_t* stg1 = stg0 + C::KP * kSS;       // [agent][token]: P2 lo
   uint16_t* stgT = stg1 + C::KP * kSS;       // [channel][token]: Q, then dO
-  const long ah = (long)head * p.nag * p.d;
+  const long ah = ((long)head * p.nag + p.a0) * p.d;   // the chunk's first agent row
+  const long vh = (long)head * p.nch + p.chunk;          // (head, chunk)
   const int col = 16 * wave + r;
   const unsigned hbytes = (unsigned)(p.N * p.d * 2);
   const rsrc_t rq = rsrc_of(p.q + hd, hbytes), ro = rsrc_of(p.dout + hd, hbytes);
@@ -582,8 +598,8 @@ __global__ void __launch_bounds__(kThr) bwd_bcast_kernel(BwdParams p) {
   uint4 qf[DT], of[DT];
   load_frags<DT>(qf, rq, t0 + col, t0 + col < t1, p.d, g);
   load_frags<DT>(of, ro, t0 + col, t0 + col < t1, p.d, g);
-  stage_kd<El, C::KP, C::DP, C::RS, C::TS>(sAh, sAl, sCh, sCl, p.A + ah, p.nag, p.d, tid);
-  stage_kd<El, C::KP, C::DP, C::RS, C::TS>(sVh, sVl, nullptr, nullptr, p.VA + ah, p.nag, p.d,
+  stage_kd<El, C::KP, C::DP, C::RS, C::TS>(sAh, sAl, sCh, sCl, p.A + ah, p.nagc, p.d, tid);
+  stage_kd<El, C::KP, C::DP, C::RS, C::TS>(sVh, sVl, nullptr, nullptr, p.VA + ah, p.nagc, p.d,
                                            tid);
   __syncthreads();
   BW_STAMP(1, 1);
@@ -597,7 +613,7 @@ __global__ void __launch_bounds__(kThr) bwd_bcast_kernel(BwdParams p) {
 #pragma unroll
   for (int kb = 0; kb < KT; ++kb)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) nb[kb][i] = 16 * kb + 4 * g + i < p.nag ? 0.f : -INFINITY;
+    for (int i = 0; i < 4; ++i) nb[kb][i] = 16 * kb + 4 * g + i < p.nagc ? 0.f : -INFINITY;
   for (int tok0 = t0; tok0 < t1; tok0 += kStep) {
     const int tok = tok0 + col;
     const bool tv = tok < t1;
@@ -638,16 +654,61 @@ __global__ void __launch_bounds__(kThr) bwd_bcast_kernel(BwdParams p) {
         l += x[kb][i];
       }
     l = group4_sum(l);
-    const float inv = tv ? 1.0f / l : 0.f;   // tokens past the range: P2 = dS2 = 0
-    float D = 0.f;
+    if (MODE == 1) {
+      // per-token statistics of this agent chunk: max, sum of 2^(x - max),
+      // and the sum of 2^(x - max) dP2
+      float S = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < KT; ++kb)
+      for (int kb = 0; kb < KT; ++kb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[kb][i] *= inv;
-        D += x[kb][i] * dp[kb][i];
+        for (int i = 0; i < 4; ++i) S += x[kb][i] * dp[kb][i];
+      S = group4_sum(S);
+      if (tv && g == 0)
+        *reinterpret_cast<float4*>(p.tst + (((long)p.chunk * p.BH + head) * p.N + tok) * 4) =
+            float4{mx, l, S, 0.f};
+#pragma unroll
+      for (int s2 = 0; s2 < DT; ++s2) {
+        qf[s2] = qn[s2];
+        of[s2] = on[s2];
       }
-    D = group4_sum(D);
+      ++step;
+      continue;
+    }
+    float inv, D = 0.f;
+    if (MODE == 2) {
+      // the softmax over all agents from every chunk's statistics of this token
+      // (running maximum: sums rescale when it grows)
+      float M = mx, L = 1.f, S = 0.f;
+      if (tv) {
+        M = -INFINITY;
+        L = 0.f;
+        for (int c2 = 0; c2 < p.nch; ++c2) {
+          const float4 st = *reinterpret_cast<const float4*>(
+              p.tst + (((long)c2 * p.BH + head) * p.N + tok) * 4);
+          const float Mn = fmaxf(M, st.x);
+          const float fo = fast_exp2((M - Mn) * p.sl2), fn = fast_exp2((st.x - Mn) * p.sl2);
+          L = L * fo + st.y * fn;
+          S = S * fo + st.z * fn;
+          M = Mn;
+        }
+      }
+      inv = tv ? fast_exp2((mx - M) * p.sl2) / L : 0.f;
+#pragma unroll
+      for (int kb = 0; kb < KT; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[kb][i] *= inv;
+      D = tv ? S / L : 0.f;
+    } else {
+      inv = tv ? 1.0f / l : 0.f;   // tokens past the range: P2 = dS2 = 0
+#pragma unroll
+      for (int kb = 0; kb < KT; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[kb][i] *= inv;
+          D += x[kb][i] * dp[kb][i];
+        }
+      D = group4_sum(D);
+    }
 #pragma unroll
     for (int kb = 0; kb < KT; ++kb)
 #pragma unroll
@@ -670,8 +731,10 @@ __global__ void __launch_bounds__(kThr) bwd_bcast_kernel(BwdParams p) {
         acc = El::mma(ch, dsl[j], acc);
         acc = El::mma(cl, dsh[j], acc);
       }
-      if (tv && 16 * db + 4 * g < p.d)
-        *reinterpret_cast<f32x4*>(dQh + (long)tok * p.d + 16 * db + 4 * g) = acc * p.scale;
+      if (tv && 16 * db + 4 * g < p.d) {
+        f32x4* dst = reinterpret_cast<f32x4*>(dQh + (long)tok * p.d + 16 * db + 4 * g);
+        *dst = p.chunk > 0 ? *dst + acc * p.scale : acc * p.scale;   // sum over agent chunks
+      }
     }
     // dA += dS2^T Q over the step's tokens: tile (kb, db) has rows = agents
     // 16 kb + 4 g + i and column = channel 16 db + r
@@ -732,6 +795,7 @@ __global__ void __launch_bounds__(kThr) bwd_bcast_kernel(BwdParams p) {
     if (step < 2) BW_STAMP(1, 6 + 5 * step);
     ++step;
   }
+  if (MODE == 1) return;   // statistics only
   if (p.P == 1) {
     // the workgroup holds the whole head: dA, dV_A and D1 = rowsum(dV_A V_A)
     // directly; D1 from per-tile partial sums in LDS (staging rows are free)
@@ -745,8 +809,8 @@ __global__ void __launch_bounds__(kThr) bwd_bcast_kernel(BwdParams p) {
         for (int i = 0; i < 4; ++i) {
           const int a = 16 * kb + 4 * g + i;
           float prod = 0.f;
-          if (a < p.nag && c < p.d) {
-            const long o = ((long)head * p.nag + a) * p.d + c;
+          if (a < p.nagc && c < p.d) {
+            const long o = ah + (long)a * p.d + c;
             p.dA[o] = accA[u][i] * p.scale;
             p.dVA[o] = accV[u][i];
             prod = accV[u][i] * p.VA[o];
@@ -758,15 +822,15 @@ __global__ void __launch_bounds__(kThr) bwd_bcast_kernel(BwdParams p) {
       }
     }
     __syncthreads();
-    if (tid < p.nag) {
+    if (tid < p.nagc) {
       float dd = 0.f;
 #pragma unroll
       for (int db = 0; db < C::DB; ++db) dd += sD[db * C::KP + tid];
-      p.D1[(long)head * C::KP + tid] = dd;
+      p.D1[vh * C::KP + tid] = dd;
     }
     return;
   }
-  float* base = p.part + ((long)head * p.P + slot) * C::PART_BCAST;
+  float* base = p.part + (vh * p.P + slot) * C::PART_BCAST;
 #pragma unroll
   for (int u = 0; u < C::TPW; ++u) {
     const int t = wave + kNW * u;
@@ -790,7 +854,9 @@ __global__ void __launch_bounds__(256) bwd_reduce_bcast(BwdParams p) {
   using C = Geo<KT, DT>;
   int head, a, wave, lane;
   if (!red_item<WPA>(p, head, a, wave, lane)) return;
-  const float* base = p.part + (long)head * p.P * C::PART_BCAST + a * C::DP;
+  const int ch = a / C::KP, al = a - ch * C::KP;   // agent chunk and index within it
+  const long vh = (long)head * p.nch + ch;
+  const float* base = p.part + vh * p.P * C::PART_BCAST + al * C::DP;
   const int ca = lane & (C::DP - 1), cb = C::DP > 64 ? lane + 64 : lane;
   float sa0 = 0.f, sa1 = 0.f, sv0 = 0.f, sv1 = 0.f;
   for (int j0 = wave; j0 < p.P; j0 += WPA * kRedBatch) {
@@ -832,7 +898,7 @@ __global__ void __launch_bounds__(256) bwd_reduce_bcast(BwdParams p) {
     dd += sv1 * p.VA[o + lane + 64];
   }
   dd = wsum(dd);
-  if (lane == 0) p.D1[(long)head * C::KP + a] = dd;
+  if (lane == 0) p.D1[vh * C::KP + al] = dd;
 }
 
 // ------------------------------------------------------------------ agg
@@ -856,7 +922,8 @@ __global__ void __launch_bounds__(kThr) bwd_agg_kernel(BwdParams p) {
   uint16_t* sHl = sHh + C::DP * C::TS;
   uint16_t* stg0 = sHl + C::DP * C::TS;      // dS1 hi [agent][token]
   uint16_t* stgT = stg0 + C::KP * kSS;       // K [channel][token]
-  const long ah = (long)head * p.nag * p.d;
+  const long ah = ((long)head * p.nag + p.a0) * p.d;   // the chunk's first agent row
+  const long vh = (long)head * p.nch + p.chunk;          // (head, chunk)
   const int col = 16 * wave + r;
   const unsigned hbytes = (unsigned)(p.N * p.d * 2);
   const rsrc_t rk = rsrc_of(p.k + hd, hbytes), rv = rsrc_of(p.v + hd, hbytes);
@@ -864,18 +931,18 @@ __global__ void __launch_bounds__(kThr) bwd_agg_kernel(BwdParams p) {
   uint4 kf[DT], vf[DT];
   load_frags<DT>(kf, rk, t0 + col, t0 + col < t1, p.d, g);
   load_frags<DT>(vf, rv, t0 + col, t0 + col < t1, p.d, g);
-  stage_kd<El, C::KP, C::DP, C::RS, C::TS>(sAh, sAl, sCh, nullptr, p.A + ah, p.nag, p.d, tid);
-  stage_kd<El, C::KP, C::DP, C::RS, C::TS>(sGh, sGl, sHh, sHl, p.dVA + ah, p.nag, p.d, tid);
+  stage_kd<El, C::KP, C::DP, C::RS, C::TS>(sAh, sAl, sCh, nullptr, p.A + ah, p.nagc, p.d, tid);
+  stage_kd<El, C::KP, C::DP, C::RS, C::TS>(sGh, sGl, sHh, sHl, p.dVA + ah, p.nagc, p.d, tid);
   // lse and D1 of this lane's agent rows 16 kb + 4 g + i (padding agents: P1 = 0)
   float Lr[KT][4], Dr[KT][4];
 #pragma unroll
   for (int kb = 0; kb < KT; ++kb) {
-    const float4 l4 = *reinterpret_cast<const float4*>(p.lse + (long)head * C::KP + 16 * kb + 4 * g);
-    const float4 d4 = *reinterpret_cast<const float4*>(p.D1 + (long)head * C::KP + 16 * kb + 4 * g);
+    const float4 l4 = *reinterpret_cast<const float4*>(p.lse + vh * C::KP + 16 * kb + 4 * g);
+    const float4 d4 = *reinterpret_cast<const float4*>(p.D1 + vh * C::KP + 16 * kb + 4 * g);
     const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const bool real = 16 * kb + 4 * g + i < p.nag;
+      const bool real = 16 * kb + 4 * g + i < p.nagc;
       Lr[kb][i] = real ? lv[i] : 1e30f;
       Dr[kb][i] = real ? dv4[i] : 0.f;
     }
@@ -937,10 +1004,18 @@ __global__ void __launch_bounds__(kThr) bwd_agg_kernel(BwdParams p) {
       }
       if (tv && 16 * db + 4 * g < p.d) {
         const long o = (long)tok * p.d + 16 * db + 4 * g;
-        *reinterpret_cast<uint2*>(dkh + o) =
-            uint2{El::pack2(ak[0] * p.scale, ak[1] * p.scale),
-                  El::pack2(ak[2] * p.scale, ak[3] * p.scale)};
-        *reinterpret_cast<uint2*>(dvh + o) = uint2{El::pack2(av[0], av[1]), El::pack2(av[2], av[3])};
+        if (p.nch > 1) {   // float32 sums over the agent chunks
+          f32x4* fk = reinterpret_cast<f32x4*>(p.dKf + hd + o);
+          f32x4* fv = reinterpret_cast<f32x4*>(p.dVf + hd + o);
+          *fk = p.chunk > 0 ? *fk + ak * p.scale : ak * p.scale;
+          *fv = p.chunk > 0 ? *fv + av : av;
+        } else {
+          *reinterpret_cast<uint2*>(dkh + o) =
+              uint2{El::pack2(ak[0] * p.scale, ak[1] * p.scale),
+                    El::pack2(ak[2] * p.scale, ak[3] * p.scale)};
+          *reinterpret_cast<uint2*>(dvh + o) =
+              uint2{El::pack2(av[0], av[1]), El::pack2(av[2], av[3])};
+        }
       }
     }
     if (step < 2) BW_STAMP(2, 3 + 4 * step);
@@ -982,13 +1057,13 @@ __global__ void __launch_bounds__(kThr) bwd_agg_kernel(BwdParams p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int a = 16 * kb + 4 * g + i;
-          if (a < p.nag && c < p.d) p.dA[((long)head * p.nag + a) * p.d + c] += accA[u][i] * p.scale;
+          if (a < p.nagc && c < p.d) p.dA[ah + (long)a * p.d + c] += accA[u][i] * p.scale;
         }
       }
     }
     return;
   }
-  float* base = p.part + ((long)head * p.P + slot) * C::PART_AGG;
+  float* base = p.part + (vh * p.P + slot) * C::PART_AGG;
 #pragma unroll
   for (int u = 0; u < C::TPW; ++u) {
     const int t = wave + kNW * u;
@@ -1007,7 +1082,8 @@ __global__ void __launch_bounds__(256) bwd_reduce_agg(BwdParams p) {
   using C = Geo<KT, DT>;
   int head, a, wave, lane;
   if (!red_item<WPA>(p, head, a, wave, lane)) return;
-  const float* base = p.part + (long)head * p.P * C::PART_AGG + a * C::DP;
+  const int ch = a / C::KP, al = a - ch * C::KP;   // agent chunk and index within it
+  const float* base = p.part + ((long)head * p.nch + ch) * p.P * C::PART_AGG + al * C::DP;
   const int ca = lane & (C::DP - 1), cb = C::DP > 64 ? lane + 64 : lane;
   float s0 = 0.f, s1 = 0.f;
   for (int j0 = wave; j0 < p.P; j0 += WPA * kRedBatch) {
@@ -1170,6 +1246,11 @@ int run_passes(BwdParams p, const Pass (&pp)[3], hipStream_t st) {
   // reductions: four waves per agent from 8 partials, else one
   const unsigned items = (unsigned)(p.BH * p.nag);
   auto rgrid = [&](int P) { return dim3(P > 8 ? items : (items + kNW - 1) / kNW); };
+  auto set_chunk = [&](int c) {
+    p.chunk = c;
+    p.a0 = c * C::KP;
+    p.nagc = min(C::KP, p.nag - p.a0);
+  };
   const int nkd = p.BH * p.nag * p.d;
   const unsigned g_kd = (unsigned)std::min(4096, (nkd + 255) / 256);
   hipError_t e;
@@ -1185,24 +1266,45 @@ int run_passes(BwdParams p, const Pass (&pp)[3], hipStream_t st) {
         p.q, const_cast<float*>(p.A), p.BH, p.N, p.h, p.w, p.d, p.s, U);
   }
   if ((e = hipGetLastError()) != hipSuccess) return (int)e;
+  // aggregation statistics, chunk by chunk, then lse and V_A of every agent
   p.P = pp[0].P;
   p.T = pp[0].T;
-  bwd_stats_kernel<El, KT, DT><<<dim3((unsigned)(p.BH * p.P)), dim3(kThr), C::STATS, st>>>(p);
-  if ((e = hipGetLastError()) != hipSuccess) return (int)e;
+  for (int c = 0; c < p.nch; ++c) {
+    set_chunk(c);
+    bwd_stats_kernel<El, KT, DT><<<dim3((unsigned)(p.BH * p.P)), dim3(kThr), C::STATS, st>>>(p);
+    if ((e = hipGetLastError()) != hipSuccess) return (int)e;
+  }
   if (p.P > 8) bwd_stats_merge<KT, DT, 4><<<rgrid(p.P), dim3(256), 0, st>>>(p);
   else if (p.P > 1) bwd_stats_merge<KT, DT, 1><<<rgrid(p.P), dim3(256), 0, st>>>(p);
   if ((e = hipGetLastError()) != hipSuccess) return (int)e;
+  // broadcast: one chunk directly; several through per-token statistics
   p.P = pp[1].P;
   p.T = pp[1].T;
-  bwd_bcast_kernel<El, KT, DT><<<dim3((unsigned)(p.BH * p.P)), dim3(kThr), C::BCAST, st>>>(p);
+  const dim3 gb((unsigned)(p.BH * p.P));
+  if (p.nch == 1) {
+    bwd_bcast_kernel<El, KT, DT, 0><<<gb, dim3(kThr), C::BCAST, st>>>(p);
+  } else {
+    for (int c = 0; c < p.nch; ++c) {
+      set_chunk(c);
+      bwd_bcast_kernel<El, KT, DT, 1><<<gb, dim3(kThr), C::BCAST, st>>>(p);
+    }
+    for (int c = 0; c < p.nch; ++c) {
+      set_chunk(c);
+      bwd_bcast_kernel<El, KT, DT, 2><<<gb, dim3(kThr), C::BCAST, st>>>(p);
+    }
+  }
   if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   if (p.P > 8) bwd_reduce_bcast<KT, DT, 4><<<rgrid(p.P), dim3(256), 0, st>>>(p);
   else if (p.P > 1) bwd_reduce_bcast<KT, DT, 1><<<rgrid(p.P), dim3(256), 0, st>>>(p);
   if ((e = hipGetLastError()) != hipSuccess) return (int)e;
+  // aggregation gradients, chunk by chunk
   p.P = pp[2].P;
   p.T = pp[2].T;
-  bwd_agg_kernel<El, KT, DT><<<dim3((unsigned)(p.BH * p.P)), dim3(kThr), C::AGG, st>>>(p);
-  if ((e = hipGetLastError()) != hipSuccess) return (int)e;
+  for (int c = 0; c < p.nch; ++c) {
+    set_chunk(c);
+    bwd_agg_kernel<El, KT, DT><<<dim3((unsigned)(p.BH * p.P)), dim3(kThr), C::AGG, st>>>(p);
+    if ((e = hipGetLastError()) != hipSuccess) return (int)e;
+  }
   if (p.P > 8) bwd_reduce_agg<KT, DT, 4><<<rgrid(p.P), dim3(256), 0, st>>>(p);
   else if (p.P > 1) bwd_reduce_agg<KT, DT, 1><<<rgrid(p.P), dim3(256), 0, st>>>(p);
   if ((e = hipGetLastError()) != hipSuccess) return (int)e;
@@ -1211,6 +1313,13 @@ int run_passes(BwdParams p, const Pass (&pp)[3], hipStream_t st) {
   bwd_finish_dq<El><<<dim3((unsigned)((nq + 255) / 256), (unsigned)p.BH), dim3(256), 0, st>>>(
       p.dQ, p.agents_in ? nullptr : p.dA, p.dq, p.N, p.h, p.w, p.d, p.s, tiled);
   if ((e = hipGetLastError()) != hipSuccess) return (int)e;
+  if (p.nch > 1) {   // dk, dv from their float32 sums over the chunks
+    const int nnd = p.BH * p.N * p.d;
+    const unsigned g_nd = (unsigned)std::min(65536, (nnd + 255) / 256);
+    bwd_narrow<El><<<dim3(g_nd), dim3(256), 0, st>>>(p.dKf, p.dk, nnd);
+    bwd_narrow<El><<<dim3(g_nd), dim3(256), 0, st>>>(p.dVf, p.dv, nnd);
+    if ((e = hipGetLastError()) != hipSuccess) return (int)e;
+  }
   if (p.agents_in) bwd_narrow<El><<<dim3(g_kd), dim3(256), 0, st>>>(p.dA, p.dagents, nkd);
   return (int)hipGetLastError();
 }

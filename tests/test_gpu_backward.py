@@ -73,6 +73,14 @@ CASES = [
     inputs.custom("bwd_d96_k36", B=1, H=2, h=16, w=16, d=96, s=6),
     inputs.custom("bwd_one_head_4096", B=1, H=1, h=64, w=64, d=64, s=8),
     inputs.custom("bwd_supplied_k64", B=2, H=2, h=16, w=16, d=64, s=8, supplied_agents=True),
+    # more than 64 agents: chunks of 64 with a ragged last chunk (81 = 64 + 17,
+    # 144 = 2 x 64 + 16), supplied agents over 196 = 3 x 64 + 4, and 512 heads
+    # of 81 tokens, where each pass holds a whole head in one workgroup
+    inputs.custom("bwd_chunk_k81", B=2, H=2, h=27, w=27, d=64, s=9),
+    inputs.custom("bwd_chunk_k144_d128_f16", B=1, H=2, h=48, w=40, d=128, s=12, dtype="f16"),
+    inputs.custom("bwd_chunk_supplied_k196", B=1, H=2, h=28, w=28, d=48, s=14,
+                  supplied_agents=True),
+    inputs.custom("bwd_chunk_512_heads", B=64, H=8, h=9, w=9, d=16, s=9),
 ]
 
 
