@@ -39,11 +39,35 @@ PMC_CMD = ("timeout -s KILL 120 rocprofv3 --pmc {c} --output-format csv -d $R/gp
            "-- python3 $R/bench.py {a}")
 
 
+def _strip_comments(src: str) -> str:
+    """C/C++ source without its comments (string and character literals kept)."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":   # literal: copy through its closing quote
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return "".join(out)
+
+
 def kernel_sources_sha256() -> str:
-    """Hash of the sources the forward's fused kernel is built and launched
-    from (its kernels, their instances, the host library that plans its
-    launches, the ABI header): HBM counters taken on an older kernel are not
-    reported."""
+    """Hash of the code (comments stripped) the forward's fused kernel is
+    built and launched from (its kernels, their instances, the host library
+    that plans its launches, the ABI header): HBM counters taken on older
+    code are not reported."""
     import glob
     import hashlib
     h = hashlib.sha256()
@@ -53,8 +77,8 @@ def kernel_sources_sha256() -> str:
     files.append(os.path.join(ROOT, "include", "agent_attn.h"))
     for f in files:
         h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            h.update(_strip_comments(fh.read()).encode())
     return h.hexdigest()
 
 
@@ -207,6 +231,56 @@ def write_trace_summary(wl, trace_dir):
     print(path)
 
 
+SIMD_COUNT = 1024   # MI355X: 256 CUs x 4 SIMDs
+
+
+def write_mfma_summary(wl, pmc_dir, trace_dir):
+    """profiles/<kernel>_<workload>_mfma_busy.md from a rocprofv3 --pmc run of
+    the derived counter MfmaUtil (matrix-core busy cycles summed over the SIMDs
+    / (GPU active cycles x SIMDs)) and the kernel trace of the same workload,
+    which gives the flop-based utilisation beside it."""
+    import csv
+    import statistics
+    m, n = _counter_means(os.path.join(pmc_dir, "run_counter_collection.csv"), FUSED_KERNEL)
+    trace = [r for r in csv.DictReader(open(os.path.join(trace_dir, "run_kernel_trace.csv")))
+             if FUSED_KERNEL in r["Kernel_Name"]]
+    dur = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in trace][-100:]
+    us = statistics.mean(dur)
+    flops = algorithmic_flops(wl)
+    util_flop = flops / (us * 1e-6) / (BF16_PEAK_TFLOPS * 1e12)
+    busy = m.get("MfmaUtil")
+    rows = [
+        f"# Matrix-core busy: {FUSED_KERNEL}, workload {wl.name}",
+        "",
+        f"Workload: B={wl.B} H={wl.H} grid {wl.h}x{wl.w} (N={wl.N}) d={wl.d} k={wl.k} {wl.dtype}.",
+        "Commands (from /tmp with TMPDIR=/tmp, R = repository root):",
+        "",
+        "    " + PMC_CMD.format(c="MfmaUtil", d=os.path.basename(pmc_dir),
+                                a=f"--workload {wl.name} --no-cpu-baseline --steps 10 --warmup 2"),
+        "    " + TRACE_CMD.format(w=wl.name),
+        f"    python3 bench.py --workload {wl.name} --mfma-summary <the two -d folders>",
+        "",
+        "MfmaUtil is rocprofv3's derived counter: SQ_VALU_MFMA_BUSY_CYCLES summed over the",
+        f"SIMDs / (GRBM_GUI_ACTIVE x {SIMD_COUNT} SIMDs) x 100.  Busy cycles cover every",
+        "matrix-core instruction the kernel issues (the lo halves of hi + lo operand pairs and",
+        "the row-sum products against a ones operand included); the flop-based figure counts",
+        "only the algorithmic 8 N k d per head.",
+        "",
+        f"- fused kernel dispatches sampled: {n.get('MfmaUtil', 0)}",
+        f"- MfmaUtil per dispatch (percent): {busy:.2f}" if busy is not None else "- MfmaUtil: absent",
+        f"- kernel duration (graph-replayed launches of the trace): {us:.2f} us",
+        f"- algorithmic flop per launch (8 N k d per head): {flops}",
+        f"- flop-based utilisation of the {BF16_PEAK_TFLOPS:.0f} TFLOP/s dense bf16 peak: "
+        f"{100 * util_flop:.2f} %",
+        f"- kernel_sources_sha256: {kernel_sources_sha256()}",
+        "",
+    ]
+    path = os.path.join(PROFILES, f"{FUSED_KERNEL}_{wl.name}_mfma_busy.md")
+    with open(path, "w") as fh:
+        fh.write("\n".join(rows))
+    print(path)
+
+
 PASS_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/{d}_{w} -o run "
             "-- python3 $R/bench.py --workload {w} --no-cpu-baseline --{m} --steps 20 --warmup 2")
 PASS_NAMES = {"backward": ("bwd_passes", "ktb"), "projections": ("module_projections", "ktp")}
@@ -231,20 +305,23 @@ def write_passes_summary(wl, mode, trace_dir):
         f"$R/gpurun_out/{tag}_{wl.name}",
         "",
         "The run makes 2 warm-up steps, 20 event-bracketed eager steps, then a graph of 20",
-        "steps replayed twice; every kernel below runs once per step.",
+        "steps replayed twice (62 steps); a kernel launched once per agent chunk (chunks of",
+        "64 agents) runs several times per step.",
         "",
-        "| kernel | calls | average us | min us | max us |",
-        "|---|---|---|---|---|",
+        "| kernel | calls | per step | average us | min us | max us |",
+        "|---|---|---|---|---|---|",
     ]
+    steps = min(int(r["Calls"]) for r in ours) if ours else 1
     total = 0.0
     for r in ours:
         nm = r["Name"].split("(")[0].replace("void ", "")
         nm = nm if len(nm) < 70 else nm[:67] + "..."
         avg = float(r["AverageNs"]) / 1e3
-        total += avg
-        rows.append(f"| `{nm}` | {r['Calls']} | {avg:.1f} | {int(r['MinNs']) / 1e3:.1f} | "
-                    f"{int(r['MaxNs']) / 1e3:.1f} |")
-    rows += ["", f"- sum of the average kernel durations (one step): {total:.1f} us"]
+        per = int(r["Calls"]) / steps
+        total += avg * per
+        rows.append(f"| `{nm}` | {r['Calls']} | {per:g} | {avg:.1f} | "
+                    f"{int(r['MinNs']) / 1e3:.1f} | {int(r['MaxNs']) / 1e3:.1f} |")
+    rows += ["", f"- sum of the kernel durations of one step: {total:.1f} us"]
     path = os.path.join(PROFILES, f"{name}_{wl.name}_kernel_trace.md")
     with open(path, "w") as fh:
         fh.write("\n".join(rows) + "\n")
@@ -350,6 +427,9 @@ def main():
                     help="write the kernel-trace summary of the backward ('backward') or the "
                          "module with projections ('projections') of --workload from a "
                          "rocprofv3 --kernel-trace --stats output folder and exit")
+    ap.add_argument("--mfma-summary", nargs=2, metavar=("PMC_DIR", "TRACE_DIR"),
+                    help="write the matrix-core busy summary of --workload from a rocprofv3 "
+                         "--pmc MfmaUtil output folder and a --kernel-trace folder and exit")
     ap.add_argument("--trace-summary", metavar="DIR",
                     help="write the kernel-trace summary of --workload from a rocprofv3 "
                          "--kernel-trace --stats output folder and exit")
@@ -361,9 +441,11 @@ def main():
             sys.exit(f"bench.py: --passes-summary takes one of {sorted(PASS_NAMES)}")
         write_passes_summary(inputs.WORKLOADS[args.workload], mode, folder)
         return
-    if args.pmc_summary or args.trace_summary:
+    if args.pmc_summary or args.trace_summary or args.mfma_summary:
         from efficient_attention_vision_amd import inputs
         wl = inputs.WORKLOADS[args.workload]
+        if args.mfma_summary:
+            write_mfma_summary(wl, *args.mfma_summary)
         if args.pmc_summary:
             write_counter_summary(wl, *args.pmc_summary)
         if args.trace_summary:

@@ -117,7 +117,7 @@ struct BwdParams {
   int nch, chunk;         // chunks per head, this launch's chunk
   int a0, nagc;           // first agent and agent count of the chunk
   float* tst;             // [nch, BH, N, 4]: max, sum, sum of P dP of a chunk per token
-  float* dKf;             // [BH, N, d] float32 sums over chunks of dk, dv (nch > 1)
+  float* dKf;             // [BH, N, d] float32 sums of dk, dv over all chunks but the last
   float* dVf;
   int P, T;               // workgroups per head and tokens per workgroup of the pass
   float sl2, scale;       // scale * log2(e), scale
@@ -598,7 +598,8 @@ __global__ void __launch_bounds__(kThr) bwd_bcast_kernel(BwdParams p) {
   uint4 qf[DT], of[DT];
   load_frags<DT>(qf, rq, t0 + col, t0 + col < t1, p.d, g);
   load_frags<DT>(of, ro, t0 + col, t0 + col < t1, p.d, g);
-  stage_kd<El, C::KP, C::DP, C::RS, C::TS>(sAh, sAl, sCh, sCl, p.A + ah, p.nagc, p.d, tid);
+  stage_kd<El, C::KP, C::DP, C::RS, C::TS>(sAh, sAl, MODE == 1 ? nullptr : sCh,
+                                           MODE == 1 ? nullptr : sCl, p.A + ah, p.nagc, p.d, tid);
   stage_kd<El, C::KP, C::DP, C::RS, C::TS>(sVh, sVl, nullptr, nullptr, p.VA + ah, p.nagc, p.d,
                                            tid);
   __syncthreads();
@@ -1004,15 +1005,20 @@ __global__ void __launch_bounds__(kThr) bwd_agg_kernel(BwdParams p) {
       }
       if (tv && 16 * db + 4 * g < p.d) {
         const long o = (long)tok * p.d + 16 * db + 4 * g;
-        if (p.nch > 1) {   // float32 sums over the agent chunks
-          f32x4* fk = reinterpret_cast<f32x4*>(p.dKf + hd + o);
-          f32x4* fv = reinterpret_cast<f32x4*>(p.dVf + hd + o);
-          *fk = p.chunk > 0 ? *fk + ak * p.scale : ak * p.scale;
-          *fv = p.chunk > 0 ? *fv + av : av;
+        // over several agent chunks: float32 sums, rounded by the last chunk
+        f32x4* fk = reinterpret_cast<f32x4*>(p.dKf + hd + o);
+        f32x4* fv = reinterpret_cast<f32x4*>(p.dVf + hd + o);
+        ak *= p.scale;
+        if (p.chunk > 0) {
+          ak += *fk;
+          av += *fv;
+        }
+        if (p.chunk + 1 < p.nch) {
+          *fk = ak;
+          *fv = av;
         } else {
           *reinterpret_cast<uint2*>(dkh + o) =
-              uint2{El::pack2(ak[0] * p.scale, ak[1] * p.scale),
-                    El::pack2(ak[2] * p.scale, ak[3] * p.scale)};
+              uint2{El::pack2(ak[0], ak[1]), El::pack2(ak[2], ak[3])};
           *reinterpret_cast<uint2*>(dvh + o) =
               uint2{El::pack2(av[0], av[1]), El::pack2(av[2], av[3])};
         }
@@ -1313,13 +1319,6 @@ int run_passes(BwdParams p, const Pass (&pp)[3], hipStream_t st) {
   bwd_finish_dq<El><<<dim3((unsigned)((nq + 255) / 256), (unsigned)p.BH), dim3(256), 0, st>>>(
       p.dQ, p.agents_in ? nullptr : p.dA, p.dq, p.N, p.h, p.w, p.d, p.s, tiled);
   if ((e = hipGetLastError()) != hipSuccess) return (int)e;
-  if (p.nch > 1) {   // dk, dv from their float32 sums over the chunks
-    const int nnd = p.BH * p.N * p.d;
-    const unsigned g_nd = (unsigned)std::min(65536, (nnd + 255) / 256);
-    bwd_narrow<El><<<dim3(g_nd), dim3(256), 0, st>>>(p.dKf, p.dk, nnd);
-    bwd_narrow<El><<<dim3(g_nd), dim3(256), 0, st>>>(p.dVf, p.dv, nnd);
-    if ((e = hipGetLastError()) != hipSuccess) return (int)e;
-  }
   if (p.agents_in) bwd_narrow<El><<<dim3(g_kd), dim3(256), 0, st>>>(p.dA, p.dagents, nkd);
   return (int)hipGetLastError();
 }

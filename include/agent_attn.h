@@ -221,10 +221,12 @@ size_t agent_attn_backward_workspace_bytes(int B, int H, int h, int w, int d,
  *                to dagents [B, H, s*s, d] of dtype (required then, else
  *                ignored).
  * The forward is recomputed inside (nothing is saved between the calls).
- * Arithmetic: float32 for float32 tensors and for more than 64 agents; for
- * 16-bit tensors with up to 64 agents, matrix-core products accumulating in
- * float32 whose non-exact operands (agents, V_A, dV_A, probabilities, score
- * gradients) enter as pairs of 16-bit values where rounding would cancel.
+ * Arithmetic: float32 for float32 tensors; for 16-bit tensors, matrix-core
+ * products accumulating in float32 whose non-exact operands (agents, V_A,
+ * dV_A, probabilities, score gradients) enter as pairs of 16-bit values where
+ * rounding would cancel.  More than 64 agents run in chunks of 64 whose
+ * contributions to dq, dk and dv are summed in float32 in a fixed order (the
+ * results are deterministic).
  * workspace: at least
  * agent_attn_backward_workspace_bytes(...) bytes, 256-byte aligned, contents
  * free.  Outputs may not overlap any argument, nor the workspace any tensor
