@@ -503,6 +503,15 @@ int run_mfma_phases(const Dims& D, aa::MfmaParams mp, int DC, int phases, bool f
   if (lds > 160 * 1024 - 64)
     return fail(AGENT_ATTN_ERR_UNSUPPORTED, "d=%d with %d agents needs %d bytes of LDS", D.d,
                 D.nag, lds);
+  // the DWC reads V from LDS when a workgroup's tokens and their 3 x 3
+  // neighbourhood (one grid row and one token on either side) fit beside the
+  // plan; otherwise each tap is a load from V
+  mp.dwc_halo_rows = 0;
+  if (mp.dwc_w) {
+    const long rows = std::min<long>(D.N, (long)mp.T + 2L * D.w + 2);
+    if (lds + rows * (32L * DC + 8) * 2 <= 160 * 1024 - 64)   // dwc_halo_lds_bytes
+      mp.dwc_halo_rows = (int)rows;
+  }
   if (((D.N - 1) * D.sn + D.d) * 2 >= (long)aa::kOOB)
     return fail(AGENT_ATTN_ERR_SHAPE, "one head spans %ld elements, above the limit of 2^30",
                 (D.N - 1) * D.sn + D.d);

@@ -100,16 +100,31 @@ struct MfmaParams {
   const float* dwc_w;           // depth-wise 3x3 weights [H*d, 3, 3]
   const float* dwc_b;           // their bias [H*d] (null: zero)
   float inv_scale;              // 1 / scale: biases in units of the unscaled scores
+  int dwc_halo_rows;            // > 0: V rows of a workgroup's tokens and their 3 x 3
+                                // neighbourhood staged in LDS (this many at most)
 };
 
 // Module terms as a kernel sees them for its head (see MfmaParams).
 struct ModCtx {
   rsrc_t b1, b2, rv;            // B1 and B2 of the head's parameters; V of the head
   const float* wl;              // DWC weights in LDS: [9][DPAD] taps, then [DPAD] bias
+  const bf16_t* hv;             // V rows hr0 .. hr0 + hrows - 1 in LDS (hrows > 0)
   bool has_b1, has_b2, has_dwc;
   float inv_scale;
   int N, nag, w;
+  int hr0, hrows;
 };
+
+// LDS of the DWC weights and bias in the MOD instances.
+template <int DC>
+constexpr int dwc_lds_bytes() { return 10 * 32 * DC * 4; }
+// Elements per staged V row of the DWC (channels padded by 8: rows 16-byte
+// aligned, and the 8-byte tap reads of 16 consecutive rows fall in distinct
+// banks).
+template <int DC>
+constexpr int dwc_halo_stride() { return 32 * DC + 8; }
+template <int DC>
+constexpr long dwc_halo_lds_bytes(int rows) { return (long)rows * dwc_halo_stride<DC>() * 2; }
 
 // Phase timestamps for profiling builds (-DAGENT_ATTN_PHASE_TRACE): 32
 // wall-clock stamps per workgroup.  Compiled out otherwise.
@@ -696,34 +711,18 @@ __device__ __forceinline__ void load_q_tile(bf16x8 (&qf)[DC], rsrc_t rq, int tok
   }
 }
 
-// One 16-query tile: S^T = A Q^T over all agents at once, softmax over the
-// agents (lane group reductions), O^T = V_A^T P^T.  VAf: [VSPLIT][KC][DT][64].
-// Broadcast logits and softmax of one 16-token query tile: P2 = softmax over
-// the agents of scale * Q A^T, as bf16 B-operand fragments pf[j] (agent pairs
-// of chunk j, see pair_index) and the reciprocal of the row sum.
-template <class E, class C, int DC, int KTC, bool MOD>
-__device__ __forceinline__ void bcast_probs(const bf16x8 (&qf)[DC], const bf16x8* Af, int nag,
-                                            float sl2, bf16x8 (&pf)[C::KC], float& inv,
-                                            const ModCtx& mc, int tok0) {
-  const int lane = threadIdx.x & 63, g = lane >> 4;
-  // When the agent and V_A fragments need more than 128 registers they
-  // cannot all stay in registers across the caller's tile loop: the LDS
-  // index and agent count are then made opaque per tile so that the fragment
-  // reads and the padding compares are redone per tile instead of being
-  // hoisted (and spilled).
-  constexpr int kFragRegs = 4 * (KTC * DC + C::KC * 2 * DC * C::VSPLIT);
-  int fl = lane, nag_t = nag;
-  if (kFragRegs > 128 || KTC >= 16) {
-    asm volatile("" : "+v"(fl));
-    asm volatile("" : "+s"(nag_t));
-  }
-  // B2[token tok0 + r][agents 16t + 4g + i] (score units), loaded before the
-  // score products so that the loads travel while they run
-  f32x4 S[KTC];
+// Initial broadcast logits of one 16-token query tile: B2[token tok0 + r]
+// [agents 16t + 4g + i] in score units (module instances with B2), else
+// zero.
+template <int KTC, bool MOD>
+__device__ __forceinline__ void bcast_bias(f32x4 (&S)[KTC], int nag, const ModCtx& mc, int tok0) {
 #pragma unroll
   for (int t = 0; t < KTC; ++t) S[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   if constexpr (MOD) {
     if (mc.has_b2) {
+      const int lane = threadIdx.x & 63, g = lane >> 4;
+      int nag_t = nag;
+      if (KTC >= 16) asm volatile("" : "+s"(nag_t));
       const int tok = tok0 + (lane & 15);
 #pragma unroll
       for (int t = 0; t < KTC; ++t) {
@@ -743,6 +742,28 @@ __device__ __forceinline__ void bcast_probs(const bf16x8 (&qf)[DC], const bf16x8
         }
       }
     }
+  }
+}
+
+// Broadcast logits and softmax of one 16-token query tile: P2 = softmax over
+// the agents of scale * Q A^T (+ the initial logits S, see bcast_bias), as
+// bf16 B-operand fragments pf[j] (agent pairs of chunk j, see pair_index)
+// and the reciprocal of the row sum.
+template <class E, class C, int DC, int KTC>
+__device__ __forceinline__ void bcast_probs_from(f32x4 (&S)[KTC], const bf16x8 (&qf)[DC],
+                                                 const bf16x8* Af, int nag, float sl2,
+                                                 bf16x8 (&pf)[C::KC], float& inv) {
+  const int lane = threadIdx.x & 63, g = lane >> 4;
+  // When the agent and V_A fragments need more than 128 registers they
+  // cannot all stay in registers across the caller's tile loop: the LDS
+  // index and agent count are then made opaque per tile so that the fragment
+  // reads and the padding compares are redone per tile instead of being
+  // hoisted (and spilled).
+  constexpr int kFragRegs = 4 * (KTC * DC + C::KC * 2 * DC * C::VSPLIT);
+  int fl = lane, nag_t = nag;
+  if (kFragRegs > 128 || KTC >= 16) {
+    asm volatile("" : "+v"(fl));
+    asm volatile("" : "+s"(nag_t));
   }
 #pragma unroll
   for (int t = 0; t < KTC; ++t) {
@@ -779,6 +800,15 @@ __device__ __forceinline__ void bcast_probs(const bf16x8 (&qf)[DC], const bf16x8
     Lacc = E::mma(ones8<E>(), u.v, Lacc);
   }
   inv = 1.0f / Lacc[0];
+}
+
+template <class E, class C, int DC, int KTC, bool MOD>
+__device__ __forceinline__ void bcast_probs(const bf16x8 (&qf)[DC], const bf16x8* Af, int nag,
+                                            float sl2, bf16x8 (&pf)[C::KC], float& inv,
+                                            const ModCtx& mc, int tok0) {
+  f32x4 S[KTC];
+  bcast_bias<KTC, MOD>(S, nag, mc, tok0);
+  bcast_probs_from<E, C, DC, KTC>(S, qf, Af, nag, sl2, pf, inv);
 }
 
 // Depth-wise 3 x 3 convolution of V at grid position (row, col) for
@@ -825,6 +855,39 @@ __device__ __attribute__((noinline)) F8 dwc8(rsrc_t rv, const float* wl, int row
             float4{acc[1][0], acc[1][1], acc[1][2], acc[1][3]}};
 }
 
+// The same sum from V rows staged in LDS (ModCtx::hv, rows hr0 ..): the
+// taps of every token of the workgroup lie in the staged range.
+template <class E, int DC>
+__device__ __forceinline__ F8 dwc8_lds(const ModCtx& mc, int rows, int row, int col, int ch) {
+  constexpr int DPAD = 32 * DC, HS = dwc_halo_stride<DC>();
+  float acc[2][4];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const float4 b = *reinterpret_cast<const float4*>(mc.wl + 9 * DPAD + ch + 16 * h);
+    acc[h][0] = b.x;
+    acc[h][1] = b.y;
+    acc[h][2] = b.z;
+    acc[h][3] = b.w;
+  }
+#pragma unroll
+  for (int tap = 0; tap < 9; ++tap) {
+    const int rr = row + tap / 3 - 1, cc = col + tap % 3 - 1;
+    if (rr < 0 || rr >= rows || cc < 0 || cc >= mc.w) continue;
+    const bf16_t* src = mc.hv + (rr * mc.w + cc - mc.hr0) * HS + ch;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const u32x2 x = *reinterpret_cast<const u32x2*>(src + 16 * h);
+      const float4 wt = *reinterpret_cast<const float4*>(mc.wl + tap * DPAD + ch + 16 * h);
+      acc[h][0] = fmaf(wt.x, E::value((uint16_t)(x[0] & 0xffffu)), acc[h][0]);
+      acc[h][1] = fmaf(wt.y, E::value((uint16_t)(x[0] >> 16)), acc[h][1]);
+      acc[h][2] = fmaf(wt.z, E::value((uint16_t)(x[1] & 0xffffu)), acc[h][2]);
+      acc[h][3] = fmaf(wt.w, E::value((uint16_t)(x[1] >> 16)), acc[h][3]);
+    }
+  }
+  return F8{float4{acc[0][0], acc[0][1], acc[0][2], acc[0][3]},
+            float4{acc[1][0], acc[1][1], acc[1][2], acc[1][3]}};
+}
+
 // Stores one normalised 16-token output tile held in the matrix-core result
 // layout (O[dt]: channels 16 dt + 4 g .. +3 of token tok0 + r in lane (r, g)),
 // with the depth-wise convolution term added in the MOD instances.
@@ -847,8 +910,10 @@ __device__ __forceinline__ void store_o_tile(const f32x4 (&O)[2 * DC], float inv
       const int col = tok - row * mc.w;
 #pragma unroll
       for (int dt = 0; dt < DT; dt += 2) {   // tiles dt and dt + 1 (channels +16)
-        const F8 x =
-            dwc8<E, DC>(mc.rv, mc.wl, mc.N / mc.w, mc.w, row, col, 16 * dt + 4 * g, d, sn);
+        const F8 x = mc.hrows > 0
+                         ? dwc8_lds<E, DC>(mc, mc.N / mc.w, row, col, 16 * dt + 4 * g)
+                         : dwc8<E, DC>(mc.rv, mc.wl, mc.N / mc.w, mc.w, row, col,
+                                       16 * dt + 4 * g, d, sn);
         val[dt][0] += x.lo.x;
         val[dt][1] += x.lo.y;
         val[dt][2] += x.lo.z;
@@ -918,6 +983,8 @@ __device__ __forceinline__ void bcast_out(const bf16x8 (&pf)[C::KC], float inv, 
   store_o_tile<E, DC, MOD>(O, inv, ro, tok0, tok_end, d, sn, mc);
 }
 
+// One 16-query tile: S^T = A Q^T over all agents at once, softmax over the
+// agents (lane group reductions), O^T = V_A^T P^T.  VAf: [VSPLIT][KC][DT][64].
 template <class E, class C, int DC, int KTC, bool MOD>
 __device__ __forceinline__ void bcast_tile(const bf16x8 (&qf)[DC], const bf16x8* Af,
                                            const bf16x8* VAf, rsrc_t ro, int tok0, int tok_end,
@@ -1639,6 +1706,35 @@ agent_mfma_kernel(MfmaParams p) {
           if (c < d) x = tap < 9 ? p.dwc_w[ch * 9 + tap] : (p.dwc_b ? p.dwc_b[ch] : 0.f);
           wl[i] = x;
         }
+        if (p.dwc_halo_rows > 0) {
+          // V rows of this workgroup's tokens and one grid row plus one
+          // token on either side (every 3 x 3 tap of its tokens), 16-byte
+          // pieces, four loads in flight per thread; channels at or past d
+          // read zero
+          constexpr int CPR = DPAD / 8, HS = dwc_halo_stride<DC>();
+          const int hr0 = max(0, n0 - p.w - 1), hr1 = min(p.N, n1 + p.w + 1);
+          const int nck = max(0, hr1 - hr0) * CPR;
+          bf16_t* hv = reinterpret_cast<bf16_t*>(smem + C::TOTAL + dwc_lds_bytes<DC>());
+          for (int c0 = 0; c0 < nck; c0 += 4 * kThreads) {
+            uint4 x[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const int idx = c0 + u * kThreads + tid;
+              const int r = idx / CPR, c = idx - r * CPR;
+              const bool in = idx < nck && 8 * c < d;
+              x[u] = bld16<kPlain>(mc.rv, in ? (unsigned)(((hr0 + r) * sn + 8 * c) * 2) : kOOB);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const int idx = c0 + u * kThreads + tid;
+              const int r = idx / CPR, c = idx - r * CPR;
+              if (idx < nck) *reinterpret_cast<uint4*>(hv + r * HS + 8 * c) = x[u];
+            }
+          }
+          mc.hv = hv;
+          mc.hr0 = hr0;
+          mc.hrows = max(0, hr1 - hr0);
+        }
       }
     }
     __syncthreads();
@@ -1675,13 +1771,10 @@ agent_mfma_kernel(MfmaParams p) {
 template <int DC, class E>
 int launch_mfma_dc(const MfmaParams& mp, int ktc, int variant, long grid, hipStream_t st);
 
-// LDS of the DWC weights and bias in the MOD instances.
-template <int DC>
-constexpr int dwc_lds_bytes() { return 10 * 32 * DC * 4; }
-
 template <int DC, int KTC, bool STRIDED, class E, bool MOD>
 int launch_mfma_one(const MfmaParams& mp, long grid, hipStream_t st) {
-  const unsigned lds = (unsigned)(Cfg<DC, KTC>::TOTAL + (MOD ? dwc_lds_bytes<DC>() : 0));
+  const unsigned lds = (unsigned)(Cfg<DC, KTC>::TOTAL + (MOD ? dwc_lds_bytes<DC>() : 0) +
+                                  (MOD ? dwc_halo_lds_bytes<DC>(mp.dwc_halo_rows) : 0));
   agent_mfma_kernel<DC, KTC, STRIDED, E, MOD><<<dim3((unsigned)grid), dim3(kThreads), lds, st>>>(mp);
   return (int)hipGetLastError();
 }
