@@ -63,6 +63,9 @@ CASES = [
     inputs.custom("proj_f32", B=2, H=2, h=8, w=8, d=32, s=4, dtype="f32"),
     inputs.custom("proj_f32_ragged", B=1, H=3, h=7, w=5, d=40, s=2, dtype="f32"),
     inputs.custom("proj_supplied", B=2, H=2, h=10, w=10, d=64, s=4, supplied_agents=True),
+    # 16 token tiles of 128 and 288 q/k/v features (three tiles of 128, the
+    # last ragged)
+    inputs.custom("proj_ragged_features", B=2, H=3, h=32, w=32, d=32, s=4),
 ]
 
 
