@@ -141,6 +141,7 @@ struct Plan {
   int chunk = 0, nchunks = 0;
   // matrix-core path
   int DC = 0, P = 1, T = 0, fused = 1, xcd_heads = 0, lds = 0;
+  int waves = 8;   // 4: one head per four-wave workgroup, two workgroups per CU
   size_t off_sync = 0, off_status = 0, off_A = 0, off_VA = 0, off_part = 0, bytes = 0;
   size_t off_ml = 0;
 };
@@ -179,6 +180,11 @@ int lds_for(int ktc) {
 int mfma_lds_bytes(int DC, int nag) {
   const int ktc = mfma_ktc(nag);
   return DC == 1 ? lds_for<1>(ktc) : DC == 2 ? lds_for<2>(ktc) : lds_for<4>(ktc);
+}
+// LDS of the four-wave instance (up to 64 agents).
+int mfma_lds_bytes4(int DC) {
+  return DC == 1 ? aa::Cfg<1, 4, 4>::TOTAL
+                 : DC == 2 ? aa::Cfg<2, 4, 4>::TOTAL : aa::Cfg<4, 4, 4>::TOTAL;
 }
 
 // Partials of the matrix-core aggregation, in register order: per (head,
@@ -350,6 +356,12 @@ Plan make_plan(const Dims& D, int cus) {
     P.lds = mfma_lds_bytes(P.DC, D.nag);
     P.fused = 1;  // BH*P <= CUs: the whole grid is co-resident
     P.xcd_heads = (P.P > 1 && D.BH % 8 == 0 && cus % 8 == 0) ? (int)(D.BH / 8) : 0;
+    // more heads than CUs, one workgroup per head: with up to 64 agents and
+    // two four-wave workgroups' LDS per CU, every head is resident at once
+    // instead of the heads running in rounds of one eight-wave workgroup per CU
+    if (P.P == 1 && D.BH > cus && mfma_ktc(D.nag) == 4 &&
+        2 * (mfma_lds_bytes4(P.DC) + 64) <= 160 * 1024)
+      P.waves = 4;
     part_bytes = 0;  // set with the fragment regions below
   }
   // A and V_A regions: fp32 rows, or in the fused path the bf16 MFMA
@@ -451,7 +463,9 @@ int launch_mfma(int DC, bool f16, const aa::MfmaParams& mp, long grid, int nag,
   const bool strided = !(mp.sn == mp.d && mp.sh == (long)mp.N * mp.d &&
                          mp.sb == (long)mp.H * mp.N * mp.d);
   const bool module = mp.bias_agg || mp.bias_bcast || mp.dwc_w;
-  const int variant = module ? aa::kModule : (strided ? aa::kStrided : aa::kDense);
+  const int variant = module    ? aa::kModule
+                      : strided ? aa::kStrided
+                                : (mp.waves == 4 && mp.fused && mp.P == 1 ? aa::kDense4 : aa::kDense);
   const int ktc = mfma_ktc(nag);
   int e;
   if (f16) {
@@ -563,6 +577,7 @@ int run_forward_mfma(const Dims& D, const Plan& P, const void* q, const void* k,
   mp.sync = (unsigned*)(ws + P.off_sync);
   mp.status = (int*)(ws + P.off_status);
   mp.xcd_heads = (P.xcd_heads > 0 && xcd_round_robin(st)) ? P.xcd_heads : 0;
+  mp.waves = P.waves;
 #ifdef AGENT_ATTN_PHASE_TRACE
   mp.trace = g_trace;
 #endif

@@ -89,6 +89,7 @@ struct MfmaParams {
   int phases;
   int fused;
   int xcd_heads;                // >0: heads per XCD for the XCD-aware mapping
+  int waves;                    // host: 4 selects the four-wave instance (else 8)
   long spin_limit;              // polls before a group wait gives up (kSpinLimit)
   long long* trace;             // phase timestamps (trace builds only)
   long sb, sh;                  // q/k/v/out element strides of batch and head
@@ -452,14 +453,14 @@ constexpr int vsplit_of(int ktc) { return ktc <= 4 ? 2 : 1; }
 constexpr long a_frag_bytes(int ktc, int dc) { return (long)ktc * dc * 1024; }
 constexpr long va_frag_bytes(int ktc, int dc) { return (long)vsplit_of(ktc) * (ktc / 2) * (2 * dc) * 1024; }
 
-template <int DC, int KTC>
+template <int DC, int KTC, int NW = kWaves>
 struct Cfg {
   static constexpr int DT = 2 * DC;                // 16-channel output tiles
   static constexpr int DPAD = 32 * DC;
   static constexpr int RT = DC <= 2 ? 256 : 128;   // tokens per K/V round
-  static constexpr int AG = KTC < kWaves ? KTC : kWaves;   // agent groups of waves
+  static constexpr int AG = KTC < NW ? KTC : NW;   // agent groups of waves
   static constexpr int ATW = KTC / AG;             // agent tiles per wave
-  static constexpr int TG = kWaves / AG;           // token groups of waves
+  static constexpr int TG = NW / AG;               // token groups of waves
   static constexpr int KC = (KTC + 1) / 2;         // 32-agent chunks
   static constexpr int VSPLIT = vsplit_of(KTC);    // V_A as bf16 hi + lo
   // Partial accumulators as agent rows (coalesced merge reads; measured
@@ -477,7 +478,7 @@ struct Cfg {
   static constexpr int COMB_BYTES = (TG - 1) * AG * ATW * (DT + 1) * 1024;
   static constexpr int STAGE_BYTES = KTC * 16 * DPAD * 4;
   static constexpr int VA_BYTES = VSPLIT * KC * DT * 1024;
-  static constexpr int POOL_BYTES = kThreads * 32;
+  static constexpr int POOL_BYTES = NW * 64 * 32;
   static constexpr int mx(int a, int b) { return a > b ? a : b; }
   static constexpr int BASE = mx(mx(VT_BYTES + KS_BYTES, COMB_BYTES), POOL_BYTES);
   static constexpr int kMaxLds = 160 * 1024 - 64;  // static LDS of the barrier flag
@@ -996,10 +997,15 @@ __device__ __forceinline__ void bcast_tile(const bf16x8 (&qf)[DC], const bf16x8*
 }
 
 // ------------------------------------------------------------- the kernel
-template <int DC, int KTC, bool STRIDED, class E, bool MOD>
-__global__ void __launch_bounds__(kThreads)
+// NW waves per workgroup: 8, or 4 for heads held by one workgroup each when
+// there are more heads than CUs (two workgroups per CU then, capped at two
+// waves per SIMD, so that every head is on the chip at once).
+template <int DC, int KTC, bool STRIDED, class E, bool MOD, int NW = kWaves>
+__global__ void __launch_bounds__(64 * NW, 8 / NW)
 agent_mfma_kernel(MfmaParams p) {
-  using C = Cfg<DC, KTC>;
+  constexpr int kWaves = NW;             // these shadow the 8-wave defaults
+  constexpr int kThreads = 64 * NW;
+  using C = Cfg<DC, KTC, NW>;
   constexpr int DT = C::DT;
   constexpr int DPAD = C::DPAD;
   constexpr int RT = C::RT;
@@ -1771,23 +1777,29 @@ agent_mfma_kernel(MfmaParams p) {
 template <int DC, class E>
 int launch_mfma_dc(const MfmaParams& mp, int ktc, int variant, long grid, hipStream_t st);
 
-template <int DC, int KTC, bool STRIDED, class E, bool MOD>
+template <int DC, int KTC, bool STRIDED, class E, bool MOD, int NW = kWaves>
 int launch_mfma_one(const MfmaParams& mp, long grid, hipStream_t st) {
-  const unsigned lds = (unsigned)(Cfg<DC, KTC>::TOTAL + (MOD ? dwc_lds_bytes<DC>() : 0) +
+  const unsigned lds = (unsigned)(Cfg<DC, KTC, NW>::TOTAL + (MOD ? dwc_lds_bytes<DC>() : 0) +
                                   (MOD ? dwc_halo_lds_bytes<DC>(mp.dwc_halo_rows) : 0));
-  agent_mfma_kernel<DC, KTC, STRIDED, E, MOD><<<dim3((unsigned)grid), dim3(kThreads), lds, st>>>(mp);
+  agent_mfma_kernel<DC, KTC, STRIDED, E, MOD, NW>
+      <<<dim3((unsigned)grid), dim3(64 * NW), lds, st>>>(mp);
   return (int)hipGetLastError();
 }
 
-// Kernel variants: the dense layout, caller strides, and the dense layout
-// with the module terms (agent biases, depth-wise convolution).
-enum Variant { kDense = 0, kStrided = 1, kModule = 2 };
+// Kernel variants: the dense layout, caller strides, the dense layout with
+// the module terms (agent biases, depth-wise convolution), and the dense
+// layout in four-wave workgroups (one head each, more heads than CUs; up to
+// 64 agents).
+enum Variant { kDense = 0, kStrided = 1, kModule = 2, kDense4 = 3 };
 
 template <int DC, int KTC, class E>
 int launch_mfma_variant(const MfmaParams& mp, int variant, long grid, hipStream_t st) {
   switch (variant) {
     case kStrided: return launch_mfma_one<DC, KTC, true, E, false>(mp, grid, st);
     case kModule: return launch_mfma_one<DC, KTC, false, E, true>(mp, grid, st);
+    case kDense4:
+      if constexpr (KTC == 4) return launch_mfma_one<DC, KTC, false, E, false, 4>(mp, grid, st);
+      return (int)hipErrorInvalidValue;
     default: return launch_mfma_one<DC, KTC, false, E, false>(mp, grid, st);
   }
 }

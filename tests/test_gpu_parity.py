@@ -77,6 +77,15 @@ EDGE = [
     inputs.custom("bh128_p2", B=16, H=8, h=24, w=24, d=64, s=6),
     inputs.custom("bh100_p2", B=25, H=4, h=20, w=20, d=32, s=5),
     inputs.custom("bh260_p1", B=26, H=10, h=8, w=8, d=64, s=4),
+    # more heads than CUs with up to 64 agents: one head per four-wave
+    # workgroup, two per CU (head dims 32, 48, 64; several key/value rounds
+    # of 256 tokens; ragged windows in fp16; supplied agents), and d = 128,
+    # whose LDS keeps one eight-wave workgroup per CU
+    inputs.custom("bh320_w4_d32", B=40, H=8, h=12, w=12, d=32, s=4),
+    inputs.custom("bh300_w4_n576", B=300, H=1, h=24, w=24, d=64, s=6),
+    inputs.custom("bh280_w4_f16_ragged", B=70, H=4, h=15, w=13, d=64, s=7, dtype="f16"),
+    inputs.custom("bh264_w4_supplied", B=33, H=8, h=10, w=10, d=48, s=3, supplied_agents=True),
+    inputs.custom("bh300_d128_p1", B=100, H=3, h=8, w=8, d=128, s=4),
     # a long sequence: 256 x 256 grid, 256 agents
     inputs.custom("long_256x256", B=1, H=2, h=256, w=256, d=64, s=16),
     # one workgroup per head with 100 agents (grouped broadcast, partial
