@@ -32,10 +32,10 @@ CSRC = os.path.join(ROOT, "efficient_attention_vision_amd", "csrc")
 FUSED_KERNEL = "agent_mfma_kernel"
 
 # rocprofv3 runs whose output the summaries below are made from (run from
-# /tmp with TMPDIR=/tmp; R = repository root)
-TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/kt_{w} -o run "
+# /tmp with TMPDIR=/tmp; R = repository root, OUT = the folder for profiler output)
+TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/kt_{w} -o run "
              "-- python3 $R/bench.py --workload {w} --no-cpu-baseline --steps 50 --warmup 5")
-PMC_CMD = ("timeout -s KILL 120 rocprofv3 --pmc {c} --output-format csv -d $R/gpurun_out/{d} -o run "
+PMC_CMD = ("timeout -s KILL 120 rocprofv3 --pmc {c} --output-format csv -d $OUT/{d} -o run "
            "-- python3 $R/bench.py {a}")
 
 
@@ -145,7 +145,7 @@ def write_counter_summary(wl, fetch_dir, write_dir, copy_fetch_dir, copy_write_d
         f"# HBM counters: {FUSED_KERNEL}, workload {wl.name}",
         "",
         f"Workload: B={wl.B} H={wl.H} grid {wl.h}x{wl.w} (N={wl.N}) d={wl.d} k={wl.k} {wl.dtype}.",
-        "Commands (from /tmp with TMPDIR=/tmp, R = repository root), one counter per run:",
+        "Commands (from /tmp with TMPDIR=/tmp, R = repository root, OUT = profiler output folder), one counter per run:",
         "",
         "    " + PMC_CMD.format(c="FETCH_SIZE", d=os.path.basename(fetch_dir),
                                 a=f"--workload {wl.name} --no-cpu-baseline --steps 10 --warmup 2"),
@@ -196,10 +196,10 @@ def write_trace_summary(wl, trace_dir):
         f"# Kernel trace: {FUSED_KERNEL}, workload {wl.name}",
         "",
         f"Workload: B={wl.B} H={wl.H} grid {wl.h}x{wl.w} (N={wl.N}) d={wl.d} k={wl.k} {wl.dtype}.",
-        "Command (from /tmp with TMPDIR=/tmp, R = repository root):",
+        "Command (from /tmp with TMPDIR=/tmp, R = repository root, OUT = profiler output folder):",
         "",
         "    " + TRACE_CMD.format(w=wl.name),
-        "    python3 bench.py --workload " + wl.name + " --trace-summary $R/gpurun_out/kt_" + wl.name,
+        "    python3 bench.py --workload " + wl.name + " --trace-summary $OUT/kt_" + wl.name,
         "",
         "The run makes 5 warm-up launches, 50 event-bracketed eager launches, then a graph of",
         "50 launches replayed twice.",
@@ -253,7 +253,7 @@ def write_mfma_summary(wl, pmc_dir, trace_dir):
         f"# Matrix-core busy: {FUSED_KERNEL}, workload {wl.name}",
         "",
         f"Workload: B={wl.B} H={wl.H} grid {wl.h}x{wl.w} (N={wl.N}) d={wl.d} k={wl.k} {wl.dtype}.",
-        "Commands (from /tmp with TMPDIR=/tmp, R = repository root):",
+        "Commands (from /tmp with TMPDIR=/tmp, R = repository root, OUT = profiler output folder):",
         "",
         "    " + PMC_CMD.format(c="MfmaUtil", d=os.path.basename(pmc_dir),
                                 a=f"--workload {wl.name} --no-cpu-baseline --steps 10 --warmup 2"),
@@ -281,7 +281,7 @@ def write_mfma_summary(wl, pmc_dir, trace_dir):
     print(path)
 
 
-PASS_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/{d}_{w} -o run "
+PASS_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/{d}_{w} -o run "
             "-- python3 $R/bench.py --workload {w} --no-cpu-baseline --{m} --steps 20 --warmup 2")
 PASS_NAMES = {"backward": ("bwd_passes", "ktb"), "projections": ("module_projections", "ktp")}
 
@@ -298,11 +298,11 @@ def write_passes_summary(wl, mode, trace_dir):
         f"# Kernel trace: {mode} path, workload {wl.name}",
         "",
         f"Workload: B={wl.B} H={wl.H} grid {wl.h}x{wl.w} (N={wl.N}) d={wl.d} k={wl.k} {wl.dtype}.",
-        "Command (from /tmp with TMPDIR=/tmp, R = repository root):",
+        "Command (from /tmp with TMPDIR=/tmp, R = repository root, OUT = profiler output folder):",
         "",
         "    " + PASS_CMD.format(d=tag, w=wl.name, m=mode),
         f"    python3 bench.py --workload {wl.name} --passes-summary {mode} "
-        f"$R/gpurun_out/{tag}_{wl.name}",
+        f"$OUT/{tag}_{wl.name}",
         "",
         "The run makes 2 warm-up steps, 20 event-bracketed eager steps, then a graph of 20",
         "steps replayed twice (62 steps); a kernel launched once per agent chunk (chunks of",
