@@ -452,7 +452,7 @@ def main():
             write_trace_summary(wl, args.trace_summary)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+        print(f"bench.py: this benchmark runs on one GPU only; --gpus {args.gpus} is not supported "
               "(heads are independent: each GPU would run this same forward on its share of B*H)",
               file=sys.stderr)
         sys.exit(2)
