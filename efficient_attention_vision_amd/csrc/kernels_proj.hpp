@@ -170,8 +170,10 @@ constexpr int gemm16_lds_bytes(int nbuf) {
              : 128 * (32 * FT + 8) * 2;
 }
 
+// At most 128 registers per lane with 64-wide feature tiles: four workgroups
+// per CU (the short products are latency-bound; more of them in flight).
 template <class El, int MODE, int FT>
-__global__ void __launch_bounds__(kThr) proj_gemm16(ProjParams p) {
+__global__ void __launch_bounds__(kThr, FT <= 2 ? 4 : 2) proj_gemm16(ProjParams p) {
   constexpr int WF = 32 * FT, WT = 128;
   constexpr int CPR = kKStep / 8;                                  // 16-byte chunks per row
   constexpr int NA = WF * CPR / kThr, NX = WT * CPR / kThr;       // chunks per thread
