@@ -186,6 +186,20 @@ int mfma_lds_bytes4(int DC) {
   return DC == 1 ? aa::Cfg<1, 4, 4>::TOTAL
                  : DC == 2 ? aa::Cfg<2, 4, 4>::TOTAL : aa::Cfg<4, 4, 4>::TOTAL;
 }
+// LDS of the plan left free during the broadcast (after the V_A staging rows
+// and fragments); it is the same for eight- and four-wave workgroups.
+template <int DC>
+long bcast_free_for(int ktc) {
+  auto f = [](auto c) {
+    using C = decltype(c);
+    return (long)C::BIG - (C::STAGE_LDS ? C::STAGE_BYTES : 0) - C::VA_BYTES;
+  };
+  return ktc == 4 ? f(aa::Cfg<DC, 4>{}) : ktc == 8 ? f(aa::Cfg<DC, 8>{}) : f(aa::Cfg<DC, 16>{});
+}
+long bcast_free_lds(int DC, int nag) {
+  const int ktc = mfma_ktc(nag);
+  return DC == 1 ? bcast_free_for<1>(ktc) : DC == 2 ? bcast_free_for<2>(ktc) : bcast_free_for<4>(ktc);
+}
 
 // Partials of the matrix-core aggregation, in register order: per (head,
 // slot, agent tile) the max/sum of 16 agents and 2*DC rows of 64 x 4 floats.
@@ -463,9 +477,10 @@ int launch_mfma(int DC, bool f16, const aa::MfmaParams& mp, long grid, int nag,
   const bool strided = !(mp.sn == mp.d && mp.sh == (long)mp.N * mp.d &&
                          mp.sb == (long)mp.H * mp.N * mp.d);
   const bool module = mp.bias_agg || mp.bias_bcast || mp.dwc_w;
-  const int variant = module    ? aa::kModule
+  const bool four = mp.waves == 4 && mp.fused && mp.P == 1;
+  const int variant = module    ? (four ? aa::kModule4 : aa::kModule)
                       : strided ? aa::kStrided
-                                : (mp.waves == 4 && mp.fused && mp.P == 1 ? aa::kDense4 : aa::kDense);
+                                : (four ? aa::kDense4 : aa::kDense);
   const int ktc = mfma_ktc(nag);
   int e;
   if (f16) {
@@ -520,11 +535,26 @@ int run_mfma_phases(const Dims& D, aa::MfmaParams mp, int DC, int phases, bool f
   // the DWC reads V from LDS when a workgroup's tokens and their 3 x 3
   // neighbourhood (one grid row and one token on either side) fit beside the
   // plan; otherwise each tap is a load from V
+  // neighbourhood (one grid row and one token on either side) fit: in the
+  // part of the plan the broadcast leaves free, else beside the plan
   mp.dwc_halo_rows = 0;
+  mp.dwc_halo_in_plan = 0;
+  long halo = 0;
   if (mp.dwc_w) {
     const long rows = std::min<long>(D.N, (long)mp.T + 2L * D.w + 2);
-    if (lds + rows * (32L * DC + 8) * 2 <= 160 * 1024 - 64)   // dwc_halo_lds_bytes
+    halo = rows * (32L * DC + 8) * 2;   // dwc_halo_lds_bytes
+    if (halo <= bcast_free_lds(DC, D.nag)) {
       mp.dwc_halo_rows = (int)rows;
+      mp.dwc_halo_in_plan = 1;
+    } else if (lds + halo <= 160 * 1024 - 64) {
+      mp.dwc_halo_rows = (int)rows;
+    }
+  }
+  // the four-wave module instance only where two workgroups still share a CU
+  if (module && mp.waves == 4) {
+    const long l4 = mfma_lds_bytes4(DC) + 10 * 32 * DC * 4 +
+                    (mp.dwc_halo_rows > 0 && !mp.dwc_halo_in_plan ? halo : 0);
+    if (2 * (l4 + 64) > 160 * 1024) mp.waves = 8;
   }
   if (((D.N - 1) * D.sn + D.d) * 2 >= (long)aa::kOOB)
     return fail(AGENT_ATTN_ERR_SHAPE, "one head spans %ld elements, above the limit of 2^30",

@@ -87,9 +87,11 @@ struct MfmaParams {
   int pool_maxcnt;              // largest pooling window, in tokens
   float sl2;                    // scale * log2(e)
   int phases;
-  int fused;
+  unsigned char fused;          // one launch for all phases, groups synchronised inside
+  unsigned char waves;          // host: 4 selects a four-wave instance (else 8)
+  unsigned char dwc_halo_in_plan;   // 1: the staged DWC rows (dwc_halo_rows) sit in the
+                                    // plan's LDS left free by the broadcast, else after it
   int xcd_heads;                // >0: heads per XCD for the XCD-aware mapping
-  int waves;                    // host: 4 selects the four-wave instance (else 8)
   long spin_limit;              // polls before a group wait gives up (kSpinLimit)
   long long* trace;             // phase timestamps (trace builds only)
   long sb, sh;                  // q/k/v/out element strides of batch and head
@@ -1720,7 +1722,9 @@ agent_mfma_kernel(MfmaParams p) {
           constexpr int CPR = DPAD / 8, HS = dwc_halo_stride<DC>();
           const int hr0 = max(0, n0 - p.w - 1), hr1 = min(p.N, n1 + p.w + 1);
           const int nck = max(0, hr1 - hr0) * CPR;
-          bf16_t* hv = reinterpret_cast<bf16_t*>(smem + C::TOTAL + dwc_lds_bytes<DC>());
+          bf16_t* hv = reinterpret_cast<bf16_t*>(
+              p.dwc_halo_in_plan ? big + (C::STAGE_LDS ? C::STAGE_BYTES : 0) + C::VA_BYTES
+                                 : smem + C::TOTAL + dwc_lds_bytes<DC>());
           for (int c0 = 0; c0 < nck; c0 += 4 * kThreads) {
             uint4 x[4];
 #pragma unroll
@@ -1779,8 +1783,9 @@ int launch_mfma_dc(const MfmaParams& mp, int ktc, int variant, long grid, hipStr
 
 template <int DC, int KTC, bool STRIDED, class E, bool MOD, int NW = kWaves>
 int launch_mfma_one(const MfmaParams& mp, long grid, hipStream_t st) {
-  const unsigned lds = (unsigned)(Cfg<DC, KTC, NW>::TOTAL + (MOD ? dwc_lds_bytes<DC>() : 0) +
-                                  (MOD ? dwc_halo_lds_bytes<DC>(mp.dwc_halo_rows) : 0));
+  const unsigned lds =
+      (unsigned)(Cfg<DC, KTC, NW>::TOTAL + (MOD ? dwc_lds_bytes<DC>() : 0) +
+                 (MOD && !mp.dwc_halo_in_plan ? dwc_halo_lds_bytes<DC>(mp.dwc_halo_rows) : 0));
   agent_mfma_kernel<DC, KTC, STRIDED, E, MOD, NW>
       <<<dim3((unsigned)grid), dim3(64 * NW), lds, st>>>(mp);
   return (int)hipGetLastError();
@@ -1788,9 +1793,9 @@ int launch_mfma_one(const MfmaParams& mp, long grid, hipStream_t st) {
 
 // Kernel variants: the dense layout, caller strides, the dense layout with
 // the module terms (agent biases, depth-wise convolution), and the dense
-// layout in four-wave workgroups (one head each, more heads than CUs; up to
-// 64 agents).
-enum Variant { kDense = 0, kStrided = 1, kModule = 2, kDense4 = 3 };
+// layout without and with the module terms in four-wave workgroups (one head
+// each, more heads than CUs; up to 64 agents).
+enum Variant { kDense = 0, kStrided = 1, kModule = 2, kDense4 = 3, kModule4 = 4 };
 
 template <int DC, int KTC, class E>
 int launch_mfma_variant(const MfmaParams& mp, int variant, long grid, hipStream_t st) {
@@ -1799,6 +1804,9 @@ int launch_mfma_variant(const MfmaParams& mp, int variant, long grid, hipStream_
     case kModule: return launch_mfma_one<DC, KTC, false, E, true>(mp, grid, st);
     case kDense4:
       if constexpr (KTC == 4) return launch_mfma_one<DC, KTC, false, E, false, 4>(mp, grid, st);
+      return (int)hipErrorInvalidValue;
+    case kModule4:
+      if constexpr (KTC == 4) return launch_mfma_one<DC, KTC, false, E, true, 4>(mp, grid, st);
       return (int)hipErrorInvalidValue;
     default: return launch_mfma_one<DC, KTC, false, E, false>(mp, grid, st);
   }

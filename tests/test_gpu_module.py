@@ -59,6 +59,10 @@ CASES = [
     inputs.custom("mod_f32_ragged", B=2, H=2, h=9, w=7, d=40, s=3, dtype="f32"),
     inputs.custom("mod_f32_d128", B=1, H=2, h=16, w=12, d=128, s=4, dtype="f32"),
     inputs.custom("mod_thin_2x300", B=1, H=2, h=2, w=300, d=64, s=2),
+    # more heads than CUs, up to 64 agents: four-wave workgroups, two per CU,
+    # the convolution's V rows staged in the plan's free LDS
+    inputs.custom("mod_w4_d32", B=40, H=8, h=12, w=12, d=32, s=4),
+    inputs.custom("mod_w4_f16_ragged", B=70, H=4, h=15, w=13, d=64, s=7, dtype="f16"),
 ]
 
 
